@@ -1,0 +1,350 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against brute force with exact rationals, a
+textbook routine, a closed form or an invariant of the method, chosen so that
+a dropped term, a wrong sign or index, or a transposed operand fails one of
+them.  CPU only.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from learned_sparse_kv_amd import synth
+from oracle import oracle
+from tests import helpers
+
+U = 2.0 ** -24  # unit roundoff of binary32
+
+
+def gamma(n):
+    return n * U / (1 - n * U)
+
+
+# ---------------------------------------------------------------- PIN-1 decode
+def test_fp8_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.decode(synth.FP8, codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    nan_codes = {0x7F, 0xFF}
+    for c in range(256):
+        if c in nan_codes:
+            assert math.isnan(mine[c]), c
+        else:
+            assert mine[c] == ref[c] and np.signbit(mine[c]) == np.signbit(ref[c]), c
+    # closed forms: largest normal, smallest subnormal, one
+    assert mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9 and mine[0x38] == 1.0
+
+
+def test_bf16_decode_all_codes_match_torch():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.decode(synth.BF16, codes)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    same = (mine.view(np.uint32) == ref.view(np.uint32)) | (np.isnan(mine) & np.isnan(ref))
+    assert same.all()
+
+
+# ---------------------------------------------------------------- geometry
+@pytest.mark.parametrize("L,C,W,exp", [
+    (16384, 64, 2048, (14336, 224, 2048)),
+    (5000, 64, 1024, (3968, 62, 1032)),
+    (512000, 64, 8192, (503808, 7872, 8192)),
+    (100, 64, 1024, (0, 0, 100)),
+    (1024 + 63, 64, 1024, (0, 0, 1087)),
+    (1024 + 64, 64, 1024, (64, 1, 1024)),
+])
+def test_geometry_closed_form(L, C, W, exp):
+    assert oracle.geometry(L, C, W) == exp
+
+
+def test_generator_layout_agrees_with_oracle_geometry():
+    inp = synth.generate(synth.small_config(seq_lens=(5000, 3000, 700)))
+    for r, L in enumerate(inp["seq_len"]):
+        rs, nh, nr = oracle.geometry(int(L), 64, 1024)
+        assert (inp["rs"][r], inp["n_hist"][r], inp["n_rec"][r]) == (rs, nh, nr)
+
+
+# ---------------------------------------------------------------- PIN-2/3 score, select
+def _exact_logits(inp):
+    cfg = inp.cfg
+    q = oracle.decode(cfg.q_dtype, inp["q_coarse"]).reshape(cfg.batch, cfg.H, cfg.d)
+    kic = oracle.decode(cfg.idx_dtype, inp["kic"]).reshape(-1, cfg.d)
+    out, bound = [], []
+    for r in range(cfg.batch):
+        c0, c1 = inp["chunk_off"][r], inp["chunk_off"][r + 1]
+        w = inp["w_coarse"][r]
+        for c in range(c0, c1):
+            s = Fraction(float(inp["kic_scale"][c])) if cfg.idx_dtype == synth.FP8 else 1
+            acc = Fraction(0)
+            mag = Fraction(0)
+            for i in range(cfg.d):
+                qb = sum(Fraction(float(w[h])) * Fraction(float(q[r, h, i])) for h in range(cfg.H))
+                qa = sum(abs(Fraction(float(w[h])) * Fraction(float(q[r, h, i]))) for h in range(cfg.H))
+                acc += qb * Fraction(float(kic[c, i]))
+                mag += qa * abs(Fraction(float(kic[c, i])))
+            b = Fraction(float(inp["bias"][r]))
+            out.append(b + s * acc)
+            bound.append(gamma(cfg.H + cfg.d + 2) * float(abs(s) * mag + abs(b)))
+    return out, bound
+
+
+@pytest.mark.parametrize("idx", [synth.F32, synth.FP8])
+def test_score_brute_force_exact(idx):
+    inp = helpers.tiny_inputs(idx_dtype=idx, d=7, H=4)
+    o = oracle.Oracle(inp)
+    z, sel, cnt = o.score_select()
+    exact, bound = _exact_logits(inp)
+    assert len(z) == len(exact) > 0
+    for zi, ei, bi in zip(z, exact, bound):
+        assert abs(float(zi) - float(ei)) <= bi + 1e-300, (zi, float(ei), bi)
+
+
+def test_score_exact_by_construction_is_bitwise():
+    """Small integers and power-of-two weights: every fp32 step is exact."""
+    inp = helpers.tiny_inputs(d=6, H=4)
+    rng = np.random.default_rng(3)
+    cfg = inp.cfg
+    inp["q_coarse"] = rng.integers(-8, 9, size=inp["q_coarse"].shape).astype(np.float32)
+    inp["w_coarse"] = np.array([[0.5, 0.25, 2.0, 1.0]] * cfg.batch, np.float32)
+    inp["kic"] = rng.integers(-8, 9, size=inp["kic"].shape).astype(np.float32)
+    inp["bias"] = np.array([-3.0, 5.0], np.float32)
+    z, _, _ = oracle.Oracle(inp).score_select()
+    exact, _ = _exact_logits(inp)
+    assert [float(v) for v in z] == [float(e) for e in exact]
+
+
+def test_score_special_cases():
+    inp = helpers.tiny_inputs(H=1, d=5)
+    inp["w_coarse"][:] = 1.0
+    z, _, _ = oracle.Oracle(inp).score_select()
+    q = inp["q_coarse"].astype(np.float64)
+    kic = inp["kic"].astype(np.float64)
+    for r in range(2):
+        for c in range(inp["chunk_off"][r], inp["chunk_off"][r + 1]):
+            ref = float(np.float32(np.dot(q[r, 0], kic[c]) + inp["bias"][r]))
+            assert abs(z[c] - ref) <= 4 * U * (np.abs(q[r, 0] * kic[c]).sum() + 1)
+    inp["kic"][:] = 0.0
+    z, _, _ = oracle.Oracle(inp).score_select()
+    for r in range(2):
+        assert (z[inp["chunk_off"][r]:inp["chunk_off"][r + 1]] == inp["bias"][r]).all()
+
+
+def test_select_is_exactly_strict_threshold():
+    inp = synth.generate(synth.small_config(seq_lens=(9000, 4000)))
+    o = oracle.Oracle(inp)
+    z, sel, cnt = o.score_select()
+    for r in range(2):
+        c0, c1 = inp["chunk_off"][r], inp["chunk_off"][r + 1]
+        want = [c for c in range(c1 - c0) if z[c0 + c] > 0.0]
+        assert list(sel[c0:c0 + cnt[r]]) == want
+        # sigmoid(z) > 0.5 exactly when z > 0
+        assert all((1 / (1 + math.exp(-float(z[c0 + c]))) > 0.5) == (z[c0 + c] > 0)
+                   for c in range(c1 - c0) if abs(z[c0 + c]) > 1e-12)
+    _, _, cnt_none = o.score_select(theta=float("inf"))
+    _, sel_all, cnt_all = o.score_select(theta=float("-inf"))
+    assert (cnt_none == 0).all()
+    assert list(cnt_all) == list(inp["n_hist"])
+    assert list(sel_all[:cnt_all[0]]) == list(range(cnt_all[0]))
+
+
+def test_select_zero_logit_not_selected():
+    inp = helpers.tiny_inputs()
+    inp["kic"][:] = 0.0
+    inp["bias"][:] = 0.0                 # z = +0 exactly
+    z, sel, cnt = oracle.Oracle(inp).score_select()
+    assert (z == 0).all() and (cnt == 0).all()
+    inp["bias"][:] = np.float32(1e-45)   # smallest subnormal above 0
+    _, _, cnt = oracle.Oracle(inp).score_select()
+    assert list(cnt) == list(inp["n_hist"])
+
+
+# ---------------------------------------------------------------- PIN-4/5 refine, top-k
+def _exact_refine(inp, r, sel_r, q_r, w_r):
+    cfg = inp.cfg
+    C = cfg.chunk
+    q = oracle.decode(cfg.q_dtype, q_r).reshape(cfg.H, cfg.d).astype(np.float64)
+    c0 = inp["chunk_off"][r]
+    res, bnd = [], []
+    for c in sel_r:
+        pg = inp["pages"][c0 + c]
+        eb = synth.ELEM_BYTES[cfg.idx_dtype]
+        raw = pg[cfg.ikey_off:]
+        dt = {0: np.float32, 1: np.uint16, 2: np.uint8}[cfg.idx_dtype]
+        keys = oracle.decode(cfg.idx_dtype, raw.view(dt)).reshape(C, cfg.d)
+        s = Fraction(float(inp["ikey_scale"][c0 + c])) if cfg.idx_dtype == synth.FP8 else 1
+        for t in range(C):
+            I = Fraction(0)
+            mag = 0.0
+            for h in range(cfg.H):
+                a = sum(Fraction(float(q[h, i])) * Fraction(float(keys[t, i])) for i in range(cfg.d))
+                I += Fraction(float(w_r[h])) * max(a, Fraction(0))
+                mag += abs(float(w_r[h])) * float(np.abs(q[h] * keys[t]).sum())
+            res.append(s * I)
+            bnd.append(gamma(cfg.H + cfg.d + 2) * float(abs(s)) * mag)
+    return res, bnd
+
+
+@pytest.mark.parametrize("idx", [synth.F32, synth.FP8])
+def test_refine_brute_force_exact(idx):
+    inp = helpers.tiny_inputs(idx_dtype=idx, H=3, d=5)
+    o = oracle.Oracle(inp)
+    _, sel, cnt = o.score_select(theta=float("-inf"))
+    for r in range(2):
+        c0 = inp["chunk_off"][r]
+        sel_r = sel[c0:c0 + cnt[r]]
+        q_r, w_r = inp["q_refine"][1, r], inp["w_refine"][1, r]
+        topk, sc = o.refine_topk(r, sel_r, q_r, w_r, k=6, want_scores=True)
+        exact, bnd = _exact_refine(inp, r, sel_r, q_r, w_r)
+        assert len(sc) == len(exact) == 4 * len(sel_r)
+        for a, e, b in zip(sc, exact, bnd):
+            assert abs(float(a) - float(e)) <= b + 1e-300
+        # top-k by the exact scores (no near-ties in this data)
+        toks = [c * 4 + t for c in sel_r for t in range(4)]
+        order = sorted(range(len(toks)), key=lambda i: (-exact[i], toks[i]))
+        kth = sorted(exact, reverse=True)
+        if len(kth) > 6:
+            # either an exact tie at 0 (both sides hold +0 exactly, the lower
+            # token wins) or a gap wider than the rounding bound
+            assert (kth[5] == kth[6] == 0) or float(kth[5] - kth[6]) > 2 * max(bnd)
+        want = sorted(toks[i] for i in order[:6])
+        assert list(topk) == want
+
+
+def test_refine_single_head_is_relu_dot():
+    inp = helpers.tiny_inputs(H=1, d=5)
+    o = oracle.Oracle(inp)
+    _, sel, cnt = o.score_select(theta=float("-inf"))
+    q_r = inp["q_refine"][0, 0]
+    _, sc = o.refine_topk(0, sel[:cnt[0]], q_r, np.ones(1, np.float32), k=3, want_scores=True)
+    for i, c in enumerate(np.repeat(sel[:cnt[0]], 4)):
+        t = i % 4
+        key = inp["pages"][c][inp.cfg.ikey_off:].view(np.float32).reshape(4, 5)[t]
+        ref = max(float(np.dot(q_r[0].astype(np.float64), key.astype(np.float64))), 0.0)
+        assert abs(sc[i] - ref) <= 8 * U * float(np.abs(q_r[0] * key).sum())
+
+
+def test_topk_matches_textbook_sort_and_ties():
+    inp = synth.generate(synth.small_config(seq_lens=(9000,), H=4, d=32, Hq=2, Dk=64, Dv=64))
+    o = oracle.Oracle(inp)
+    _, sel, cnt = o.score_select()
+    sel_r = sel[:cnt[0]]
+    toks = [c * 64 + t for c in sel_r for t in range(64)]
+    q_r, w_r = inp["q_refine"][0, 0], inp["w_refine"][0, 0]
+    for k in (1, 17, 256, len(toks) - 1, len(toks), len(toks) + 5):
+        topk, sc = o.refine_topk(0, sel_r, q_r, w_r, k=k, want_scores=True)
+        want = sorted(sorted(range(len(toks)), key=lambda i: (-sc[i], toks[i]))[:k])
+        assert list(topk) == [toks[i] for i in want]
+    # all scores equal (q = 0): the k lowest token indices
+    zq = np.zeros_like(q_r)
+    topk = o.refine_topk(0, sel_r, zq, w_r, k=100)
+    assert list(topk) == toks[:100]
+    # empty candidate set
+    assert len(o.refine_topk(0, sel_r[:0], q_r, w_r, k=100)) == 0
+
+
+# ---------------------------------------------------------------- PIN-6/7/8 attention
+def _units_all(inp, theta, k):
+    o = oracle.Oracle(inp)
+    _, sel, cnt = o.score_select(theta=theta)
+    units = [(r, j) for r in range(inp.cfg.batch) for j in range(inp.cfg.steps)]
+    topk, out, lse = o.decode_units(units, sel, cnt, k, inp.cfg.sm_scale)
+    return units, topk, out, lse
+
+
+@pytest.mark.parametrize("kind", ["f32_sep", "bf16_latent"])
+def test_full_selection_equals_dense_attention(kind):
+    if kind == "f32_sep":
+        inp = helpers.tiny_inputs()
+    else:
+        inp = synth.generate(synth.small_config(seq_lens=(700, 1500), window=256, H=2, d=16,
+                                                Hq=4, steps=2))
+    cfg = inp.cfg
+    units, topk, out, lse = _units_all(inp, float("-inf"), k=10 ** 6)
+    for u, (r, j) in enumerate(units):
+        K, V = helpers.kv_rows(inp, r)
+        q = oracle.decode(cfg.kv_dtype, inp["q_attn"][j, r]).reshape(cfg.Hq, cfg.Dk)
+        o_ref, lse_ref = helpers.dense_attention(q.astype(np.float64), K, V, cfg.sm_scale)
+        assert len(topk[u]) == inp["rs"][r]
+        np.testing.assert_allclose(out[u], o_ref, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse[u], lse_ref, rtol=1e-12)
+
+
+def test_no_selection_equals_sliding_window_attention():
+    inp = synth.generate(synth.small_config(seq_lens=(3000, 1100), window=512, H=2, d=16,
+                                            Hq=4, steps=2))
+    cfg = inp.cfg
+    units, topk, out, lse = _units_all(inp, float("inf"), k=64)
+    for u, (r, j) in enumerate(units):
+        assert len(topk[u]) == 0
+        K, V = helpers.kv_rows(inp, r)
+        rs = inp["rs"][r]
+        q = oracle.decode(cfg.kv_dtype, inp["q_attn"][j, r]).reshape(cfg.Hq, cfg.Dk)
+        o_ref, lse_ref = helpers.dense_attention(q.astype(np.float64), K[rs:], V[rs:], cfg.sm_scale)
+        np.testing.assert_allclose(out[u], o_ref, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse[u], lse_ref, rtol=1e-12)
+
+
+def test_attention_closed_forms():
+    inp = helpers.tiny_inputs(seq_lens=(1, 23))
+    cfg = inp.cfg
+    o = oracle.Oracle(inp)
+    # |A| = 1: output is that V row exactly, lse = sm * q . k
+    q = inp["q_attn"][0, 0]
+    out, lse = o.attend(0, [], q, cfg.sm_scale)
+    K, V = helpers.kv_rows(inp, 0)
+    assert (out == V[0][None, :]).all()
+    np.testing.assert_allclose(lse, cfg.sm_scale * (q.astype(np.float64) @ K[0]), rtol=1e-14)
+    # Q = 0: mean of the attended V rows, lse = ln |A|
+    _, sel, cnt = o.score_select(theta=float("-inf"))
+    c0 = inp["chunk_off"][1]
+    topk = o.refine_topk(1, sel[c0:c0 + cnt[1]], inp["q_refine"][0, 1], inp["w_refine"][0, 1], 3)
+    out, lse = o.attend(1, topk, np.zeros_like(inp["q_attn"][0, 1]), cfg.sm_scale)
+    K, V = helpers.kv_rows(inp, 1)
+    rs = inp["rs"][1]
+    rows = list(topk) + list(range(rs, 23))
+    np.testing.assert_allclose(out, np.broadcast_to(V[rows].mean(axis=0), out.shape), rtol=1e-12)
+    np.testing.assert_allclose(lse, np.log(len(rows)), rtol=1e-14)
+
+
+# ---------------------------------------------------------------- PIN-10 pool
+def test_pool_sim_closed_forms():
+    s = [set(range(10)), set(range(10)), set(range(10))]
+    assert oracle.pool_sim(s, 10) == [10, 0, 0]
+    s = [set(range(0, 5)), set(range(5, 10)), set(range(10, 15))]
+    assert oracle.pool_sim(s, 10) == [5, 5, 5]
+    # a chunk dropped for one window and re-selected while still resident
+    s = [{1, 2}, {2, 3}, {1, 3}]
+    assert oracle.pool_sim(s, 4) == [2, 1, 0]
+    s = [{1, 2}, {3, 4}, {5, 6}, {1, 2}]
+    assert oracle.pool_sim(s, 4) == [2, 2, 2, 2]
+    with pytest.raises(OverflowError):
+        oracle.pool_sim([set(range(6)), set(range(3, 10))], 8)
+
+
+# ---------------------------------------------------------------- PIN-11 determinism
+def test_oracle_deterministic_across_threads():
+    inp = synth.generate(synth.small_config(seq_lens=(6000, 2500), H=4, d=32, Hq=8, steps=2))
+    o = oracle.Oracle(inp)
+    _, sel, cnt = o.score_select()
+    units = [(r, j) for r in range(2) for j in range(2)]
+    a = o.decode_units(units, sel, cnt, 256, inp.cfg.sm_scale, threads=1)
+    b = o.decode_units(units, sel, cnt, 256, inp.cfg.sm_scale, threads=4)
+    for x, y in zip(a[0], b[0]):
+        assert (x == y).all()
+    assert (a[1] == b[1]).all() and (a[2] == b[2]).all()
+
+
+# ---------------------------------------------------------------- generator recipe
+def test_generator_selection_rate_cfg0():
+    """cfg 0: 12 % planted, all planted chunks selected, ~2 % leakage."""
+    inp = synth.generate(synth.config(0), steps=1)
+    z, sel, cnt = oracle.Oracle(inp).score_select()
+    n = int(inp["n_hist"][0])
+    planted = set(inp["planted"][0][0].tolist())
+    chosen = set(sel[:cnt[0]].tolist())
+    assert planted <= chosen
+    leak = len(chosen - planted) / (n - len(planted))
+    assert 0.0 <= leak < 0.08
+    assert 0.10 <= cnt[0] / n <= 0.20
