@@ -1,0 +1,290 @@
+/*
+ * lsa.h -- C-ABI of the Lookahead Sparse Attention (LSA) decode hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is that of "FlashMemory-DeepSeek-V4: Lightning Index
+ * Ultra-Long Context via Lookahead Sparse Attention".  Every 64 decode steps a
+ * memory indexer scores every history chunk against the current query
+ * state.  The chunks whose sigmoid score exceeds 0.5 move from a cold pool
+ * into GPU memory.  At each step a lightning-indexer top-k picks tokens
+ * inside that set, and sparse attention runs over them plus the recent
+ * window.
+ *
+ * Conventions for every entry point:
+ *  - extern "C"; no C++ exception crosses the boundary; every function
+ *    returns an lsa_status (or nothing, for destructors).
+ *  - Pointers marked (device) are HBM addresses; (host) are CPU addresses.
+ *    The caller owns every buffer.  The library keeps no pointer beyond the
+ *    call, except for objects created by lsa_pool_create / lsa_ctx_create,
+ *    which borrow what they are given until destroyed.
+ *  - Streams and events are hipStream_t / hipEvent_t passed as void*.
+ *    NULL means the default stream.  Device work is enqueued
+ *    asynchronously; outputs are valid once the stream reaches that point.
+ *  - Arguments are checked before anything is enqueued.  On an error nothing
+ *    has been enqueued and outputs are untouched.  A HIP launch or copy
+ *    failure returns LSA_ERR_HIP; a kernel fault surfaces at the next
+ *    synchronisation.
+ *  - Calls are reentrant when given distinct outputs and workspaces.
+ *
+ * Geometry (per request r, context L_r, chunk C, recent window W).  The most
+ * recent W tokens are always attended (cjcn.com.cn explainer, section 二, last
+ * paragraph); history is cut into chunks of C tokens ("fixed-size blocks",
+ * ai-feeds.com digest, method section), and a partial chunk next to the
+ * recent window counts as recent:
+ *     rs_r     = C * floor(max(L_r - W, 0) / C)   first recent token
+ *     N_r      = rs_r / C                         history chunks
+ *     R_r      = L_r - rs_r                       recent tokens (W .. W+C-1, or L_r)
+ *     chunk_off[r] = sum_{i<r} N_i,   rec_off[r] = sum_{i<r} R_i
+ * Arrays "over chunks" are concatenated over requests: request r owns
+ * entries [chunk_off[r], chunk_off[r] + N_r).  Recent KV rows likewise own
+ * rows [rec_off[r], rec_off[r] + R_r).
+ *
+ * Pages.  The cold tier and the HBM slot pool store one chunk per page of
+ * page_bytes: C KV rows of row_bytes, then, at byte ikey_off, C index-key
+ * rows of d elements.  A page table maps chunk (chunk_off[r] + c) to a page
+ * index in a page array; NULL means the identity, i.e. the page array is the
+ * cold tier itself.
+ */
+#ifndef LSA_H_
+#define LSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LSA_MAX_BATCH 64
+#define LSA_CHUNK 64
+
+typedef enum {
+    LSA_OK = 0,
+    LSA_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shapes        */
+    LSA_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype or shape)         */
+    LSA_ERR_CAPACITY = -3,    /* slot pool too small for the selection              */
+    LSA_ERR_WORKSPACE = -4,   /* workspace smaller than the lsa_*_ws_bytes query    */
+    LSA_ERR_HIP = -5          /* a HIP runtime call failed                          */
+} lsa_status;
+
+typedef enum { LSA_F32 = 0, LSA_BF16 = 1, LSA_FP8_E4M3FN = 2 } lsa_dtype;
+
+/* Batch geometry.  seq_len is a host array of B contexts (each >= 1); the
+ * library derives rs, N, R and the offsets above from it. */
+typedef struct {
+    int32_t batch;          /* B, 1..LSA_MAX_BATCH                      */
+    int32_t chunk;          /* C, must be LSA_CHUNK (64)                */
+    int32_t window;         /* W >= 0, recent tokens always attended    */
+    const int32_t* seq_len; /* (host) [B]                               */
+} lsa_geom;
+
+/* Layout of one KV row and of a page. */
+typedef struct {
+    lsa_dtype kv_dtype; /* LSA_F32 or LSA_BF16                                    */
+    int32_t Dk;         /* key width: K = elements [0, Dk) of the row               */
+    int32_t Dv;         /* value width                                              */
+    int32_t v_off;      /* V = elements [v_off, v_off+Dv); 0 for a latent row       */
+    int64_t row_bytes;  /* bytes per KV row (>= element size * max(Dk, v_off+Dv))   */
+    int64_t page_bytes; /* bytes per page                                           */
+    int64_t ikey_off;   /* byte offset of the C index-key rows inside a page        */
+} lsa_kv_layout;
+
+const char* lsa_status_str(lsa_status s);
+
+/* ------------------------------------------------------------------------
+ * a2. Chunk scoring.  "Lookahead index score" between the current query and
+ * the compressed index keys (KIComp) of previous chunks: a head-fused
+ * matching score through a sigmoid (gist.science summary, section 2.1,
+ * "Scoring-Mechanismus"); the match is a plain dot product (cjcn.com.cn,
+ * section 六; gist.science, section 5).  Computes the logit of that score:
+ *     qbar[i] = sum_h w[r,h] * q[r,h,i]          (fp32 fma chain over h)
+ *     z[c]    = fma(s_c, sum_i qbar[i]*k_c[i], bias[r])   (fma chain over i)
+ * for every history chunk c of every request; s_c = kic_scale[c] for fp8
+ * keys, else 1.  sigmoid(z) > 0.5 exactly when z > 0.
+ *   q        (device) [B, H, d] in q_dt (LSA_F32 or LSA_BF16)
+ *   w        (device) [B, H] f32;  bias (device) [B] f32
+ *   kic      (device) [sum N, d] in kic_dt (f32, bf16 or fp8 e4m3fn)
+ *   kic_scale(device) [sum N] f32, required iff kic_dt is fp8, else ignored
+ *   z        (device) [sum N] f32 output
+ *   ws       (device) >= lsa_score_ws_bytes(g, d) bytes of scratch
+ * d must be 64 or 128; 1 <= H <= 256.
+ * ---------------------------------------------------------------------- */
+size_t lsa_score_ws_bytes(const lsa_geom* g, int32_t d);
+lsa_status lsa_score_chunks(const lsa_geom* g, const void* q, lsa_dtype q_dt, const float* w,
+                            const float* bias, int32_t H, int32_t d, const void* kic,
+                            lsa_dtype kic_dt, const float* kic_scale, float* z, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * a3. Threshold selection.  A fixed threshold replaces a fixed top-k, so
+ * the number of fetched chunks varies (cjcn.com.cn, section 二; gist.science
+ * 2.1 "Dynamisches Fetching").  Chunk c of request r is selected iff
+ * z[c] > theta (strict); theta = 0 is sigmoid > 0.5.  Output, per request:
+ * the ascending selected chunk ids (0-based within the request) in
+ * sel_ids[chunk_off[r] ...], and their count in sel_cnt[r].
+ *   z (device) [sum N] f32;  sel_ids (device) [sum N] int32;  sel_cnt (device) [B] int32
+ * ---------------------------------------------------------------------- */
+lsa_status lsa_select_threshold(const lsa_geom* g, const float* z, float theta, int32_t* sel_ids,
+                                int32_t* sel_cnt, void* stream);
+
+/* ------------------------------------------------------------------------
+ * a5+a6. Lightning refine and top-k.  Inside the fetched candidate set the
+ * native lightning indexer takes a fine-grained top-k for core attention
+ * (gist.science 2.1 "Gestufte Selektion"; cjcn.com.cn section 二); its score
+ * is a ReLU-weighted sum over heads (cjcn.com.cn section 二 names the ReLU).
+ * For every token s of every selected chunk c (candidate set T, ascending):
+ *     a_h = sum_i q[r,h,i] * key_s[i]  (fp32 fma chain over i, from +0)
+ *     I_s = sum_h w[r,h] * max(a_h, +0) (fp32 fma chain over h, from +0)
+ *     I_s = I_s * ikey_scale[chunk]     (fp8 keys only)
+ * keeps the min(k, |T|) largest I_s, ties to the lower token, and writes
+ * their absolute token positions (c*C + t) ascending.
+ *   sel_ids, sel_cnt (device): as produced by lsa_select_threshold
+ *   pages      (device) page array; index keys of chunk x live in page
+ *              page_table[x] (or x if page_table is NULL) at byte ikey_off
+ *   ikey_scale (device) [sum N] f32, required iff idx_dt is fp8
+ *   q (device) [B, H, d] q_dt;  w (device) [B, H] f32
+ *   topk_idx (device) [B, k] int32 out (first topk_cnt[r] valid); topk_cnt (device) [B] out
+ *   ws (device) >= lsa_refine_ws_bytes(g, k) bytes
+ * d in {64, 128}; 1 <= H <= 128; 1 <= k.
+ * ---------------------------------------------------------------------- */
+size_t lsa_refine_ws_bytes(const lsa_geom* g, int32_t k);
+lsa_status lsa_topk_refine(const lsa_geom* g, const int32_t* sel_ids, const int32_t* sel_cnt,
+                           const void* pages, int64_t page_bytes, int64_t ikey_off,
+                           const int32_t* page_table, lsa_dtype idx_dt, const float* ikey_scale,
+                           const void* q, lsa_dtype q_dt, const float* w, int32_t H, int32_t d,
+                           int32_t k, int32_t* topk_idx, int32_t* topk_cnt, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * a7. Sparse decode attention.  Core attention over the selected tokens plus
+ * the always-resident recent window (gist.science 2.1 "Gestufte Selektion";
+ * cjcn.com.cn section 二 last paragraph and section 五).  All query heads
+ * share one KV (MQA).  With A_r = topk tokens of r followed by [rs_r, L_r):
+ *     o[r,h] = softmax(sm_scale * q[r,h] . K_A^T) V_A,   lse[r,h] = log-sum-exp
+ * accumulated in fp32, written in the KV dtype (RNE).
+ *   q (device) [B, Hq, Dk] kv dtype;  pages/page_table as above (KV rows at
+ *   byte 0 of a page);  recent (device) [sum R, row_bytes]
+ *   topk_idx/topk_cnt (device): as produced by lsa_topk_refine (stride k)
+ *   out (device) [B, Hq, Dv] kv dtype;  lse (device) [B, Hq] f32 or NULL
+ *   n_splits: token splits per request (0 = automatic)
+ *   ws (device) >= lsa_attn_ws_bytes(g, kv, Hq, k, n_splits) bytes
+ * Supported: bf16 latent rows (Dk 576, Dv 512, v_off 0, Hq a multiple of
+ * 32); f32 rows with Dk, Dv <= 256 and Hq <= 16.
+ * ---------------------------------------------------------------------- */
+size_t lsa_attn_ws_bytes(const lsa_geom* g, const lsa_kv_layout* kv, int32_t Hq, int32_t k,
+                         int32_t n_splits);
+lsa_status lsa_sparse_decode_attn(const lsa_geom* g, const void* q, int32_t Hq,
+                                  const lsa_kv_layout* kv, const void* pages,
+                                  const int32_t* page_table, const void* recent,
+                                  const int32_t* topk_idx, const int32_t* topk_cnt, int32_t k,
+                                  float sm_scale, void* out, float* lse, int32_t n_splits,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * a4. Slot pool and candidate fetch.  Selected chunks move from the cold
+ * pool (CPU memory) into GPU memory; the rest stay behind (cjcn.com.cn
+ * section 二 and Q&A 1; gist.science 2.1 "Dynamisches Fetching").
+ * The pool gives request r the slots [r*slots_per_req, (r+1)*slots_per_req)
+ * of slot_mem (device, B*slots_per_req*page_bytes bytes, caller-owned).  The
+ * cold tier holds page (chunk_off[r] + c) for every history chunk; it is
+ * pinned host memory (cold_on_host = 1) or device memory (0).
+ * lsa_pool_create allocates only host bookkeeping and one small device copy
+ * list; it borrows slot_mem and cold until lsa_pool_destroy.
+ * ---------------------------------------------------------------------- */
+typedef struct lsa_pool lsa_pool;
+
+typedef struct {
+    int64_t fetched;  /* chunks copied by the last gather                 */
+    int64_t resident; /* chunks resident after it                         */
+    int64_t evicted;  /* chunks released by it                            */
+    int64_t copies;   /* copy commands issued (runs are coalesced)        */
+    int64_t bytes;    /* bytes copied                                     */
+} lsa_gather_stats;
+
+lsa_status lsa_pool_create(lsa_pool** pool, const lsa_geom* g, void* slot_mem,
+                           int32_t slots_per_req, int64_t page_bytes, const void* cold,
+                           int32_t cold_on_host);
+void lsa_pool_destroy(lsa_pool* pool);
+
+/* Make the chunks in (sel_ids, sel_cnt) resident while keeping the chunks in
+ * (keep_ids, keep_cnt) -- the selection in use by the running window --
+ * untouched.  Every other resident chunk is released.  Missing chunks are
+ * copied on copy_stream after it waits on wait_event (if not NULL: the event
+ * marking that released slots are no longer read).  Then page_table (device,
+ * [sum N] int32) is rewritten for the new selection (slot index, or -1 for
+ * chunks not selected) and done_event (if not NULL) is recorded on
+ * copy_stream.  All id arrays are host arrays in the lsa_select_threshold
+ * layout; keep_* may be NULL (nothing to keep).  If the selection and the
+ * kept set together exceed a request's slots, LSA_ERR_CAPACITY is returned
+ * and the pool is unchanged.  Only one gather per pool may be in flight; the
+ * host part runs synchronously. */
+lsa_status lsa_gather_kv(lsa_pool* pool, const int32_t* sel_ids, const int32_t* sel_cnt,
+                         const int32_t* keep_ids, const int32_t* keep_cnt, int32_t* page_table,
+                         void* copy_stream, void* wait_event, void* done_event,
+                         lsa_gather_stats* stats);
+
+/* ------------------------------------------------------------------------
+ * a1+a8. The window pipeline.  The indexer fires every 64 generation steps
+ * and predicts the history the next 64 steps need (cjcn.com.cn section 二;
+ * gist.science 2.1 "Periodische Triggerung").  A context binds the static
+ * inputs; lsa_ctx_prime scores and fetches the first window; each
+ * lsa_step64 call then runs the decode steps of the current window
+ * (refine + top-k + attention per step) on main_stream while it scores the
+ * next window (if given), fetches its missing chunks on copy_stream, and
+ * builds its page table.  One window ahead, so a window's refill overlaps
+ * the previous window's steps.
+ * ---------------------------------------------------------------------- */
+typedef struct lsa_ctx lsa_ctx;
+
+typedef struct {
+    lsa_geom geom;
+    int32_t H, d;             /* indexer heads and dim                       */
+    lsa_dtype q_dt, idx_dt;   /* indexer query dtype, index key dtype         */
+    int32_t Hq, k;            /* attention heads, top-k                       */
+    lsa_kv_layout kv;         /* KV row and page layout                       */
+    float sm_scale, theta;    /* softmax scale, logit threshold (0 = sig 0.5) */
+    const void* recent;       /* (device) [sum R, row_bytes]                  */
+    const float* ikey_scale;  /* (device) [sum N] (fp8 index keys), else NULL */
+    lsa_pool* pool;           /* slot pool (its cold tier holds the pages)    */
+    void* ws;                 /* (device) >= lsa_ctx_ws_bytes(desc) bytes     */
+    size_t ws_bytes;
+} lsa_ctx_desc;
+
+typedef struct {
+    const void* kic;          /* (device) [sum N, d] KIComp for this scoring  */
+    const float* kic_scale;   /* (device) [sum N] or NULL                      */
+    const void* q;            /* (device) [B, H, d] coarse query               */
+    const float* w;           /* (device) [B, H]                               */
+    const float* bias;        /* (device) [B]                                  */
+} lsa_trigger_in;
+
+typedef struct {
+    int32_t steps;            /* decode steps in this window, 1..64           */
+    const void* q_refine;     /* (device) [steps, B, H, d] q_dt               */
+    const float* w_refine;    /* (device) [steps, B, H]                        */
+    const void* q_attn;       /* (device) [steps, B, Hq, Dk] kv dtype          */
+    const lsa_trigger_in* next; /* next window's trigger, or NULL (last window) */
+} lsa_window_in;
+
+typedef struct {
+    void* out;                /* (device) [steps, B, Hq, Dv] kv dtype          */
+    float* lse;               /* (device) [steps, B, Hq] or NULL               */
+    int32_t* topk_idx;        /* (device) [steps, B, k] or NULL                */
+    int32_t* topk_cnt;        /* (device) [steps, B] or NULL                   */
+    int32_t* sel_cnt;         /* (host) [B] or NULL: the next window's counts  */
+    lsa_gather_stats stats;   /* the next window's fetch                       */
+} lsa_window_out;
+
+size_t lsa_ctx_ws_bytes(const lsa_ctx_desc* desc);
+lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc);
+void lsa_ctx_destroy(lsa_ctx* ctx);
+/* Score, select and fetch the first window (synchronous on the host). */
+lsa_status lsa_ctx_prime(lsa_ctx* ctx, const lsa_trigger_in* first, void* main_stream,
+                         void* copy_stream, lsa_window_out* out);
+lsa_status lsa_step64(lsa_ctx* ctx, const lsa_window_in* in, lsa_window_out* out,
+                      void* main_stream, void* copy_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSA_H_ */

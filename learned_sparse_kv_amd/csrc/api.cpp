@@ -1,0 +1,190 @@
+// C-ABI entry points: argument checks, workspace sizing and dispatch.
+// Every check runs before anything is enqueued; on error nothing is.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "lsa_internal.h"
+
+#define LSA_HIP(x)                                      \
+    do {                                                \
+        if ((x) != hipSuccess) return LSA_ERR_HIP;      \
+    } while (0)
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static int64_t esize(lsa_dtype t) { return t == LSA_F32 ? 4 : (t == LSA_BF16 ? 2 : 1); }
+
+lsa_status geom_derive(const lsa_geom* g, GeomDev* d) {
+    if (!g || !d || !g->seq_len) return LSA_ERR_INVALID_ARG;
+    if (g->batch < 1 || g->batch > LSA_MAX_BATCH) return LSA_ERR_INVALID_ARG;
+    if (g->chunk != LSA_CHUNK || g->window < 0) return LSA_ERR_INVALID_ARG;
+    std::memset(d, 0, sizeof(*d));
+    d->B = g->batch;
+    d->W = g->window;
+    int64_t co = 0, ro = 0;
+    int64_t to = 0;
+    for (int r = 0; r < g->batch; ++r) {
+        const int32_t L = g->seq_len[r];
+        if (L < 1) return LSA_ERR_INVALID_ARG;
+        int64_t h = (int64_t)L - g->window;
+        if (h < 0) h = 0;
+        const int64_t rs = (int64_t)LSA_CHUNK * (h / LSA_CHUNK);
+        d->L[r] = L;
+        d->rs[r] = (int32_t)rs;
+        d->nhist[r] = (int32_t)(rs / LSA_CHUNK);
+        d->nrec[r] = (int32_t)(L - rs);
+        d->chunk_off[r] = co;
+        d->rec_off[r] = ro;
+        d->tile_off[r] = (int32_t)to;
+        co += d->nhist[r];
+        ro += d->nrec[r];
+        to += (d->nhist[r] + 63) / 64;
+    }
+    d->chunk_off[g->batch] = co;
+    d->rec_off[g->batch] = ro;
+    d->tile_off[g->batch] = (int32_t)to;
+    if (co * LSA_CHUNK > INT32_MAX) return LSA_ERR_INVALID_ARG;  // token ids are int32
+    return LSA_OK;
+}
+
+extern "C" {
+
+const char* lsa_status_str(lsa_status s) {
+    switch (s) {
+        case LSA_OK: return "ok";
+        case LSA_ERR_INVALID_ARG: return "invalid argument";
+        case LSA_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+        case LSA_ERR_CAPACITY: return "slot pool capacity exceeded";
+        case LSA_ERR_WORKSPACE: return "workspace too small";
+        case LSA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t lsa_score_ws_bytes(const lsa_geom* g, int32_t d) {
+    if (!g || g->batch < 1 || d < 1) return 0;
+    return align_up((size_t)g->batch * d * sizeof(float), 256);
+}
+
+lsa_status lsa_score_chunks(const lsa_geom* g, const void* q, lsa_dtype q_dt, const float* w,
+                            const float* bias, int32_t H, int32_t d, const void* kic,
+                            lsa_dtype kic_dt, const float* kic_scale, float* z, void* ws,
+                            size_t ws_bytes, void* stream) {
+    GeomDev gd;
+    lsa_status st = geom_derive(g, &gd);
+    if (st != LSA_OK) return st;
+    if (!q || !w || !bias || !ws) return LSA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LSA_ERR_UNSUPPORTED;
+    if (H < 1 || H > 256) return LSA_ERR_INVALID_ARG;
+    if (q_dt != LSA_F32 && q_dt != LSA_BF16) return LSA_ERR_UNSUPPORTED;
+    if (kic_dt != LSA_F32 && kic_dt != LSA_BF16 && kic_dt != LSA_FP8_E4M3FN)
+        return LSA_ERR_UNSUPPORTED;
+    const int64_t n = gd.chunk_off[gd.B];
+    if (n > 0 && (!kic || !z || !aligned16(kic))) return LSA_ERR_INVALID_ARG;
+    if (n > 0 && kic_dt == LSA_FP8_E4M3FN && !kic_scale) return LSA_ERR_INVALID_ARG;
+    if (ws_bytes < lsa_score_ws_bytes(g, d)) return LSA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    float* qbar = (float*)ws;
+    LSA_HIP(launch_fuse_query(gd, q, q_dt, w, H, d, qbar, s));
+    LSA_HIP(launch_score(gd, kic, kic_dt, kic_scale, qbar, bias, d, z, s));
+    return LSA_OK;
+}
+
+lsa_status lsa_select_threshold(const lsa_geom* g, const float* z, float theta, int32_t* sel_ids,
+                                int32_t* sel_cnt, void* stream) {
+    GeomDev gd;
+    lsa_status st = geom_derive(g, &gd);
+    if (st != LSA_OK) return st;
+    if (!sel_cnt) return LSA_ERR_INVALID_ARG;
+    if (gd.chunk_off[gd.B] > 0 && (!z || !sel_ids)) return LSA_ERR_INVALID_ARG;
+    if (theta != theta) return LSA_ERR_INVALID_ARG;  // NaN threshold
+    LSA_HIP(launch_select(gd, z, theta, sel_ids, sel_cnt, (hipStream_t)stream));
+    return LSA_OK;
+}
+
+size_t lsa_refine_ws_bytes(const lsa_geom* g, int32_t k) {
+    GeomDev gd;
+    (void)k;
+    if (geom_derive(g, &gd) != LSA_OK) return 0;
+    return align_up((size_t)gd.chunk_off[gd.B] * LSA_CHUNK * sizeof(float), 256) + 256;
+}
+
+lsa_status lsa_topk_refine(const lsa_geom* g, const int32_t* sel_ids, const int32_t* sel_cnt,
+                           const void* pages, int64_t page_bytes, int64_t ikey_off,
+                           const int32_t* page_table, lsa_dtype idx_dt, const float* ikey_scale,
+                           const void* q, lsa_dtype q_dt, const float* w, int32_t H, int32_t d,
+                           int32_t k, int32_t* topk_idx, int32_t* topk_cnt, void* ws,
+                           size_t ws_bytes, void* stream) {
+    GeomDev gd;
+    lsa_status st = geom_derive(g, &gd);
+    if (st != LSA_OK) return st;
+    if (!sel_cnt || !q || !w || !topk_idx || !topk_cnt || !ws) return LSA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LSA_ERR_UNSUPPORTED;
+    if (H < 1 || H > 128 || k < 1) return LSA_ERR_INVALID_ARG;
+    if (((int64_t)H * d + H) * 4 > 65536) return LSA_ERR_UNSUPPORTED;  // queries fit in LDS
+    if (q_dt != LSA_F32 && q_dt != LSA_BF16) return LSA_ERR_UNSUPPORTED;
+    if (idx_dt != LSA_F32 && idx_dt != LSA_BF16 && idx_dt != LSA_FP8_E4M3FN)
+        return LSA_ERR_UNSUPPORTED;
+    const int64_t n = gd.chunk_off[gd.B];
+    if (n > 0) {
+        if (!sel_ids || !pages || !aligned16(pages)) return LSA_ERR_INVALID_ARG;
+        if (page_bytes < ikey_off + (int64_t)LSA_CHUNK * d * esize(idx_dt)) return LSA_ERR_INVALID_ARG;
+        if (page_bytes % 16 || ikey_off % 16 || ikey_off < 0) return LSA_ERR_INVALID_ARG;
+        if (idx_dt == LSA_FP8_E4M3FN && !ikey_scale) return LSA_ERR_INVALID_ARG;
+    }
+    if (ws_bytes < lsa_refine_ws_bytes(g, k)) return LSA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    float* scores = (float*)ws;
+    if (n > 0)
+        LSA_HIP(launch_refine(gd, sel_ids, sel_cnt, pages, page_bytes, ikey_off, page_table, idx_dt,
+                              ikey_scale, q, q_dt, w, H, d, scores, 0, s));
+    LSA_HIP(launch_topk(gd, sel_ids, sel_cnt, scores, k, topk_idx, topk_cnt, s));
+    return LSA_OK;
+}
+
+static lsa_status check_kv(const lsa_kv_layout* kv) {
+    if (!kv) return LSA_ERR_INVALID_ARG;
+    if (kv->Dk < 1 || kv->Dv < 1 || kv->v_off < 0) return LSA_ERR_INVALID_ARG;
+    const int64_t need = esize(kv->kv_dtype) * (kv->Dk > kv->v_off + kv->Dv ? kv->Dk : kv->v_off + kv->Dv);
+    if (kv->row_bytes < need) return LSA_ERR_INVALID_ARG;
+    if (kv->page_bytes < kv->row_bytes * LSA_CHUNK) return LSA_ERR_INVALID_ARG;
+    return LSA_OK;
+}
+
+size_t lsa_attn_ws_bytes(const lsa_geom* g, const lsa_kv_layout* kv, int32_t Hq, int32_t k,
+                         int32_t n_splits) {
+    GeomDev gd;
+    AttnPlan p;
+    if (geom_derive(g, &gd) != LSA_OK || check_kv(kv) != LSA_OK || k < 1 || Hq < 1) return 0;
+    if (attn_plan(gd, kv, Hq, k, n_splits, &p) != LSA_OK) return 0;
+    return p.part_o_bytes + p.part_ml_bytes;
+}
+
+lsa_status lsa_sparse_decode_attn(const lsa_geom* g, const void* q, int32_t Hq,
+                                  const lsa_kv_layout* kv, const void* pages,
+                                  const int32_t* page_table, const void* recent,
+                                  const int32_t* topk_idx, const int32_t* topk_cnt, int32_t k,
+                                  float sm_scale, void* out, float* lse, int32_t n_splits,
+                                  void* ws, size_t ws_bytes, void* stream) {
+    GeomDev gd;
+    lsa_status st = geom_derive(g, &gd);
+    if (st != LSA_OK) return st;
+    st = check_kv(kv);
+    if (st != LSA_OK) return st;
+    if (!q || !recent || !topk_idx || !topk_cnt || !out || !ws || Hq < 1 || k < 1)
+        return LSA_ERR_INVALID_ARG;
+    if (gd.chunk_off[gd.B] > 0 && !pages) return LSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(recent) || (pages && !aligned16(pages)))
+        return LSA_ERR_INVALID_ARG;
+    if (!(sm_scale == sm_scale) || n_splits < 0) return LSA_ERR_INVALID_ARG;
+    AttnPlan plan;
+    st = attn_plan(gd, kv, Hq, k, n_splits, &plan);
+    if (st != LSA_OK) return st;
+    if (ws_bytes < plan.part_o_bytes + plan.part_ml_bytes) return LSA_ERR_WORKSPACE;
+    LSA_HIP(launch_attn(gd, plan, q, Hq, *kv, pages, page_table, recent, topk_idx, topk_cnt, k,
+                        sm_scale, out, lse, ws, (hipStream_t)stream));
+    return LSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal declarations of the LSA HIP library (gfx950).  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lsa.h"
+
+// Batch geometry derived on the host and passed by value to every kernel
+// (B <= LSA_MAX_BATCH keeps it well under the kernel-argument limit).
+struct GeomDev {
+    int32_t B;
+    int32_t W;
+    int32_t L[LSA_MAX_BATCH];
+    int32_t rs[LSA_MAX_BATCH];       // first recent token
+    int32_t nhist[LSA_MAX_BATCH];    // history chunks
+    int32_t nrec[LSA_MAX_BATCH];     // recent tokens
+    int32_t tile_off[LSA_MAX_BATCH + 1];   // prefix of ceil(nhist/64) (score tiles)
+    int64_t chunk_off[LSA_MAX_BATCH + 1];  // prefix of nhist
+    int64_t rec_off[LSA_MAX_BATCH + 1];    // prefix of nrec
+};
+
+// Fills d from the caller's geometry; returns LSA_OK or LSA_ERR_INVALID_ARG.
+lsa_status geom_derive(const lsa_geom* g, GeomDev* d);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- launchers (each returns the launch error) ----
+hipError_t launch_fuse_query(const GeomDev& g, const void* q, lsa_dtype q_dt, const float* w,
+                             int H, int d, float* qbar, hipStream_t s);
+hipError_t launch_score(const GeomDev& g, const void* kic, lsa_dtype kdt, const float* kscale,
+                        const float* qbar, const float* bias, int d, float* z, hipStream_t s);
+hipError_t launch_select(const GeomDev& g, const float* z, float theta, int32_t* sel,
+                         int32_t* cnt, hipStream_t s);
+
+hipError_t launch_refine(const GeomDev& g, const int32_t* sel, const int32_t* cnt,
+                         const void* pages, int64_t page_bytes, int64_t ikey_off,
+                         const int32_t* page_table, lsa_dtype idx_dt, const float* ikey_scale,
+                         const void* q, lsa_dtype q_dt, const float* w, int H, int d,
+                         float* scores, int grid_hint, hipStream_t s);
+hipError_t launch_topk(const GeomDev& g, const int32_t* sel, const int32_t* cnt,
+                       const float* scores, int k, int32_t* topk, int32_t* tcnt, hipStream_t s);
+
+struct AttnPlan {
+    int mode;        // 0: f32 VALU, 1: bf16 MFMA latent 576/512
+    int n_splits;    // splits per request
+    int per_split;   // positions per split (multiple of the tile)
+    int head_groups; // WGs per (request, split) along heads
+    int P_max;       // k + max recent
+    size_t part_o_bytes, part_ml_bytes;
+};
+lsa_status attn_plan(const GeomDev& g, const lsa_kv_layout* kv, int Hq, int k, int n_splits,
+                     AttnPlan* plan);
+hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, int Hq,
+                       const lsa_kv_layout& kv, const void* pages, const int32_t* page_table,
+                       const void* recent, const int32_t* topk, const int32_t* tcnt, int k,
+                       float sm_scale, void* out, float* lse, void* ws, hipStream_t s);
+
+hipError_t launch_gather(const int32_t* pairs, int n_pairs, const void* src, void* dst,
+                         int64_t page_bytes, hipStream_t s);
+
+// Device slot memory of a pool (pages of the resident chunks).
+void* lsa_pool_slots(const lsa_pool* p);
+int64_t lsa_pool_page_bytes(const lsa_pool* p);
+int32_t lsa_pool_batch(const lsa_pool* p);

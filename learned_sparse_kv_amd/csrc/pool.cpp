@@ -1,0 +1,233 @@
+// HBM slot pool and candidate fetch.
+//
+// Selected chunks move from the cold pool into GPU memory and the rest stay
+// in the cold pool (cjcn.com.cn explainer, section 二 and Q&A 1;
+// gist.science summary, section 2.1 "Dynamisches Fetching").  The pool keeps
+// a chunk -> slot table per request on the host.  A gather releases every
+// resident chunk outside (new selection U kept selection), gives each
+// missing chunk the lowest free slot of its request, and copies it on the
+// copy stream: hipMemcpyAsync per run of consecutive chunks into
+// consecutive slots when the cold tier is pinned host memory (SDMA), or one
+// k_gather launch when it is device memory.  The page table for the new
+// selection then goes up from pinned staging on the same stream.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <vector>
+
+#include "lsa_internal.h"
+
+struct lsa_pool {
+    GeomDev g;
+    int32_t spr = 0;
+    int64_t page_bytes = 0;
+    uint8_t* slots = nullptr;
+    const uint8_t* cold = nullptr;
+    int32_t on_host = 0;
+    std::vector<std::vector<int32_t>> chunk_slot;  // [r][c] slot within r, or -1
+    std::vector<std::vector<int32_t>> slot_chunk;  // [r][s] chunk, or -1
+    std::vector<std::vector<uint8_t>> mark;        // scratch marks [r][c]
+    int32_t* h_pairs = nullptr;                    // pinned [B*spr*2]
+    int32_t* d_pairs = nullptr;                    // device [B*spr*2]
+    int32_t* h_pt = nullptr;                       // pinned [sum N]
+    hipEvent_t staging_done = nullptr;
+    bool staging_pending = false;
+};
+
+void* lsa_pool_slots(const lsa_pool* p) { return p ? p->slots : nullptr; }
+int64_t lsa_pool_page_bytes(const lsa_pool* p) { return p ? p->page_bytes : 0; }
+int32_t lsa_pool_batch(const lsa_pool* p) { return p ? p->g.B : 0; }
+
+extern "C" {
+
+lsa_status lsa_pool_create(lsa_pool** pool, const lsa_geom* g, void* slot_mem,
+                           int32_t slots_per_req, int64_t page_bytes, const void* cold,
+                           int32_t cold_on_host) {
+    if (!pool) return LSA_ERR_INVALID_ARG;
+    *pool = nullptr;
+    GeomDev gd;
+    lsa_status st = geom_derive(g, &gd);
+    if (st != LSA_OK) return st;
+    if (slots_per_req < 1 || page_bytes < 16 || page_bytes % 16) return LSA_ERR_INVALID_ARG;
+    if (!slot_mem || (!cold && gd.chunk_off[gd.B] > 0)) return LSA_ERR_INVALID_ARG;
+    if (((uintptr_t)slot_mem & 15u) || ((uintptr_t)cold & 15u)) return LSA_ERR_INVALID_ARG;
+    if ((int64_t)gd.B * slots_per_req > INT32_MAX / 2) return LSA_ERR_INVALID_ARG;
+    lsa_pool* p = new (std::nothrow) lsa_pool();
+    if (!p) return LSA_ERR_INVALID_ARG;
+    p->g = gd;
+    p->spr = slots_per_req;
+    p->page_bytes = page_bytes;
+    p->slots = (uint8_t*)slot_mem;
+    p->cold = (const uint8_t*)cold;
+    p->on_host = cold_on_host ? 1 : 0;
+    p->chunk_slot.resize(gd.B);
+    p->slot_chunk.resize(gd.B);
+    p->mark.resize(gd.B);
+    for (int r = 0; r < gd.B; ++r) {
+        p->chunk_slot[r].assign(gd.nhist[r], -1);
+        p->slot_chunk[r].assign(slots_per_req, -1);
+        p->mark[r].assign(gd.nhist[r], 0);
+    }
+    const size_t npairs = (size_t)gd.B * slots_per_req;
+    const size_t nh = (size_t)(gd.chunk_off[gd.B] > 0 ? gd.chunk_off[gd.B] : 1);
+    if (hipHostMalloc((void**)&p->h_pairs, npairs * 2 * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
+        hipHostMalloc((void**)&p->h_pt, nh * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
+        hipMalloc((void**)&p->d_pairs, npairs * 2 * sizeof(int32_t)) != hipSuccess ||
+        hipEventCreateWithFlags(&p->staging_done, hipEventDisableTiming) != hipSuccess) {
+        lsa_pool_destroy(p);
+        return LSA_ERR_HIP;
+    }
+    *pool = p;
+    return LSA_OK;
+}
+
+void lsa_pool_destroy(lsa_pool* p) {
+    if (!p) return;
+    if (p->staging_done) {
+        if (p->staging_pending) (void)hipEventSynchronize(p->staging_done);
+        (void)hipEventDestroy(p->staging_done);
+    }
+    if (p->h_pairs) (void)hipHostFree(p->h_pairs);
+    if (p->h_pt) (void)hipHostFree(p->h_pt);
+    if (p->d_pairs) (void)hipFree(p->d_pairs);
+    delete p;
+}
+
+lsa_status lsa_gather_kv(lsa_pool* p, const int32_t* sel_ids, const int32_t* sel_cnt,
+                         const int32_t* keep_ids, const int32_t* keep_cnt, int32_t* page_table,
+                         void* copy_stream, void* wait_event, void* done_event,
+                         lsa_gather_stats* stats) {
+    if (!p || !sel_cnt || !page_table) return LSA_ERR_INVALID_ARG;
+    const GeomDev& g = p->g;
+    const int64_t nh = g.chunk_off[g.B];
+    if (nh > 0 && !sel_ids) return LSA_ERR_INVALID_ARG;
+    if ((keep_ids == nullptr) != (keep_cnt == nullptr)) return LSA_ERR_INVALID_ARG;
+    // ---- validate everything and check capacity before touching the pool ----
+    for (int r = 0; r < g.B; ++r) {
+        const int n = g.nhist[r];
+        const int32_t* s = sel_ids + g.chunk_off[r];
+        if (sel_cnt[r] < 0 || sel_cnt[r] > n) return LSA_ERR_INVALID_ARG;
+        for (int i = 0; i < sel_cnt[r]; ++i)
+            if (s[i] < 0 || s[i] >= n || (i > 0 && s[i] <= s[i - 1])) return LSA_ERR_INVALID_ARG;
+        int need = sel_cnt[r];
+        std::vector<uint8_t>& mk = p->mark[r];
+        for (int i = 0; i < sel_cnt[r]; ++i) mk[s[i]] = 1;
+        if (keep_ids) {
+            const int32_t* kp = keep_ids + g.chunk_off[r];
+            if (keep_cnt[r] < 0 || keep_cnt[r] > n) {
+                for (int i = 0; i < sel_cnt[r]; ++i) mk[s[i]] = 0;
+                return LSA_ERR_INVALID_ARG;
+            }
+            for (int i = 0; i < keep_cnt[r]; ++i) {
+                const int32_t c = kp[i];
+                if (c >= 0 && c < n && !mk[c] && p->chunk_slot[r][c] >= 0) {
+                    mk[c] = 2;
+                    ++need;
+                }
+            }
+            for (int i = 0; i < keep_cnt[r]; ++i) {
+                const int32_t c = kp[i];
+                if (c >= 0 && c < n && mk[c] == 2) mk[c] = 0;
+            }
+        }
+        for (int i = 0; i < sel_cnt[r]; ++i) mk[s[i]] = 0;
+        if (need > p->spr) return LSA_ERR_CAPACITY;
+    }
+    if (p->staging_pending) {
+        if (hipEventSynchronize(p->staging_done) != hipSuccess) return LSA_ERR_HIP;
+        p->staging_pending = false;
+    }
+    // ---- update residency ----
+    lsa_gather_stats st{};
+    int npairs = 0;
+    for (int r = 0; r < g.B; ++r) {
+        const int n = g.nhist[r];
+        const int32_t* s = sel_ids + g.chunk_off[r];
+        std::vector<uint8_t>& mk = p->mark[r];
+        std::vector<int32_t>& cs = p->chunk_slot[r];
+        std::vector<int32_t>& sc = p->slot_chunk[r];
+        for (int i = 0; i < sel_cnt[r]; ++i) mk[s[i]] = 1;
+        if (keep_ids) {
+            const int32_t* kp = keep_ids + g.chunk_off[r];
+            for (int i = 0; i < keep_cnt[r]; ++i)
+                if (kp[i] >= 0 && kp[i] < n) mk[kp[i]] |= 2;
+        }
+        for (int sl = 0; sl < p->spr; ++sl) {
+            const int32_t c = sc[sl];
+            if (c >= 0 && !mk[c]) {
+                sc[sl] = -1;
+                cs[c] = -1;
+                ++st.evicted;
+            }
+        }
+        int cursor = 0;
+        for (int i = 0; i < sel_cnt[r]; ++i) {
+            const int32_t c = s[i];
+            if (cs[c] >= 0) continue;
+            while (sc[cursor] >= 0) ++cursor;  // capacity was checked above
+            sc[cursor] = c;
+            cs[c] = cursor;
+            p->h_pairs[2 * npairs] = (int32_t)(g.chunk_off[r] + c);
+            p->h_pairs[2 * npairs + 1] = r * p->spr + cursor;
+            ++npairs;
+        }
+        for (int i = 0; i < sel_cnt[r]; ++i) mk[s[i]] = 0;
+        if (keep_ids) {
+            const int32_t* kp = keep_ids + g.chunk_off[r];
+            for (int i = 0; i < keep_cnt[r]; ++i)
+                if (kp[i] >= 0 && kp[i] < n) mk[kp[i]] = 0;
+        }
+        for (int sl = 0; sl < p->spr; ++sl) st.resident += sc[sl] >= 0;
+    }
+    st.fetched = npairs;
+    st.bytes = (int64_t)npairs * p->page_bytes;
+    // ---- copies on the copy stream ----
+    hipStream_t cs = (hipStream_t)copy_stream;
+    if (wait_event && hipStreamWaitEvent(cs, (hipEvent_t)wait_event, 0) != hipSuccess)
+        return LSA_ERR_HIP;
+    if (npairs > 0) {
+        if (p->on_host) {
+            int i = 0;
+            while (i < npairs) {
+                int j = i + 1;
+                while (j < npairs && p->h_pairs[2 * j] == p->h_pairs[2 * (j - 1)] + 1 &&
+                       p->h_pairs[2 * j + 1] == p->h_pairs[2 * (j - 1) + 1] + 1)
+                    ++j;
+                const int64_t src = p->h_pairs[2 * i], dst = p->h_pairs[2 * i + 1];
+                if (hipMemcpyAsync(p->slots + dst * p->page_bytes, p->cold + src * p->page_bytes,
+                                   (size_t)(j - i) * p->page_bytes, hipMemcpyHostToDevice,
+                                   cs) != hipSuccess)
+                    return LSA_ERR_HIP;
+                ++st.copies;
+                i = j;
+            }
+        } else {
+            if (hipMemcpyAsync(p->d_pairs, p->h_pairs, (size_t)npairs * 2 * sizeof(int32_t),
+                               hipMemcpyHostToDevice, cs) != hipSuccess)
+                return LSA_ERR_HIP;
+            if (launch_gather(p->d_pairs, npairs, p->cold, p->slots, p->page_bytes, cs) !=
+                hipSuccess)
+                return LSA_ERR_HIP;
+            st.copies = 1;
+        }
+    }
+    // ---- page table of the new selection ----
+    if (nh > 0) {
+        for (int64_t i = 0; i < nh; ++i) p->h_pt[i] = -1;
+        for (int r = 0; r < g.B; ++r) {
+            const int32_t* s = sel_ids + g.chunk_off[r];
+            for (int i = 0; i < sel_cnt[r]; ++i)
+                p->h_pt[g.chunk_off[r] + s[i]] = r * p->spr + p->chunk_slot[r][s[i]];
+        }
+        if (hipMemcpyAsync(page_table, p->h_pt, (size_t)nh * sizeof(int32_t),
+                           hipMemcpyHostToDevice, cs) != hipSuccess)
+            return LSA_ERR_HIP;
+    }
+    if (hipEventRecord(p->staging_done, cs) != hipSuccess) return LSA_ERR_HIP;
+    p->staging_pending = true;
+    if (done_event && hipEventRecord((hipEvent_t)done_event, cs) != hipSuccess) return LSA_ERR_HIP;
+    if (stats) *stats = st;
+    return LSA_OK;
+}
+
+}  // extern "C"

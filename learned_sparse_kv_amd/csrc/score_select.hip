@@ -1,0 +1,211 @@
+// Chunk scoring and threshold selection (gfx950).
+//
+// The memory indexer's lookahead score between the current query state and
+// each history chunk's compressed index key is a head-fused matching score
+// through a sigmoid (gist.science summary, section 2.1); every chunk whose
+// score exceeds 0.5 is fetched (cjcn.com.cn explainer, section 二).  The
+// score's logit is a dot product of one KIComp row with the head-fused query
+//     qbar = sum_h w_h q_h,   z_c = fma(s_c, qbar . k_c, b),
+// and sigmoid(z) > 0.5 exactly when z > 0.
+//
+// Arithmetic order (shared by definition with the CPU oracle, not by code):
+// fp32, IEEE fma chains from +0 over h (fusion) and over i (dot product), no
+// denormal flush, no other contraction.  One lane owns one chunk so each
+// dot product is a plain sequential chain.
+//
+// k_score streams KIComp from HBM: one wave per tile of 64 chunks, rows
+// loaded with coalesced 16-byte loads into a wave-private LDS tile, then
+// read back one row per lane.  1 (bf16) to 2 (fp8) flop per byte: HBM-bound.
+#include "lsa_internal.h"
+
+namespace {
+
+__device__ __forceinline__ float bf16f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+template <int QDT>
+__global__ void k_fuse_query(GeomDev g, const void* __restrict__ q, const float* __restrict__ w,
+                             int H, int d, float* __restrict__ qbar) {
+    const int r = blockIdx.x;
+    const int i = threadIdx.x;
+    if (i >= d) return;
+    float acc = 0.0f;
+    for (int h = 0; h < H; ++h) {
+        const size_t e = ((size_t)r * H + h) * d + i;
+        float qv;
+        if constexpr (QDT == LSA_F32)
+            qv = ((const float*)q)[e];
+        else
+            qv = bf16f(((const uint16_t*)q)[e]);
+        acc = __builtin_fmaf(w[(size_t)r * H + h], qv, acc);
+    }
+    qbar[(size_t)r * d + i] = acc;
+}
+
+// Dot product of a row held as 16-byte pieces (ROWB bytes) with qbar, as a
+// sequential fma chain in element order.
+template <int KDT, int D>
+__device__ __forceinline__ float row_dot(const uint4* __restrict__ row,
+                                         const float* __restrict__ qb) {
+    float acc = 0.0f;
+    if constexpr (KDT == LSA_F32) {
+#pragma unroll
+        for (int j = 0; j < D / 4; ++j) {
+            const uint4 v = row[j];
+            acc = __builtin_fmaf(qb[4 * j + 0], __uint_as_float(v.x), acc);
+            acc = __builtin_fmaf(qb[4 * j + 1], __uint_as_float(v.y), acc);
+            acc = __builtin_fmaf(qb[4 * j + 2], __uint_as_float(v.z), acc);
+            acc = __builtin_fmaf(qb[4 * j + 3], __uint_as_float(v.w), acc);
+        }
+    } else if constexpr (KDT == LSA_BF16) {
+#pragma unroll
+        for (int j = 0; j < D / 8; ++j) {
+            const uint4 v = row[j];
+            const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc = __builtin_fmaf(qb[8 * j + 2 * e], __uint_as_float(wds[e] << 16), acc);
+                acc = __builtin_fmaf(qb[8 * j + 2 * e + 1], __uint_as_float(wds[e] & 0xffff0000u),
+                                     acc);
+            }
+        }
+    } else {  // fp8 e4m3fn (OCP), converted exactly to fp32 by the hardware
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+            const uint4 v = row[j];
+            const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wds[e], false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wds[e], true);
+                acc = __builtin_fmaf(qb[16 * j + 4 * e + 0], lo[0], acc);
+                acc = __builtin_fmaf(qb[16 * j + 4 * e + 1], lo[1], acc);
+                acc = __builtin_fmaf(qb[16 * j + 4 * e + 2], hi[0], acc);
+                acc = __builtin_fmaf(qb[16 * j + 4 * e + 3], hi[1], acc);
+            }
+        }
+    }
+    return acc;
+}
+
+// Waves per block so that the block's LDS tiles stay near 36 KB.
+template <int KDT, int D>
+constexpr int score_waves() {
+    constexpr int rowb = D * (KDT == LSA_F32 ? 4 : (KDT == LSA_BF16 ? 2 : 1));
+    return rowb <= 128 ? 4 : (rowb <= 256 ? 2 : 1);
+}
+
+template <int KDT, int D>
+__global__ __launch_bounds__((64 * score_waves<KDT, D>())) void k_score(
+    GeomDev g, const uint8_t* __restrict__ kic, const float* __restrict__ kscale,
+    const float* __restrict__ qbar, const float* __restrict__ bias, float* __restrict__ z) {
+    constexpr int kScoreWaves = score_waves<KDT, D>();
+    constexpr int EB = KDT == LSA_F32 ? 4 : (KDT == LSA_BF16 ? 2 : 1);
+    constexpr int ROWB = D * EB;          // bytes per KIComp row
+    constexpr int PIECES = ROWB / 16;     // 16-byte pieces per row
+    constexpr int STRIDE = ROWB + 16;     // padded LDS row (conflict-free reads)
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kScoreWaves][64 * STRIDE];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int gt = blockIdx.x * kScoreWaves + wv;  // global tile of 64 chunks
+    if (gt >= g.tile_off[g.B]) return;             // whole wave leaves together
+    int r = 0;
+    while (gt >= g.tile_off[r + 1]) ++r;
+    r = __builtin_amdgcn_readfirstlane(r);
+    const int c0 = (gt - g.tile_off[r]) * 64;
+    const int nvalid = min(64, g.nhist[r] - c0);
+    const int64_t row0 = g.chunk_off[r] + c0;
+
+    // coalesced load of the tile (nvalid rows, contiguous) into LDS
+    const uint4* src = (const uint4*)(kic + row0 * ROWB);
+    uint8_t* t = tile[wv];
+#pragma unroll
+    for (int j = 0; j < PIECES; ++j) {
+        const int piece = j * 64 + lane;          // 16-byte piece index in the tile
+        const int rr = piece / PIECES, cc = piece % PIECES;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (rr < nvalid) v = src[piece];
+        *(uint4*)(t + rr * STRIDE + cc * 16) = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    if (lane >= nvalid) return;
+    const float* qb = qbar + (size_t)r * D;
+    const float acc = row_dot<KDT, D>((const uint4*)(t + lane * STRIDE), qb);
+    const int64_t c = row0 + lane;
+    const float s = (KDT == LSA_FP8_E4M3FN) ? kscale[c] : 1.0f;
+    z[c] = __builtin_fmaf(s, acc, bias[r]);
+}
+
+// Ordered stream compaction of {c : z_c > theta} per request: wave ballot,
+// in-wave rank by popcount, wave totals through LDS.  One block per request.
+__global__ __launch_bounds__(1024) void k_select(GeomDev g, const float* __restrict__ z,
+                                                 float theta, int32_t* __restrict__ sel,
+                                                 int32_t* __restrict__ cnt) {
+    __shared__ int wsum[16];
+    const int r = blockIdx.x;
+    const int n = g.nhist[r];
+    const int64_t off = g.chunk_off[r];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int base = 0;
+    for (int c0 = 0; c0 < n; c0 += 1024) {
+        const int c = c0 + (int)threadIdx.x;
+        const bool f = (c < n) && (z[off + c] > theta);
+        const uint64_t m = __ballot(f);
+        const int pre = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == 0) wsum[wv] = __popcll(m);
+        __syncthreads();
+        int wpre = 0, tot = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int v = wsum[i];
+            wpre += (i < wv) ? v : 0;
+            tot += v;
+        }
+        if (f) sel[off + base + wpre + pre] = c;
+        base += tot;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) cnt[r] = base;
+}
+
+}  // namespace
+
+hipError_t launch_fuse_query(const GeomDev& g, const void* q, lsa_dtype q_dt, const float* w,
+                             int H, int d, float* qbar, hipStream_t s) {
+    if (q_dt == LSA_F32)
+        hipLaunchKernelGGL(k_fuse_query<LSA_F32>, dim3(g.B), dim3(128), 0, s, g, q, w, H, d, qbar);
+    else
+        hipLaunchKernelGGL(k_fuse_query<LSA_BF16>, dim3(g.B), dim3(128), 0, s, g, q, w, H, d, qbar);
+    return hipGetLastError();
+}
+
+hipError_t launch_score(const GeomDev& g, const void* kic, lsa_dtype kdt, const float* kscale,
+                        const float* qbar, const float* bias, int d, float* z, hipStream_t s) {
+    const int tiles = g.tile_off[g.B];
+    if (tiles == 0) return hipSuccess;
+    const uint8_t* k = (const uint8_t*)kic;
+#define LSA_SCORE_CASE(KDT, D)                                                                  \
+    if (kdt == KDT && d == D) {                                                                 \
+        constexpr int nw = score_waves<KDT, D>();                                               \
+        hipLaunchKernelGGL((k_score<KDT, D>), dim3((tiles + nw - 1) / nw), dim3(64 * nw), 0, s, \
+                           g, k, kscale, qbar, bias, z);                                        \
+        return hipGetLastError();                                                               \
+    }
+    LSA_SCORE_CASE(LSA_F32, 64)
+    LSA_SCORE_CASE(LSA_F32, 128)
+    LSA_SCORE_CASE(LSA_BF16, 64)
+    LSA_SCORE_CASE(LSA_BF16, 128)
+    LSA_SCORE_CASE(LSA_FP8_E4M3FN, 64)
+    LSA_SCORE_CASE(LSA_FP8_E4M3FN, 128)
+#undef LSA_SCORE_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_select(const GeomDev& g, const float* z, float theta, int32_t* sel,
+                         int32_t* cnt, hipStream_t s) {
+    hipLaunchKernelGGL(k_select, dim3(g.B), dim3(1024), 0, s, g, z, theta, sel, cnt);
+    return hipGetLastError();
+}

@@ -1,0 +1,271 @@
+// The window pipeline (lsa_step64).
+//
+// The memory indexer fires every 64 generation steps and predicts which
+// history chunks the next 64 steps need; only those are moved from the CPU
+// cold pool into GPU memory (cjcn.com.cn explainer, section 二; gist.science
+// summary, section 2.1 "Periodische Triggerung").  Here the prediction runs
+// one window ahead: while window m's decode steps run on the main stream,
+// window m+1 is scored and selected (main stream, before the steps), its
+// selection comes back to the host, and its missing chunks are copied on the
+// copy stream into slots that window m does not read.  Window m+1 waits for
+// that copy only when it starts.  Two page tables and two selection buffers
+// alternate between windows.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <new>
+
+#include "lsa_internal.h"
+
+struct lsa_ctx {
+    lsa_ctx_desc d;
+    GeomDev g;
+    AttnPlan plan;
+    int64_t nh = 0;
+    float* qbar = nullptr;
+    float* z = nullptr;
+    int32_t* sel[2] = {nullptr, nullptr};
+    int32_t* cnt[2] = {nullptr, nullptr};
+    float* scores = nullptr;
+    int32_t* topk_tmp = nullptr;
+    int32_t* tcnt_tmp = nullptr;
+    void* attn_ws = nullptr;
+    int32_t* pt[2] = {nullptr, nullptr};
+    int32_t* h_sel[2] = {nullptr, nullptr};
+    int32_t* h_cnt[2] = {nullptr, nullptr};
+    hipEvent_t ev_sel = nullptr, ev_win[2] = {nullptr, nullptr}, ev_fetch[2] = {nullptr, nullptr};
+    int cur = 0;
+    bool primed = false;
+    bool have_next = false;
+};
+
+namespace {
+
+int64_t esz(lsa_dtype t) { return t == LSA_F32 ? 4 : (t == LSA_BF16 ? 2 : 1); }
+
+struct Carve {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        const size_t o = off;
+        off += align_up(bytes ? bytes : 1, 256);
+        return o;
+    }
+};
+
+// Workspace layout; returns total bytes (0 on invalid description).
+size_t layout(const lsa_ctx_desc* d, GeomDev* g, AttnPlan* plan, size_t offs[12]) {
+    if (!d) return 0;
+    if (geom_derive(&d->geom, g) != LSA_OK) return 0;
+    if (attn_plan(*g, &d->kv, d->Hq, d->k, 0, plan) != LSA_OK) return 0;
+    const int64_t nh = g->chunk_off[g->B];
+    const int B = g->B;
+    Carve c;
+    offs[0] = c.take((size_t)B * d->d * 4);             // qbar
+    offs[1] = c.take((size_t)nh * 4);                   // z
+    offs[2] = c.take((size_t)nh * 4);                   // sel[0]
+    offs[3] = c.take((size_t)nh * 4);                   // sel[1]
+    offs[4] = c.take((size_t)B * 4);                    // cnt[0]
+    offs[5] = c.take((size_t)B * 4);                    // cnt[1]
+    offs[6] = c.take((size_t)nh * LSA_CHUNK * 4);       // refine scores
+    offs[7] = c.take((size_t)B * d->k * 4);             // top-k scratch
+    offs[8] = c.take((size_t)B * 4);                    // top-k counts scratch
+    offs[9] = c.take(plan->part_o_bytes + plan->part_ml_bytes);  // attention partials
+    offs[10] = c.take((size_t)nh * 4);                  // page table 0
+    offs[11] = c.take((size_t)nh * 4);                  // page table 1
+    return c.off;
+}
+
+lsa_status score_select(lsa_ctx* x, const lsa_trigger_in* t, int buf, hipStream_t s) {
+    const lsa_ctx_desc& d = x->d;
+    if (!t || !t->q || !t->w || !t->bias) return LSA_ERR_INVALID_ARG;
+    if (x->nh > 0 && !t->kic) return LSA_ERR_INVALID_ARG;
+    if (x->nh > 0 && d.idx_dt == LSA_FP8_E4M3FN && !t->kic_scale) return LSA_ERR_INVALID_ARG;
+    if (launch_fuse_query(x->g, t->q, d.q_dt, t->w, d.H, d.d, x->qbar, s) != hipSuccess)
+        return LSA_ERR_HIP;
+    if (launch_score(x->g, t->kic, d.idx_dt, t->kic_scale, x->qbar, t->bias, d.d, x->z, s) !=
+        hipSuccess)
+        return LSA_ERR_HIP;
+    if (launch_select(x->g, x->z, d.theta, x->sel[buf], x->cnt[buf], s) != hipSuccess)
+        return LSA_ERR_HIP;
+    if (x->nh > 0 && hipMemcpyAsync(x->h_sel[buf], x->sel[buf], (size_t)x->nh * 4,
+                                    hipMemcpyDeviceToHost, s) != hipSuccess)
+        return LSA_ERR_HIP;
+    if (hipMemcpyAsync(x->h_cnt[buf], x->cnt[buf], (size_t)x->g.B * 4, hipMemcpyDeviceToHost, s) !=
+        hipSuccess)
+        return LSA_ERR_HIP;
+    if (hipEventRecord(x->ev_sel, s) != hipSuccess) return LSA_ERR_HIP;
+    return LSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lsa_ctx_ws_bytes(const lsa_ctx_desc* desc) {
+    GeomDev g;
+    AttnPlan p;
+    size_t offs[12];
+    return layout(desc, &g, &p, offs);
+}
+
+lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc) {
+    if (!ctx || !desc) return LSA_ERR_INVALID_ARG;
+    *ctx = nullptr;
+    GeomDev g;
+    AttnPlan plan;
+    size_t offs[12];
+    lsa_status st = geom_derive(&desc->geom, &g);
+    if (st != LSA_OK) return st;
+    if (desc->d != 64 && desc->d != 128) return LSA_ERR_UNSUPPORTED;
+    if (desc->H < 1 || desc->H > 128 || desc->k < 1 || desc->Hq < 1) return LSA_ERR_INVALID_ARG;
+    if (desc->q_dt != LSA_F32 && desc->q_dt != LSA_BF16) return LSA_ERR_UNSUPPORTED;
+    if (!desc->pool || !desc->recent || !desc->ws) return LSA_ERR_INVALID_ARG;
+    if (desc->idx_dt == LSA_FP8_E4M3FN && !desc->ikey_scale && g.chunk_off[g.B] > 0)
+        return LSA_ERR_INVALID_ARG;
+    if (desc->kv.ikey_off % 16 || desc->kv.page_bytes % 16) return LSA_ERR_INVALID_ARG;
+    if (((int64_t)desc->H * desc->d + desc->H) * 4 > 65536) return LSA_ERR_UNSUPPORTED;
+    if (desc->kv.ikey_off < (int64_t)LSA_CHUNK * desc->kv.row_bytes ||
+        desc->kv.page_bytes < desc->kv.ikey_off + (int64_t)LSA_CHUNK * desc->d * esz(desc->idx_dt))
+        return LSA_ERR_INVALID_ARG;
+    if (lsa_pool_page_bytes(desc->pool) != desc->kv.page_bytes ||
+        lsa_pool_batch(desc->pool) != g.B)
+        return LSA_ERR_INVALID_ARG;
+    st = attn_plan(g, &desc->kv, desc->Hq, desc->k, 0, &plan);
+    if (st != LSA_OK) return st;
+    const size_t need = layout(desc, &g, &plan, offs);
+    if (need == 0) return LSA_ERR_INVALID_ARG;
+    if (desc->ws_bytes < need) return LSA_ERR_WORKSPACE;
+    lsa_ctx* x = new (std::nothrow) lsa_ctx();
+    if (!x) return LSA_ERR_INVALID_ARG;
+    x->d = *desc;
+    x->g = g;
+    x->plan = plan;
+    x->nh = g.chunk_off[g.B];
+    uint8_t* base = (uint8_t*)desc->ws;
+    x->qbar = (float*)(base + offs[0]);
+    x->z = (float*)(base + offs[1]);
+    x->sel[0] = (int32_t*)(base + offs[2]);
+    x->sel[1] = (int32_t*)(base + offs[3]);
+    x->cnt[0] = (int32_t*)(base + offs[4]);
+    x->cnt[1] = (int32_t*)(base + offs[5]);
+    x->scores = (float*)(base + offs[6]);
+    x->topk_tmp = (int32_t*)(base + offs[7]);
+    x->tcnt_tmp = (int32_t*)(base + offs[8]);
+    x->attn_ws = base + offs[9];
+    x->pt[0] = (int32_t*)(base + offs[10]);
+    x->pt[1] = (int32_t*)(base + offs[11]);
+    const size_t nhb = (size_t)(x->nh > 0 ? x->nh : 1) * 4;
+    bool ok = true;
+    for (int i = 0; i < 2 && ok; ++i) {
+        ok = hipHostMalloc((void**)&x->h_sel[i], nhb, hipHostMallocDefault) == hipSuccess &&
+             hipHostMalloc((void**)&x->h_cnt[i], (size_t)g.B * 4, hipHostMallocDefault) == hipSuccess &&
+             hipEventCreateWithFlags(&x->ev_win[i], hipEventDisableTiming) == hipSuccess &&
+             hipEventCreateWithFlags(&x->ev_fetch[i], hipEventDisableTiming) == hipSuccess;
+    }
+    ok = ok && hipEventCreateWithFlags(&x->ev_sel, hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+        lsa_ctx_destroy(x);
+        return LSA_ERR_HIP;
+    }
+    *ctx = x;
+    return LSA_OK;
+}
+
+void lsa_ctx_destroy(lsa_ctx* x) {
+    if (!x) return;
+    for (int i = 0; i < 2; ++i) {
+        if (x->ev_win[i]) (void)hipEventSynchronize(x->ev_win[i]);
+        if (x->ev_fetch[i]) (void)hipEventSynchronize(x->ev_fetch[i]);
+    }
+    for (int i = 0; i < 2; ++i) {
+        if (x->h_sel[i]) (void)hipHostFree(x->h_sel[i]);
+        if (x->h_cnt[i]) (void)hipHostFree(x->h_cnt[i]);
+        if (x->ev_win[i]) (void)hipEventDestroy(x->ev_win[i]);
+        if (x->ev_fetch[i]) (void)hipEventDestroy(x->ev_fetch[i]);
+    }
+    if (x->ev_sel) (void)hipEventDestroy(x->ev_sel);
+    delete x;
+}
+
+lsa_status lsa_ctx_prime(lsa_ctx* x, const lsa_trigger_in* first, void* main_stream,
+                         void* copy_stream, lsa_window_out* out) {
+    if (!x || !first) return LSA_ERR_INVALID_ARG;
+    hipStream_t ms = (hipStream_t)main_stream;
+    x->cur = 0;
+    lsa_status st = score_select(x, first, 0, ms);
+    if (st != LSA_OK) return st;
+    if (hipEventRecord(x->ev_win[0], ms) != hipSuccess || hipEventRecord(x->ev_win[1], ms) != hipSuccess)
+        return LSA_ERR_HIP;
+    if (hipEventSynchronize(x->ev_sel) != hipSuccess) return LSA_ERR_HIP;
+    lsa_gather_stats gs{};
+    st = lsa_gather_kv(x->d.pool, x->h_sel[0], x->h_cnt[0], nullptr, nullptr, x->pt[0],
+                       copy_stream, nullptr, x->ev_fetch[0], &gs);
+    if (st != LSA_OK) return st;
+    if (out) {
+        out->stats = gs;
+        if (out->sel_cnt) std::memcpy(out->sel_cnt, x->h_cnt[0], (size_t)x->g.B * 4);
+    }
+    x->primed = true;
+    x->have_next = true;
+    return LSA_OK;
+}
+
+lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
+                      void* main_stream, void* copy_stream) {
+    if (!x || !in || !out || !out->out) return LSA_ERR_INVALID_ARG;
+    if (!x->primed || !x->have_next) return LSA_ERR_INVALID_ARG;  // no selected window to run
+    if (in->steps < 1 || in->steps > 64 || !in->q_refine || !in->w_refine || !in->q_attn)
+        return LSA_ERR_INVALID_ARG;
+    const lsa_ctx_desc& d = x->d;
+    const GeomDev& g = x->g;
+    hipStream_t ms = (hipStream_t)main_stream;
+    const int cur = x->cur, nxt = cur ^ 1;
+
+    if (hipStreamWaitEvent(ms, x->ev_fetch[cur], 0) != hipSuccess) return LSA_ERR_HIP;
+    if (in->next) {
+        lsa_status st = score_select(x, in->next, nxt, ms);
+        if (st != LSA_OK) return st;
+    }
+    int groups = 0;
+    for (int r = 0; r < g.B; ++r) groups += (x->h_cnt[cur][r] + 3) / 4;
+    const size_t qr_step = (size_t)g.B * d.H * d.d * esz(d.q_dt);
+    const size_t qa_step = (size_t)g.B * d.Hq * d.kv.Dk * esz(d.kv.kv_dtype);
+    const size_t o_step = (size_t)g.B * d.Hq * d.kv.Dv * esz(d.kv.kv_dtype);
+    for (int j = 0; j < in->steps; ++j) {
+        int32_t* tk = out->topk_idx ? out->topk_idx + (size_t)j * g.B * d.k : x->topk_tmp;
+        int32_t* tc = out->topk_cnt ? out->topk_cnt + (size_t)j * g.B : x->tcnt_tmp;
+        const uint8_t* qr = (const uint8_t*)in->q_refine + j * qr_step;
+        const float* wr = in->w_refine + (size_t)j * g.B * d.H;
+        if (groups > 0 &&
+            launch_refine(g, x->sel[cur], x->cnt[cur], lsa_pool_slots(d.pool), d.kv.page_bytes,
+                          d.kv.ikey_off, x->pt[cur], d.idx_dt, d.ikey_scale, qr, d.q_dt, wr, d.H,
+                          d.d, x->scores, groups, ms) != hipSuccess)
+            return LSA_ERR_HIP;
+        if (launch_topk(g, x->sel[cur], x->cnt[cur], x->scores, d.k, tk, tc, ms) != hipSuccess)
+            return LSA_ERR_HIP;
+        if (launch_attn(g, x->plan, (const uint8_t*)in->q_attn + j * qa_step, d.Hq, d.kv,
+                        lsa_pool_slots(d.pool), x->pt[cur], d.recent, tk, tc, d.k, d.sm_scale,
+                        (uint8_t*)out->out + j * o_step,
+                        out->lse ? out->lse + (size_t)j * g.B * d.Hq : nullptr, x->attn_ws,
+                        ms) != hipSuccess)
+            return LSA_ERR_HIP;
+    }
+    if (hipEventRecord(x->ev_win[cur], ms) != hipSuccess) return LSA_ERR_HIP;
+    if (in->next) {
+        if (hipEventSynchronize(x->ev_sel) != hipSuccess) return LSA_ERR_HIP;
+        lsa_gather_stats gs{};
+        lsa_status st = lsa_gather_kv(x->d.pool, x->h_sel[nxt], x->h_cnt[nxt], x->h_sel[cur],
+                                      x->h_cnt[cur], x->pt[nxt], copy_stream, x->ev_win[nxt],
+                                      x->ev_fetch[nxt], &gs);
+        if (st != LSA_OK) return st;
+        out->stats = gs;
+        if (out->sel_cnt) std::memcpy(out->sel_cnt, x->h_cnt[nxt], (size_t)g.B * 4);
+        x->cur = nxt;
+        x->have_next = true;
+    } else {
+        x->have_next = false;
+    }
+    return LSA_OK;
+}
+
+}  // extern "C"
