@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""LSA decode hot-path benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg4]
+
+A bench step is one pass of the whole hot path: one lsa_step64 window.
+That is 64 decode steps of lightning refine + top-k + sparse decode attention
+for every request, plus the next window's chunk scoring, threshold
+selection and slot-pool refill from the cold tier (pinned host memory,
+hipMemcpyAsync on a side stream).  Inputs are seeded synthetic tensors
+already resident in HBM / pinned memory when timing starts.
+
+Prints one JSON line:
+  value        decode steps per second (each decode step serves every request)
+  roofline     for the kernel with the largest share of the window's time,
+               algorithmic work per launch / its mean HIP-event duration
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LSA decode steps/s + scoring/attn HBM GB/s (% of peak) at 128K and 500K ctx"
+HBM_PEAK_GBS = 8000.0
+# fp32 VALU fma without packed ops: 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
+VALU_F32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_work(name, cfg, inp, sel_cnt, k, tcnt_total, B):
+    """Algorithmic bytes and flops of one launch of a kernel in one window."""
+    eb = {0: 4, 1: 2, 2: 1}
+    n_cand = int(sel_cnt.sum()) * cfg.chunk
+    nrec = int(inp["n_rec"].sum())
+    nh = int(inp["chunk_off"][-1])
+    if name == "k_refine":
+        per = cfg.d * eb[cfg.idx_dtype]
+        flops = n_cand * (2 * cfg.H * cfg.d + 2 * cfg.H + 1)
+        return n_cand * per + int(sel_cnt.sum()) * 4 + n_cand * 4, flops
+    if name in ("k_attn_mla", "k_attn_f32"):
+        toks = tcnt_total + nrec
+        row = cfg.Dk * eb[cfg.kv_dtype]
+        qb = B * cfg.Hq * cfg.Dk * eb[cfg.kv_dtype]
+        return toks * row + qb, toks * cfg.Hq * (cfg.Dk + cfg.Dv) * 2
+    if name == "k_score":
+        per = cfg.d * eb[cfg.idx_dtype] + (4 if cfg.idx_dtype == 2 else 0) + 4
+        return nh * per, nh * 2 * cfg.d
+    if name == "k_topk":
+        return n_cand * 4 + B * k * 4, 0
+    if name == "k_select":
+        return nh * 4 + int(sel_cnt.sum()) * 4, 0
+    return 0, 0
+
+
+def source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "learned_sparse_kv_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCE = {"k_refine": ["refine_topk.hip"], "k_topk": ["refine_topk.hip"],
+                 "k_attn_mla": ["attn_decode.hip"], "k_attn_f32": ["attn_decode.hip"],
+                 "k_attn_merge": ["attn_decode.hip"], "k_score": ["score_select.hip"],
+                 "k_select": ["score_select.hip"], "k_gather": ["gather.hip"]}
+
+
+def traffic_for(kernel, workload, launches_per_window):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get(workload, {}).get(kernel)
+    if not e or e.get("source_hash") != source_hash(KERNEL_SOURCE.get(kernel, [])):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, cfg, sel_o_cnt, threads):
+    """The oracle on one decode step of every request plus the trigger."""
+    import numpy as np
+    from oracle import oracle
+    o = oracle.Oracle(inp)
+    t0 = time.perf_counter()
+    _, sel, cnt = o.score_select()
+    units = [(r, 0) for r in range(cfg.batch)]
+    o.decode_units(units, sel, cnt, cfg.topk, cfg.sm_scale, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(1.0 / dt, 4), "unit": "decode steps/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"one trigger (score+select, {cfg.batch} requests) and one decode step "
+                      f"(refine+top-k+attention) of all {cfg.batch} requests of {cfg.name}; "
+                      f"{dt:.1f} s wall on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=8, help="timed windows (64 decode steps each)")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed windows before timing")
+    ap.add_argument("--workload", default="cfg4", choices=["cfg1", "cfg2", "cfg3", "cfg4"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the LSA decode "
+              "path here is a single-GPU build; see DESIGN.md for how it would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from learned_sparse_kv_amd import lsa, runner, synth
+
+    torch.cuda.set_device(0)
+    cfg = synth.config(int(args.workload[3]))
+    # one KIComp version per window run (2 % of chunks drift between versions)
+    cfg = synth.dataclasses.replace(cfg, windows=args.warmup + args.steps + 3, drift=0.02)
+    t0 = time.perf_counter()
+    inp = synth.generate(cfg, steps=64, threads=16)
+    log(f"[bench] generated {cfg.name} in {time.perf_counter() - t0:.1f}s; "
+        f"lens {list(inp['seq_len'][:4])}... history chunks {int(inp['chunk_off'][-1])}")
+    dev = runner.DeviceInputs(inp)
+    pipe = runner.Pipeline(dev)
+    B, S = cfg.batch, 64
+    odt = torch.float32 if cfg.kv_dtype == synth.F32 else torch.int16
+    out = torch.empty((S, B, cfg.Hq, cfg.Dv), dtype=odt, device="cuda")
+    lse = torch.empty((S, B, cfg.Hq), dtype=torch.float32, device="cuda")
+    tcnt = torch.empty((S, B), dtype=torch.int32, device="cuda")
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    st0, cnt = pipe.prime()
+    torch.cuda.synchronize()
+    prime_s = time.perf_counter() - t0
+    log(f"[bench] initial fill: {st0['fetched']} chunks, {st0['bytes'] / 1e6:.1f} MB, {prime_s * 1e3:.1f} ms")
+
+    m = 0
+    fetch = []
+
+    def run_window(m, cur_cnt):
+        st, nxt_cnt = pipe.window(m, 0, S, out, lse=lse, tcnt=tcnt)
+        return st, nxt_cnt
+
+    cur = cnt
+    for _ in range(args.warmup):
+        st, cur = run_window(m, cur)
+        m += 1
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    sel_hist = []
+    for _ in range(args.steps):
+        sel_hist.append(cur.copy())
+        st, cur = run_window(m, cur)
+        fetch.append(st)
+        m += 1
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    value = S * args.steps / wall
+    log(f"[bench] {args.steps} windows in {wall * 1e3:.1f} ms wall ({gpu_ms:.1f} ms main-stream "
+        f"events): {value:.1f} decode steps/s")
+
+    # ---- instrumented window: per-kernel HIP-event durations ----
+    lsa.lsa_timing_reset()
+    lsa.lsa_timing_enable(True)
+    win_cnt = cur.copy()
+    st, cur = run_window(m, cur)
+    m += 1
+    torch.cuda.synchronize()
+    lsa.lsa_timing_enable(False)
+    tsum = int(tcnt.sum().item())  # top-k tokens attended over the window's steps
+    kern = {}
+    for name in lsa.KERNELS:
+        n, ms = lsa.lsa_timing_read(name)
+        if n:
+            kern[name] = {"launches": n, "avg_us": round(ms * 1e3 / n, 2), "total_ms": round(ms, 3)}
+    lsa.lsa_timing_reset()
+    dom = max(kern, key=lambda k_: kern[k_]["total_ms"])
+    per_step_topk = tsum / S
+    for name, e in kern.items():
+        b, f = kernel_work(name, cfg, inp, win_cnt, cfg.topk, per_step_topk, B)
+        sec = e["avg_us"] * 1e-6
+        e["alg_bytes"] = int(b)
+        e["gbs"] = round(b / sec / 1e9, 1) if b else None
+        e["tflops"] = round(f / sec / 1e12, 2) if f else None
+    log("[bench] kernels: " + json.dumps(kern))
+
+    d = kern[dom]
+    if dom == "k_refine":
+        b, f = kernel_work(dom, cfg, inp, win_cnt, cfg.topk, per_step_topk, B)
+        ach = f / (d["avg_us"] * 1e-6) / 1e12
+        roof = {"kernel": dom, "bound": "alu", "achieved": round(ach, 2),
+                "peak": round(VALU_F32_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+                "frac": round(ach / VALU_F32_PEAK_TFLOPS, 4)}
+    else:
+        b, f = kernel_work(dom, cfg, inp, win_cnt, cfg.topk, per_step_topk, B)
+        ach = b / (d["avg_us"] * 1e-6) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = traffic_for(dom, cfg.name, d["launches"])
+
+    def hbm(name):
+        e = kern.get(name)
+        return None if not e or not e.get("gbs") else {"gbs": e["gbs"], "pct_peak": round(100 * e["gbs"] / HBM_PEAK_GBS, 1),
+                                                       "avg_us": e["avg_us"]}
+
+    refill_mb = [f["bytes"] / 1e6 for f in fetch]
+    ctx = int(inp["seq_len"][0])
+    resident = (np.asarray(inp["n_rec"]) + cfg.chunk * win_cnt) / np.asarray(inp["seq_len"])
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "decode steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "context": ctx,
+                   "index_keys": {0: "f32", 1: "bf16", 2: "fp8_e4m3fn"}[cfg.idx_dtype],
+                   "topk": cfg.topk, "recent_window": cfg.window,
+                   "step": "one lsa_step64 window = 64 decode steps",
+                   "cold_tier": "pinned host" if cfg.host_cold else "HBM"},
+        "roofline": roof,
+        "tokens_per_s": round(value * B, 1),
+        "scoring_500k": hbm("k_score"),
+        "attention_500k": hbm("k_attn_mla") or hbm("k_attn_f32"),
+        "kernels": kern,
+        "initial_fill_ms": round(prime_s * 1e3, 2),
+        "refill_mb_per_window": round(float(np.mean(refill_mb)), 2),
+        "selected_chunks_per_request": round(float(win_cnt.mean()), 1),
+        "resident_fraction": round(float(resident.mean()), 4),
+    }
+    if args.copy_calibration:
+        a = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        bb = torch.empty_like(a)
+        for _ in range(3):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        threads = min(16, len(os.sched_getaffinity(0)))
+        result["cpu_baseline"] = cpu_baseline(inp, cfg, win_cnt, threads)
+    pipe.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -284,6 +284,20 @@ lsa_status lsa_ctx_prime(lsa_ctx* ctx, const lsa_trigger_in* first, void* main_s
 lsa_status lsa_step64(lsa_ctx* ctx, const lsa_window_in* in, lsa_window_out* out,
                       void* main_stream, void* copy_stream);
 
+/* ------------------------------------------------------------------------
+ * Diagnostics: per-kernel timing.  While enabled, every kernel the library
+ * launches is bracketed by two hipEvents recorded on the stream it is
+ * launched on (adds a little launch overhead).  lsa_timing_read waits for
+ * the recorded events and returns, for one kernel name (k_fuse_query,
+ * k_score, k_select, k_refine, k_topk, k_attn_mla, k_attn_f32,
+ * k_attn_merge, k_gather), the number of timed launches and their summed
+ * duration in milliseconds since the last reset.  Process-wide; the hooks
+ * are thread-safe.
+ * ---------------------------------------------------------------------- */
+lsa_status lsa_timing_enable(int32_t on);
+void lsa_timing_reset(void);
+lsa_status lsa_timing_read(const char* kernel, int64_t* launches, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

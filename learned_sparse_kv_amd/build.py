@@ -20,7 +20,7 @@ OUT = os.path.join(PKG, "liblsa.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["score_select.hip", "refine_topk.hip", "attn_decode.hip", "gather.hip",
-           "api.cpp", "pool.cpp", "step64.cpp"]
+           "api.cpp", "pool.cpp", "step64.cpp", "timing.cpp"]
 
 # -ffp-contract=off + explicit fmaf: the scores that decide selections follow
 # one written fp32 order; denormals are kept; packed fp32 ops are disabled.

@@ -481,22 +481,28 @@ hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, in
     if (plan.mode == 1) {
         const int units = g.B * plan.n_splits;
         const int grid = (units + 7) / 8 * 8 * plan.head_groups;
+        timing_begin("k_attn_mla", s);
         hipLaunchKernelGGL(k_attn_mla, dim3(grid), dim3(256), 0, s, g, pm, tcnt,
                            (const uint16_t*)q, Hq, plan.n_splits, plan.per_split,
                            plan.head_groups, sm_log2e, part_o, part_ml);
+        timing_end("k_attn_mla", s);
     } else {
+        timing_begin("k_attn_f32", s);
         hipLaunchKernelGGL(k_attn_f32, dim3(g.B * plan.n_splits), dim3(256), 0, s, g, pm, tcnt,
                            (const float*)q, Hq, kv.Dk, kv.Dv, kv.v_off, plan.n_splits,
                            plan.per_split, sm_log2e, part_o, part_ml);
+        timing_end("k_attn_f32", s);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int mt = kv.Dv < 512 ? kv.Dv : 512;
+    timing_begin("k_attn_merge", s);
     if (kv.kv_dtype == LSA_F32)
         hipLaunchKernelGGL(k_attn_merge<LSA_F32>, dim3(g.B * Hq), dim3(mt), 0, s, part_o, part_ml,
                            Hq, kv.Dv, plan.n_splits, out, lse);
     else
         hipLaunchKernelGGL(k_attn_merge<LSA_BF16>, dim3(g.B * Hq), dim3(mt), 0, s, part_o,
                            part_ml, Hq, kv.Dv, plan.n_splits, out, lse);
+    timing_end("k_attn_merge", s);
     return hipGetLastError();
 }

@@ -21,7 +21,9 @@ __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ pair
 hipError_t launch_gather(const int32_t* pairs, int n_pairs, const void* src, void* dst,
                          int64_t page_bytes, hipStream_t s) {
     if (n_pairs <= 0) return hipSuccess;
+    timing_begin("k_gather", s);
     hipLaunchKernelGGL(k_gather, dim3(n_pairs), dim3(256), 0, s, pairs, (const uint8_t*)src,
                        (uint8_t*)dst, page_bytes);
+    timing_end("k_gather", s);
     return hipGetLastError();
 }

@@ -63,3 +63,7 @@ hipError_t launch_gather(const int32_t* pairs, int n_pairs, const void* src, voi
 void* lsa_pool_slots(const lsa_pool* p);
 int64_t lsa_pool_page_bytes(const lsa_pool* p);
 int32_t lsa_pool_batch(const lsa_pool* p);
+
+// Per-kernel event timing hooks (no-ops unless lsa_timing_enable(1)).
+void timing_begin(const char* name, hipStream_t s);
+void timing_end(const char* name, hipStream_t s);

@@ -280,9 +280,11 @@ hipError_t launch_refine(const GeomDev& g, const int32_t* sel, const int32_t* cn
     const int qf32 = q_dt == LSA_F32;
 #define LSA_REFINE_CASE(KDT, D)                                                                 \
     if (idx_dt == KDT && d == D) {                                                              \
+        timing_begin("k_refine", s);                                                            \
         hipLaunchKernelGGL((k_refine<KDT, D>), dim3(grid), dim3(64 * kRefineWaves), shm, s, g,   \
                            sel, cnt, pg, page_bytes, ikey_off, page_table, ikey_scale, q, qf32, \
                            w, H, scores);                                                       \
+        timing_end("k_refine", s);                                                              \
         return hipGetLastError();                                                               \
     }
     LSA_REFINE_CASE(LSA_F32, 64)
@@ -297,6 +299,8 @@ hipError_t launch_refine(const GeomDev& g, const int32_t* sel, const int32_t* cn
 
 hipError_t launch_topk(const GeomDev& g, const int32_t* sel, const int32_t* cnt,
                        const float* scores, int k, int32_t* topk, int32_t* tcnt, hipStream_t s) {
+    timing_begin("k_topk", s);
     hipLaunchKernelGGL(k_topk, dim3(g.B), dim3(1024), 0, s, g, sel, cnt, scores, k, topk, tcnt);
+    timing_end("k_topk", s);
     return hipGetLastError();
 }

@@ -175,10 +175,12 @@ __global__ __launch_bounds__(1024) void k_select(GeomDev g, const float* __restr
 
 hipError_t launch_fuse_query(const GeomDev& g, const void* q, lsa_dtype q_dt, const float* w,
                              int H, int d, float* qbar, hipStream_t s) {
+    timing_begin("k_fuse_query", s);
     if (q_dt == LSA_F32)
         hipLaunchKernelGGL(k_fuse_query<LSA_F32>, dim3(g.B), dim3(128), 0, s, g, q, w, H, d, qbar);
     else
         hipLaunchKernelGGL(k_fuse_query<LSA_BF16>, dim3(g.B), dim3(128), 0, s, g, q, w, H, d, qbar);
+    timing_end("k_fuse_query", s);
     return hipGetLastError();
 }
 
@@ -190,8 +192,10 @@ hipError_t launch_score(const GeomDev& g, const void* kic, lsa_dtype kdt, const 
 #define LSA_SCORE_CASE(KDT, D)                                                                  \
     if (kdt == KDT && d == D) {                                                                 \
         constexpr int nw = score_waves<KDT, D>();                                               \
+        timing_begin("k_score", s);                                                             \
         hipLaunchKernelGGL((k_score<KDT, D>), dim3((tiles + nw - 1) / nw), dim3(64 * nw), 0, s, \
                            g, k, kscale, qbar, bias, z);                                        \
+        timing_end("k_score", s);                                                               \
         return hipGetLastError();                                                               \
     }
     LSA_SCORE_CASE(LSA_F32, 64)
@@ -206,6 +210,8 @@ hipError_t launch_score(const GeomDev& g, const void* kic, lsa_dtype kdt, const 
 
 hipError_t launch_select(const GeomDev& g, const float* z, float theta, int32_t* sel,
                          int32_t* cnt, hipStream_t s) {
+    timing_begin("k_select", s);
     hipLaunchKernelGGL(k_select, dim3(g.B), dim3(1024), 0, s, g, z, theta, sel, cnt);
+    timing_end("k_select", s);
     return hipGetLastError();
 }

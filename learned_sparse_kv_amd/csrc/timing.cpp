@@ -1,0 +1,91 @@
+// Per-kernel timing with HIP events (diagnostics).
+//
+// When enabled, every kernel the library launches is bracketed by two
+// events recorded on the stream it is launched on; lsa_timing_read
+// synchronises them and returns the launch count and summed duration per
+// kernel name.  Disabled (the default), the hooks cost one relaxed load.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "lsa_internal.h"
+
+namespace {
+
+struct Pair {
+    hipEvent_t a, b;
+};
+
+std::atomic<int> g_on{0};
+std::mutex g_mu;
+std::map<std::string, std::vector<Pair>> g_pending;
+std::map<std::string, std::pair<int64_t, double>> g_done;
+thread_local hipEvent_t t_start = nullptr;
+
+}  // namespace
+
+void timing_begin(const char* name, hipStream_t s) {
+    (void)name;
+    if (!g_on.load(std::memory_order_relaxed)) return;
+    if (hipEventCreate(&t_start) != hipSuccess) {
+        t_start = nullptr;
+        return;
+    }
+    (void)hipEventRecord(t_start, s);
+}
+
+void timing_end(const char* name, hipStream_t s) {
+    if (!g_on.load(std::memory_order_relaxed) || !t_start) return;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    (void)hipEventRecord(e, s);
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_pending[name].push_back({t_start, e});
+    t_start = nullptr;
+}
+
+static void drain() {
+    for (auto& kv : g_pending) {
+        auto& acc = g_done[kv.first];
+        for (auto& p : kv.second) {
+            float ms = 0.f;
+            if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+                acc.first += 1;
+                acc.second += ms;
+            }
+            (void)hipEventDestroy(p.a);
+            (void)hipEventDestroy(p.b);
+        }
+    }
+    g_pending.clear();
+}
+
+extern "C" {
+
+lsa_status lsa_timing_enable(int32_t on) {
+    g_on.store(on ? 1 : 0);
+    return LSA_OK;
+}
+
+void lsa_timing_reset(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    drain();
+    g_done.clear();
+}
+
+lsa_status lsa_timing_read(const char* kernel, int64_t* launches, double* total_ms) {
+    if (!kernel || !launches || !total_ms) return LSA_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_mu);
+    drain();
+    auto it = g_done.find(kernel);
+    *launches = it == g_done.end() ? 0 : it->second.first;
+    *total_ms = it == g_done.end() ? 0.0 : it->second.second;
+    return LSA_OK;
+}
+
+}  // extern "C"

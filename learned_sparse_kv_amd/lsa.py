@@ -98,6 +98,9 @@ def _load():
         "lsa_ctx_destroy": ([P], None),
         "lsa_ctx_prime": ([P, C.POINTER(lsa_trigger_in), P, P, C.POINTER(lsa_window_out)], I),
         "lsa_step64": ([P, C.POINTER(lsa_window_in), C.POINTER(lsa_window_out), P, P], I),
+        "lsa_timing_enable": ([I32], I),
+        "lsa_timing_reset": ([], None),
+        "lsa_timing_read": ([C.c_char_p, C.POINTER(I64), C.POINTER(C.c_double)], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -273,3 +276,22 @@ def lsa_ctx_ws_bytes(desc: lsa_ctx_desc) -> int:
 
 def lsa_step64(ctx: Ctx, win, out, main=None, copy=None):
     return ctx.step64(win, out, main, copy)
+
+
+# ---------------------------------------------------------------- diagnostics
+KERNELS = ("k_fuse_query", "k_score", "k_select", "k_refine", "k_topk", "k_attn_mla",
+           "k_attn_f32", "k_attn_merge", "k_gather")
+
+
+def lsa_timing_enable(on: bool):
+    _check("lsa_timing_enable", _lib.lsa_timing_enable(1 if on else 0))
+
+
+def lsa_timing_reset():
+    _lib.lsa_timing_reset()
+
+
+def lsa_timing_read(kernel: str):
+    n, ms = C.c_int64(), C.c_double()
+    _check("lsa_timing_read", _lib.lsa_timing_read(kernel.encode(), C.byref(n), C.byref(ms)))
+    return int(n.value), float(ms.value)

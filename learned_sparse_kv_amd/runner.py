@@ -138,7 +138,7 @@ class Pipeline:
 
     def trigger(self, window: int) -> lsa.lsa_trigger_in:
         d = self.dev
-        w = min(window, len(d.kic) - 1)
+        w = window % len(d.kic)
         return lsa.lsa_trigger_in(d.kic[w].data_ptr(), d.kic_scale[w].data_ptr(),
                                   d.q_coarse.data_ptr(), d.w_coarse.data_ptr(), d.bias.data_ptr())
 
