@@ -107,7 +107,9 @@ size_t lsa_refine_ws_bytes(const lsa_geom* g, int32_t k) {
     GeomDev gd;
     (void)k;
     if (geom_derive(g, &gd) != LSA_OK) return 0;
-    return align_up((size_t)gd.chunk_off[gd.B] * LSA_CHUNK * sizeof(float), 256) + 256;
+    const size_t plain = align_up((size_t)gd.chunk_off[gd.B] * LSA_CHUNK * sizeof(float), 256) + 256;
+    const size_t band = band_ws_bytes(gd);
+    return plain > band ? plain : band;
 }
 
 lsa_status lsa_topk_refine(const lsa_geom* g, const int32_t* sel_ids, const int32_t* sel_cnt,
@@ -135,6 +137,11 @@ lsa_status lsa_topk_refine(const lsa_geom* g, const int32_t* sel_ids, const int3
     }
     if (ws_bytes < lsa_refine_ws_bytes(g, k)) return LSA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
+    if (n > 0 && band_supported(idx_dt, q_dt, H, d) && band_fits(gd)) {
+        LSA_HIP(launch_refine_band(gd, sel_ids, sel_cnt, pages, page_bytes, ikey_off, page_table,
+                                   idx_dt, ikey_scale, q, w, H, d, k, topk_idx, topk_cnt, ws, 0, s));
+        return LSA_OK;
+    }
     float* scores = (float*)ws;
     if (n > 0)
         LSA_HIP(launch_refine(gd, sel_ids, sel_cnt, pages, page_bytes, ikey_off, page_table, idx_dt,

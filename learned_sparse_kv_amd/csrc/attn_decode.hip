@@ -375,39 +375,76 @@ __global__ __launch_bounds__(256) void k_attn_f32(GeomDev g, PosMap pm, const in
 }
 
 // ----------------------------------------------------------------------------
-// merge of the splits: one block per (request, head), one thread per column
+// merge of the splits: one block per (request, head).  The split weights
+// 2^(m_s - m) and the total sum are formed once per block in a fixed order;
+// then each thread combines four columns at a time.
 // ----------------------------------------------------------------------------
+constexpr int kMergeMaxSplits = 1024;
+
 template <int ODT>
-__global__ __launch_bounds__(512) void k_attn_merge(const float* __restrict__ part_o,
+__global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml, int Hq,
                                                     int Dv, int n_splits, void* __restrict__ out,
                                                     float* __restrict__ lse) {
+    __shared__ float fac[kMergeMaxSplits];
+    __shared__ float s_m, s_inv, s_L;
     const int rh = blockIdx.x;  // r * Hq + h
     const int r = rh / Hq, h = rh % Hq;
+    const int64_t b0 = (int64_t)r * n_splits * Hq + h;  // split s: (b0 + s*Hq)
+    // split weights in parallel; max and sum by a fixed-order tree
+    __shared__ float red[128];
     float m = -INFINITY;
-    for (int s = 0; s < n_splits; ++s)
-        m = fmaxf(m, part_ml[(((int64_t)r * n_splits + s) * Hq + h) * 2]);
-    float L = 0.0f;
-    for (int s = 0; s < n_splits; ++s) {
-        const int64_t b = (((int64_t)r * n_splits + s) * Hq + h) * 2;
-        const float ms = part_ml[b];
-        if (ms != -INFINITY) L += part_ml[b + 1] * exp2f(ms - m);
+    for (int s = threadIdx.x; s < n_splits; s += blockDim.x)
+        m = fmaxf(m, part_ml[(b0 + (int64_t)s * Hq) * 2]);
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int w = 64; w > 0; w >>= 1) {
+        if (threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+        __syncthreads();
     }
-    const float inv = 1.0f / L;
-    for (int v = threadIdx.x; v < Dv; v += blockDim.x) {
-        float o = 0.0f;
+    m = red[0];
+    __syncthreads();
+    float part = 0.0f;
+    for (int s = threadIdx.x; s < n_splits; s += blockDim.x) {
+        const float ms = part_ml[(b0 + (int64_t)s * Hq) * 2];
+        const float f = (ms == -INFINITY) ? 0.0f : exp2f(ms - m);
+        fac[s] = f;
+        part += part_ml[(b0 + (int64_t)s * Hq) * 2 + 1] * f;
+    }
+    red[threadIdx.x] = part;
+    __syncthreads();
+    for (int w = 64; w > 0; w >>= 1) {
+        if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        s_m = m;
+        s_L = red[0];
+        s_inv = 1.0f / red[0];
+    }
+    __syncthreads();
+    const float inv = s_inv;
+    for (int v = 4 * threadIdx.x; v < Dv; v += 4 * blockDim.x) {
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
         for (int s = 0; s < n_splits; ++s) {
-            const int64_t b = ((int64_t)r * n_splits + s) * Hq + h;
-            const float ms = part_ml[b * 2];
-            if (ms != -INFINITY) o += part_o[b * Dv + v] * exp2f(ms - m);
+            const float f = fac[s];
+            const float4 x = *(const float4*)&part_o[(b0 + (int64_t)s * Hq) * Dv + v];
+            o.x += f == 0.0f ? 0.0f : x.x * f;
+            o.y += f == 0.0f ? 0.0f : x.y * f;
+            o.z += f == 0.0f ? 0.0f : x.z * f;
+            o.w += f == 0.0f ? 0.0f : x.w * f;
         }
-        o *= inv;
-        if constexpr (ODT == LSA_F32)
-            ((float*)out)[(int64_t)rh * Dv + v] = o;
-        else
-            ((uint16_t*)out)[(int64_t)rh * Dv + v] = f2bf(o);
+        const float ov[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (ODT == LSA_F32)
+                ((float*)out)[(int64_t)rh * Dv + v + e] = ov[e];
+            else
+                ((uint16_t*)out)[(int64_t)rh * Dv + v + e] = f2bf(ov[e]);
+        }
     }
-    if (lse && threadIdx.x == 0) lse[rh] = (m + __log2f(L)) * kLn2;
+    if (lse && threadIdx.x == 0) lse[rh] = (s_m + __log2f(s_L)) * kLn2;
 }
 
 }  // namespace
@@ -463,6 +500,7 @@ lsa_status attn_plan(const GeomDev& g, const lsa_kv_layout* kv, int Hq, int k, i
     } else {
         return LSA_ERR_UNSUPPORTED;
     }
+    if (p.n_splits > kMergeMaxSplits) return LSA_ERR_UNSUPPORTED;
     p.part_o_bytes = align_up((size_t)g.B * p.n_splits * Hq * kv->Dv * sizeof(float), 256);
     p.part_ml_bytes = align_up((size_t)g.B * p.n_splits * Hq * 2 * sizeof(float), 256);
     *plan = p;
@@ -495,13 +533,12 @@ hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, in
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int mt = kv.Dv < 512 ? kv.Dv : 512;
     timing_begin("k_attn_merge", s);
     if (kv.kv_dtype == LSA_F32)
-        hipLaunchKernelGGL(k_attn_merge<LSA_F32>, dim3(g.B * Hq), dim3(mt), 0, s, part_o, part_ml,
-                           Hq, kv.Dv, plan.n_splits, out, lse);
+        hipLaunchKernelGGL(k_attn_merge<LSA_F32>, dim3(g.B * Hq), dim3(128), 0, s, part_o,
+                           part_ml, Hq, kv.Dv, plan.n_splits, out, lse);
     else
-        hipLaunchKernelGGL(k_attn_merge<LSA_BF16>, dim3(g.B * Hq), dim3(mt), 0, s, part_o,
+        hipLaunchKernelGGL(k_attn_merge<LSA_BF16>, dim3(g.B * Hq), dim3(128), 0, s, part_o,
                            part_ml, Hq, kv.Dv, plan.n_splits, out, lse);
     timing_end("k_attn_merge", s);
     return hipGetLastError();

@@ -19,9 +19,10 @@
 // in LDS and read as wave-uniform broadcasts.  8K fma per token at H=64,
 // d=128: VALU-bound.
 //
-// k_topk: one block per request.  Radix select (4 passes of 8 bits, LDS
-// histograms with integer atomics) finds the k-th largest order-preserving
-// key; an ordered emit pass keeps keys above it plus the lowest-index ties.
+// k_topk: one block per request.  Radix select over the order-preserving
+// uint32 keys (digits of 12, 12 and 8 bits, 4096-bin LDS histograms with
+// integer atomics) finds the k-th largest key; an ordered emit pass keeps
+// keys above it plus the lowest-index ties.
 #include "lsa_internal.h"
 
 namespace {
@@ -161,35 +162,113 @@ __device__ __forceinline__ uint32_t fkey(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive rank of flag f among the block's threads in thread order, and
-// the block total.  1024 threads = 16 waves.
-__device__ __forceinline__ int block_rank(bool f, int* wsum, int& total) {
+// Block-wide exclusive prefix of a per-thread count over NW waves, and the
+// block total.
+template <int NW = 16>
+__device__ __forceinline__ int block_scan(int v, int* wsum, int& total) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const uint64_t m = __ballot(f);
-    const int pre = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[wv] = __popcll(m);
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wv] = incl;
     __syncthreads();
     int wpre = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int v = wsum[i];
-        wpre += (i < wv) ? v : 0;
-        tot += v;
+    for (int i = 0; i < NW; ++i) {
+        const int x = wsum[i];
+        wpre += (i < wv) ? x : 0;
+        tot += x;
     }
     __syncthreads();
     total = tot;
-    return wpre + pre;
+    return wpre + incl - v;
 }
 
-__global__ __launch_bounds__(1024) void k_topk(GeomDev g, const int32_t* __restrict__ sel,
-                                               const int32_t* __restrict__ cnt,
-                                               const float* __restrict__ scores, int k,
-                                               int32_t* __restrict__ topk,
-                                               int32_t* __restrict__ tcnt) {
-    __shared__ uint32_t hist[256];
-    __shared__ int wsum[16];
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kBatch = 8;  // independent loads in flight per thread
+
+// Radix select over the order-preserving uint32 keys with digits of 12, 12
+// and 8 bits (4096-bin LDS histograms, integer atomics).  Each pass streams
+// the request's scores (L2-resident) with kBatch loads in flight per thread;
+// only keys matching the digits chosen so far are counted.
+__device__ __forceinline__ void topk_select(const float* __restrict__ sc, int n, int k,
+                                            uint32_t* hist, int* wsum, uint32_t* s_prefix,
+                                            int* s_remaining, int* s_eq, uint32_t& K, int& need,
+                                            int& eq_total) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0, mask = 0;
+    int remaining = k;
+    const int shifts[3] = {20, 8, 0};
+    const int widths[3] = {12, 12, 8};
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = shifts[pass];
+        const int nb = 1 << widths[pass];
+        for (int i = tid; i < nb; i += kTopkThreads) hist[i] = 0;
+        __syncthreads();
+        for (int p0 = 0; p0 < n; p0 += kBatch * kTopkThreads) {
+            float v[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int p = p0 + j * kTopkThreads + tid;
+                v[j] = p < n ? sc[p] : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int p = p0 + j * kTopkThreads + tid;
+                const uint32_t key = fkey(v[j]);
+                if (p < n && (key & mask) == prefix)
+                    atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+            }
+        }
+        __syncthreads();
+        // suffix scan from the top digit: thread t owns 4 digits
+        int c4[4], s4 = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int b = nb - 1 - (4 * tid + j);
+            c4[j] = b >= 0 ? (int)hist[b] : 0;
+            s4 += c4[j];
+        }
+        int tot;
+        const int excl = block_scan<kTopkWaves>(s4, wsum, tot);
+        if (excl < remaining && excl + s4 >= remaining) {
+            int acc = excl, j = 0;
+            for (; j < 3; ++j) {
+                if (acc + c4[j] >= remaining) break;
+                acc += c4[j];
+            }
+            *s_prefix = prefix | ((uint32_t)(nb - 1 - (4 * tid + j)) << shift);
+            *s_remaining = remaining - acc;
+            *s_eq = c4[j];
+        }
+        __syncthreads();
+        prefix = *s_prefix;
+        remaining = *s_remaining;
+        mask |= (uint32_t)(nb - 1) << shift;
+    }
+    K = prefix;
+    need = remaining;
+    eq_total = *s_eq;  // keys equal to K (the final digit's count)
+}
+
+// One block per request: select the k-th largest key K, then emit in
+// ascending candidate order every key above K and the `need` lowest-index
+// keys equal to K.  When every key equal to K is taken (the usual case)
+// the emit needs one block scan per batch; otherwise a second scan ranks
+// the ties.
+__global__ __launch_bounds__(kTopkThreads) void k_topk(GeomDev g, const int32_t* __restrict__ sel,
+                                                      const int32_t* __restrict__ cnt,
+                                                      const float* __restrict__ scores, int k,
+                                                      int32_t* __restrict__ topk,
+                                                      int32_t* __restrict__ tcnt) {
+    __shared__ uint32_t hist[4096];
+    __shared__ int wsum[kTopkWaves];
     __shared__ uint32_t s_prefix;
-    __shared__ int s_remaining;
+    __shared__ int s_remaining, s_eq;
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t off = g.chunk_off[r];
@@ -199,65 +278,54 @@ __global__ __launch_bounds__(1024) void k_topk(GeomDev g, const int32_t* __restr
     int32_t* out = topk + (int64_t)r * k;
 
     if (n <= k) {  // every candidate is kept; candidates are already ascending
-        for (int p = tid; p < n; p += blockDim.x) out[p] = sl[p >> 6] * 64 + (p & 63);
+        for (int p = tid; p < n; p += kTopkThreads) out[p] = sl[p >> 6] * 64 + (p & 63);
         if (tid == 0) tcnt[r] = n;
         return;
     }
-    uint32_t prefix = 0, mask = 0;
-    int remaining = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        if (tid < 256) hist[tid] = 0;
-        __syncthreads();
-        for (int p = tid; p < n; p += blockDim.x) {
-            const uint32_t key = fkey(sc[p]);
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (tid < 64) {  // wave 0: find the digit holding the remaining-th largest
-            const int lane = tid;
-            int c4[4], s = 0;
+    uint32_t K;
+    int need, eq_total;
+    topk_select(sc, n, k, hist, wsum, &s_prefix, &s_remaining, &s_eq, K, need, eq_total);
+    const bool all_ties = (eq_total == need);
+    // ordered emit: thread t owns 4 consecutive candidates of each 4096-block
+    int base = 0, eqbase = 0;
+    float4 nxt = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (4 * tid < n) nxt = *(const float4*)(sc + 4 * tid);
+    for (int p0 = 0; p0 < n; p0 += 4 * kTopkThreads) {
+        const int pb = p0 + 4 * tid;
+        const float4 cur = nxt;
+        if (pb + 4 * kTopkThreads < n) nxt = *(const float4*)(sc + pb + 4 * kTopkThreads);
+        const uint32_t key[4] = {fkey(cur.x), fkey(cur.y), fkey(cur.z), fkey(cur.w)};
+        bool take[4];
+        int tc = 0, tot;
+        if (all_ties) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                c4[j] = (int)hist[255 - 4 * lane - j];
-                s += c4[j];
+                take[j] = pb + j < n && key[j] >= K;
+                tc += take[j];
             }
-            int incl = s;
+        } else {
+            int eqc = 0;
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int t = __shfl_up(incl, o);
-                if (lane >= o) incl += t;
-            }
-            const int excl = incl - s;
-            if (excl < remaining && incl >= remaining) {
-                int acc = excl, j = 0;
-                for (; j < 3; ++j) {
-                    if (acc + c4[j] >= remaining) break;
-                    acc += c4[j];
-                }
-                s_prefix = prefix | ((uint32_t)(255 - 4 * lane - j) << shift);
-                s_remaining = remaining - acc;
+            for (int j = 0; j < 4; ++j) eqc += (pb + j < n && key[j] == K);
+            int eqr = eqbase + block_scan<kTopkWaves>(eqc, wsum, tot);
+            eqbase += tot;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool valid = pb + j < n;
+                const bool eq = valid && key[j] == K;
+                take[j] = valid && (key[j] > K || (eq && eqr < need));
+                eqr += eq;
+                tc += take[j];
             }
         }
-        __syncthreads();
-        prefix = s_prefix;
-        remaining = s_remaining;
-        mask |= 255u << shift;
-    }
-    // prefix is the k-th largest key; take every key above it and the
-    // `remaining` lowest-index keys equal to it, in ascending order.
-    int base = 0, eqbase = 0;
-    for (int p0 = 0; p0 < n; p0 += blockDim.x) {
-        const int p = p0 + tid;
-        const uint32_t key = p < n ? fkey(sc[p]) : 0u;
-        const bool gt = p < n && key > prefix;
-        const bool eq = p < n && key == prefix;
-        int eqtot, taketot;
-        const int eqrank = eqbase + block_rank(eq, wsum, eqtot);
-        const bool take = gt || (eq && eqrank < remaining);
-        const int pos = base + block_rank(take, wsum, taketot);
-        if (take) out[pos] = sl[p >> 6] * 64 + (p & 63);
-        base += taketot;
-        eqbase += eqtot;
+        int pos = base + block_scan<kTopkWaves>(tc, wsum, tot);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (take[j]) {
+                const int p = pb + j;
+                out[pos++] = sl[p >> 6] * 64 + (p & 63);
+            }
+        base += tot;
     }
     if (tid == 0) tcnt[r] = base;
 }
@@ -300,7 +368,8 @@ hipError_t launch_refine(const GeomDev& g, const int32_t* sel, const int32_t* cn
 hipError_t launch_topk(const GeomDev& g, const int32_t* sel, const int32_t* cnt,
                        const float* scores, int k, int32_t* topk, int32_t* tcnt, hipStream_t s) {
     timing_begin("k_topk", s);
-    hipLaunchKernelGGL(k_topk, dim3(g.B), dim3(1024), 0, s, g, sel, cnt, scores, k, topk, tcnt);
+    hipLaunchKernelGGL(k_topk, dim3(g.B), dim3(kTopkThreads), 0, s, g, sel, cnt, scores, k, topk,
+                       tcnt);
     timing_end("k_topk", s);
     return hipGetLastError();
 }

@@ -29,6 +29,7 @@ __global__ void k_fuse_query(GeomDev g, const void* __restrict__ q, const float*
     const int i = threadIdx.x;
     if (i >= d) return;
     float acc = 0.0f;
+#pragma unroll 16
     for (int h = 0; h < H; ++h) {
         const size_t e = ((size_t)r * H + h) * d + i;
         float qv;

@@ -66,7 +66,8 @@ size_t layout(const lsa_ctx_desc* d, GeomDev* g, AttnPlan* plan, size_t offs[12]
     offs[3] = c.take((size_t)nh * 4);                   // sel[1]
     offs[4] = c.take((size_t)B * 4);                    // cnt[0]
     offs[5] = c.take((size_t)B * 4);                    // cnt[1]
-    offs[6] = c.take((size_t)nh * LSA_CHUNK * 4);       // refine scores
+    const size_t plain = (size_t)nh * LSA_CHUNK * 4, band = band_ws_bytes(*g);
+    offs[6] = c.take(plain > band ? plain : band);      // refine scores / band scratch
     offs[7] = c.take((size_t)B * d->k * 4);             // top-k scratch
     offs[8] = c.take((size_t)B * 4);                    // top-k counts scratch
     offs[9] = c.take(plan->part_o_bytes + plan->part_ml_bytes);  // attention partials
@@ -236,13 +237,21 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
         int32_t* tc = out->topk_cnt ? out->topk_cnt + (size_t)j * g.B : x->tcnt_tmp;
         const uint8_t* qr = (const uint8_t*)in->q_refine + j * qr_step;
         const float* wr = in->w_refine + (size_t)j * g.B * d.H;
-        if (groups > 0 &&
-            launch_refine(g, x->sel[cur], x->cnt[cur], lsa_pool_slots(d.pool), d.kv.page_bytes,
-                          d.kv.ikey_off, x->pt[cur], d.idx_dt, d.ikey_scale, qr, d.q_dt, wr, d.H,
-                          d.d, x->scores, groups, ms) != hipSuccess)
-            return LSA_ERR_HIP;
-        if (launch_topk(g, x->sel[cur], x->cnt[cur], x->scores, d.k, tk, tc, ms) != hipSuccess)
-            return LSA_ERR_HIP;
+        if (groups > 0 && band_supported(d.idx_dt, d.q_dt, d.H, d.d) && band_fits(g)) {
+            if (launch_refine_band(g, x->sel[cur], x->cnt[cur], lsa_pool_slots(d.pool),
+                                   d.kv.page_bytes, d.kv.ikey_off, x->pt[cur], d.idx_dt,
+                                   d.ikey_scale, qr, wr, d.H, d.d, d.k, tk, tc, x->scores, groups,
+                                   ms) != hipSuccess)
+                return LSA_ERR_HIP;
+        } else {
+            if (groups > 0 &&
+                launch_refine(g, x->sel[cur], x->cnt[cur], lsa_pool_slots(d.pool), d.kv.page_bytes,
+                              d.kv.ikey_off, x->pt[cur], d.idx_dt, d.ikey_scale, qr, d.q_dt, wr,
+                              d.H, d.d, x->scores, groups, ms) != hipSuccess)
+                return LSA_ERR_HIP;
+            if (launch_topk(g, x->sel[cur], x->cnt[cur], x->scores, d.k, tk, tc, ms) != hipSuccess)
+                return LSA_ERR_HIP;
+        }
         if (launch_attn(g, x->plan, (const uint8_t*)in->q_attn + j * qa_step, d.Hq, d.kv,
                         lsa_pool_slots(d.pool), x->pt[cur], d.recent, tk, tc, d.k, d.sm_scale,
                         (uint8_t*)out->out + j * o_step,

@@ -31,11 +31,14 @@ def small(kind):
                                   H=4, d=64, Hq=8, Dk=128, Dv=128, separate_v=True, topk=256,
                                   steps=2)
     if kind == "bf16":
-        return synth.small_config("bf16_small", 22, (9000, 4100, 300), window=1024, idx=BF16, H=8,
+        return synth.small_config("bf16_small", 22, (9000, 4100, 300), window=1024, idx=BF16, H=16,
                                   topk=256, steps=2)
     if kind == "fp8":
-        return synth.small_config("fp8_small", 23, (9000, 6500), window=1024, idx=FP8, H=8,
+        return synth.small_config("fp8_small", 23, (9000, 6500), window=1024, idx=FP8, H=16,
                                   topk=512, steps=2)
+    if kind == "bf16_h8":  # head count off the matrix-core path: the VALU refine
+        return synth.small_config("bf16_h8", 25, (7000, 2500), window=1024, idx=BF16, H=8,
+                                  topk=256, steps=2)
     if kind == "bf16_h128":
         return synth.small_config("bf16_h128", 24, (4000,), window=512, idx=BF16, H=16, Hq=128,
                                   topk=128, steps=1)
@@ -67,7 +70,7 @@ def setup(kind):
     return _cache[kind]
 
 
-SMALL = ["f32", "bf16", "fp8", "bf16_h128"]
+SMALL = ["f32", "bf16", "fp8", "bf16_h128", "bf16_h8"]
 
 
 @pytest.mark.parametrize("kind", SMALL + ["cfg0", "cfg1", "cfg2", "cfg3"])
@@ -199,7 +202,7 @@ def test_window_pipeline_matches_oracle(host_cold):
     """lsa_step64 over three windows with drift: per-window outputs and
     per-fetch copy counts against the oracle and the pool simulation."""
     R = _runner()
-    cfg = synth.small_config("pipe", 31, (12000, 7000), window=1024, idx=FP8, H=8, topk=256,
+    cfg = synth.small_config("pipe", 31, (12000, 7000), window=1024, idx=FP8, H=16, topk=256,
                              steps=6, planted=0.10)
     cfg = synth.dataclasses.replace(cfg, windows=4, drift=0.10, host_cold=host_cold,
                                     slots_per_req=80)
@@ -239,3 +242,24 @@ def test_window_pipeline_matches_oracle(host_cold):
     want = [sum(sim[r][m] for r in range(B)) for m in range(windows)]
     assert fetched == want
     pipe.close()
+
+
+def test_topk_all_ties_zero_query():
+    """q = 0 makes every refine score +0: the k lowest candidate tokens."""
+    inp, dev, o = setup("fp8")
+    cfg = inp.cfg
+    z, sel, cnt = dev.score_select()
+    _, sel_o, cnt_o = o.score_select()
+    saved = dev.q_refine.clone()
+    dev.q_refine.zero_()
+    try:
+        topk, tcnt = dev.refine_topk(sel, cnt, 0, cfg.topk)
+        torch.cuda.synchronize()
+    finally:
+        dev.q_refine.copy_(saved)
+    for r in range(cfg.batch):
+        a = int(inp["chunk_off"][r])
+        toks = [c * 64 + t for c in sel_o[a:a + cnt_o[r]] for t in range(64)]
+        want = toks[:cfg.topk]
+        got = topk.cpu().numpy()[r, :tcnt.cpu().numpy()[r]]
+        assert list(got) == want
