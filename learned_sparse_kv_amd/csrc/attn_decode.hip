@@ -13,16 +13,10 @@
 // unnormalised output (online softmax, base 2) and writes them to a
 // workspace; k_attn_merge combines the splits of each (request, head).
 //
-// k_attn_mla (bf16, Dk 576 / Dv 512): one block per (request, split, group
-// of 32 heads), 4 waves, 32-token tiles, MFMA 16x16x32 bf16.
-//   S = Q K^T: the 576-wide contraction is split over the waves (wave w owns
-//   dims [128w, 128w+128) plus one 32-wide slice of the 64 rope dims), Q
-//   stays in registers, K comes straight from HBM into the MFMA operand
-//   layout (one tile ahead), partial S goes through LDS.
-//   O += P V: wave w owns value columns [128w, 128w+128) for all 32 heads;
-//   its own V slice is the K slice it loaded, written transposed to LDS.
-// So every KV byte is read from HBM once per head group and feeds both
-// products.  Algorithmic bytes per attended token: 1,152 (HBM-bound).
+// k_attn_mla2 (bf16, Dk 576 / Dv 512): one block per (request, split, group
+// of 32 heads), 4 waves, 32-token tiles, MFMA 16x16x32 bf16; every KV byte
+// is read from HBM once per head group and feeds both products.
+// Algorithmic bytes per attended token: 1,152 (HBM-bound).
 //
 // k_attn_f32: fp32 rows, VALU, for small head counts (fp32 path).
 #include "lsa_internal.h"
@@ -71,28 +65,53 @@ __device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even
 constexpr int MT = 32;           // tokens per tile
 constexpr int MH = 32;           // heads per block
 constexpr int MDK = 576, MDV = 512;
-constexpr int SPS = 36;          // sp row stride (floats)
-constexpr int VTS = 40;          // vt row stride (bf16)
 constexpr int PLS = 40;          // pl row stride (bf16)
 constexpr int kMaxSplitPos = 1024;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-__global__ __launch_bounds__(256) void k_attn_mla(GeomDev g, PosMap pm, const int32_t* __restrict__ tcnt,
-                                                  const uint16_t* __restrict__ q, int Hq,
-                                                  int n_splits, int per_split, int hgroups,
-                                                  float sm_log2e, float* __restrict__ part_o,
-                                                  float* __restrict__ part_ml) {
-    __shared__ __attribute__((aligned(16))) float sp[4][MH][SPS];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[MDV][VTS];
-    __shared__ __attribute__((aligned(16))) uint16_t pl[MH][PLS];
-    __shared__ float alpha_s[MH];
-    __shared__ const uint8_t* rowp[kMaxSplitPos];
 
-    // block -> (request, split, head group); the head groups of one
-    // (request, split) land on the same XCD one after another (blocks are
-    // dispatched round-robin over the 8 XCDs), so their shared K/V tiles
-    // are read from HBM once and from that XCD's L2 after.
+// ----------------------------------------------------------------------------
+// bf16 latent MQA, second form: the 32-token KV tile sits row-major in LDS
+// (rows padded to 1168 bytes), filled from registers that prefetch the next
+// tile.  S = Q K^T splits the 576-wide contraction over the 4 waves as
+// above; O += P V takes its V operands with LDS transpose reads
+// (ds_read_b64_tr_b16: lane n of each 16-lane group, pointing at
+// V[t0 + n/4][v0 + 4(n%4)], receives V[t0..t0+3][v0 + n]), so no transposed
+// copy of V is written.  Softmax is spread over all waves, one head per 8
+// lanes.  About 66 KB of LDS: two blocks per CU.
+// ----------------------------------------------------------------------------
+constexpr int RB = 1152, RBP = 1168;    // KV row bytes, padded LDS row bytes
+constexpr int SPT = 36;                 // sp row stride (floats), head-major [h][t]
+constexpr int kPieces = MT * RB / 16;   // 16-byte pieces per tile (2304)
+constexpr int kPPT = kPieces / 256;     // pieces per thread (9)
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 lds_tr16(const uint8_t* base_lds, int byte_off) {
+    const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16_t*)((__attribute__((address_space(3))) uint8_t*)base_lds +
+                                                      byte_off));
+    return __builtin_bit_cast(uint2, r);
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;
+
+__global__ __launch_bounds__(256, 2) void k_attn_mla2(GeomDev g, PosMap pm,
+                                                     const int32_t* __restrict__ tcnt,
+                                                     const uint16_t* __restrict__ q, int Hq,
+                                                     int n_splits, int per_split, int hgroups,
+                                                     float sm_log2e, float* __restrict__ part_o,
+                                                     float* __restrict__ part_ml) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[MT * RBP];
+    __shared__ __attribute__((aligned(16))) float sp[4][MH * SPT];
+    __shared__ __attribute__((aligned(16))) uint16_t pl[MH][PLS];
+    __shared__ __attribute__((aligned(16))) float alpha_s[MH];
+    // row address per position; bit 0 set: empty position (the address is then
+    // a valid row of finite values, whose probability is forced to 0)
+    __shared__ uint64_t rowp[kMaxSplitPos];
+
     const int bi = blockIdx.x;
     const int xcd = bi & 7, j = bi >> 3;
     const int hg = j % hgroups;
@@ -105,133 +124,127 @@ __global__ __launch_bounds__(256) void k_attn_mla(GeomDev g, PosMap pm, const in
     const int p_begin = split * per_split;
     const int P = pm.k + g.nrec[r];
     const int npos = max(0, min(per_split, P - p_begin));
+    const int ntiles = (npos + MT - 1) / MT;
+    const uint64_t dummy = (uint64_t)(pm.recent + g.rec_off[r] * pm.row_bytes) | 1ull;
 
-    for (int i = tid; i < per_split; i += 256)
-        rowp[i] = (i < npos) ? pos_row(g, pm, r, kcnt, p_begin + i) : nullptr;
+    for (int i = tid; i < ntiles * MT; i += 256) {
+        const uint8_t* row = (i < npos) ? pos_row(g, pm, r, kcnt, p_begin + i) : nullptr;
+        rowp[i] = row ? (uint64_t)row : dummy;
+    }
 
-    // Q in registers as MFMA A operands: Qa[hb][jj] = q[h = hb*16 + l16][ks*32 + lq*8 .. +8]
-    const int nks = (w < 2) ? 5 : 4;
+    // Q slices as MFMA A operands: k-steps 4w..4w+3 and the rope k-step 16+w
+    // (waves 2 and 3 have no rope k-step: a zero slice)
     uint4 Qa[2][5];
     const uint16_t* qr = q + ((int64_t)r * Hq + hg * MH) * MDK;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
-        for (int jj = 0; jj < 5; ++jj) {
-            const int ks = jj < 4 ? 4 * w + jj : 16 + w;
-            Qa[hb][jj] = (jj < nks) ? *(const uint4*)(qr + (hb * 16 + l16) * MDK + ks * 32 + lq * 8)
-                                    : make_uint4(0, 0, 0, 0);
-        }
-    __syncthreads();
+        for (int jj = 0; jj < 4; ++jj)
+            Qa[hb][jj] = *(const uint4*)(qr + (hb * 16 + l16) * MDK + (4 * w + jj) * 32 + lq * 8);
+        Qa[hb][4] = (w < 2) ? *(const uint4*)(qr + (hb * 16 + l16) * MDK + (16 + w) * 32 + lq * 8)
+                            : make_uint4(0, 0, 0, 0);
+    }
+    const int ks4 = 16 + (w & 1);  // rope k-step read by this wave (harmless for w >= 2)
+    __syncthreads();  // rowp ready
+
+    // tile loader: 8 threads per row; thread t copies the 16-byte columns
+    // (t%8) + 8k, k = 0..8, of row t/8 (coalesced 128-byte runs per row)
+    const int ld_row = tid >> 3, ld_col = (tid & 7) * 16;
+    uint8_t* const ld_dst = tile + ld_row * RBP + ld_col;
 
     f32x4_t acc[2][8];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int vb = 0; vb < 8; ++vb) acc[hb][vb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;  // waves 0, 1: head w*16 + l16
+    float m_run = -INFINITY, l_run = 0.0f;  // head 8w + l/8
 
-    const int ntiles = (npos + MT - 1) / MT;
-    uint4 Kb[2][5], Kn[2][5];
-    auto load_tile = [&](int t0, uint4 (&dst)[2][5]) {
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const uint8_t* row = rowp[t0 + tb * 16 + l16];
-#pragma unroll
-            for (int jj = 0; jj < 5; ++jj) {
-                const int ks = jj < 4 ? 4 * w + jj : 16 + w;
-                dst[tb][jj] = (row != nullptr && jj < nks)
-                                  ? *(const uint4*)(row + (ks * 32 + lq * 8) * 2)
-                                  : make_uint4(0, 0, 0, 0);
-            }
+    u32x4_t R0[kPPT];  // the next tile, in flight while this one is computed
+    if (ntiles > 0) {
+        const int T0_ = 0;
+        {
+            gu32x4_t* src_ = (gu32x4_t*)((rowp[T0_ + ld_row] & ~15ull) + ld_col);
+            R0[0] = src_[0]; R0[1] = src_[8]; R0[2] = src_[16]; R0[3] = src_[24];
+            R0[4] = src_[32]; R0[5] = src_[40]; R0[6] = src_[48]; R0[7] = src_[56];
+            R0[8] = src_[64];
         }
-    };
-    if (ntiles > 0) load_tile(0, Kb);
+        {
+            u32x4_t* d_ = (u32x4_t*)ld_dst;
+            d_[0] = R0[0]; d_[8] = R0[1]; d_[16] = R0[2]; d_[24] = R0[3]; d_[32] = R0[4];
+            d_[40] = R0[5]; d_[48] = R0[6]; d_[56] = R0[7]; d_[64] = R0[8];
+        }
+    }
+    if (ntiles > 1) {
+        const int T0_ = MT;
+        {
+            gu32x4_t* src_ = (gu32x4_t*)((rowp[T0_ + ld_row] & ~15ull) + ld_col);
+            R0[0] = src_[0]; R0[1] = src_[8]; R0[2] = src_[16]; R0[3] = src_[24];
+            R0[4] = src_[32]; R0[5] = src_[40]; R0[6] = src_[48]; R0[7] = src_[56];
+            R0[8] = src_[64];
+        }
+    }
 
     for (int it = 0; it < ntiles; ++it) {
         const int t0 = it * MT;
-        if (it + 1 < ntiles) load_tile(t0 + MT, Kn);
-
-        // ---- partial S over this wave's dims ----
-        f32x4_t S[2][2];
+        __syncthreads();  // tile `it` is in LDS
+        // ---- partial S over this wave's dims: sp[w][h][t] ----
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
+        for (int tb = 0; tb < 2; ++tb) {
+            const uint8_t* krow = tile + (tb * 16 + l16) * RBP + lq * 16;
+            uint4 kb[5];
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
+            for (int jj = 0; jj < 4; ++jj) kb[jj] = *(const uint4*)(krow + (4 * w + jj) * 64);
+            kb[4] = *(const uint4*)(krow + ks4 * 64);
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
                 f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int jj = 0; jj < 5; ++jj)
-                    if (jj < nks)
-                        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Qa[hb][jj]),
-                                                                    as_bf16x8(Kb[tb][jj]), c, 0, 0, 0);
-                S[hb][tb] = c;
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Qa[hb][jj]),
+                                                                as_bf16x8(kb[jj]), c, 0, 0, 0);
+                float* dst = &sp[w][(hb * 16 + lq * 4) * SPT + tb * 16 + l16];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i * SPT] = c[i];
             }
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sp[w][hb * 16 + lq * 4 + i][tb * 16 + l16] = S[hb][tb][i];
-        // ---- this wave's value columns, transposed: vt[v][token] ----
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const uint4 v = Kb[tb][jj];
-                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-                const int v0 = (4 * w + jj) * 32 + lq * 8;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vt[v0 + 2 * e][tb * 16 + l16] = (uint16_t)(w4[e] & 0xffffu);
-                    vt[v0 + 2 * e + 1][tb * 16 + l16] = (uint16_t)(w4[e] >> 16);
-                }
-            }
+        }
         __syncthreads();
-
-        // ---- online softmax for heads w*16 + l16 (waves 0 and 1) ----
-        if (w < 2) {
-            const int h = w * 16 + l16;
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; e += 4) {
-                const float4 a = *(const float4*)&sp[0][h][lq * 8 + e];
-                const float4 b = *(const float4*)&sp[1][h][lq * 8 + e];
-                const float4 c = *(const float4*)&sp[2][h][lq * 8 + e];
-                const float4 d = *(const float4*)&sp[3][h][lq * 8 + e];
-                x[e + 0] = ((a.x + b.x) + c.x) + d.x;
-                x[e + 1] = ((a.y + b.y) + c.y) + d.y;
-                x[e + 2] = ((a.z + b.z) + c.z) + d.z;
-                x[e + 3] = ((a.w + b.w) + c.w) + d.w;
-            }
+        // ---- online softmax: head h = 8w + l/8, tokens 4*(l%8) .. +4 ----
+        {
+            const int h = 8 * w + (l >> 3), tq = 4 * (l & 7);
+            const float4 a = *(const float4*)&sp[0][h * SPT + tq];
+            const float4 b = *(const float4*)&sp[1][h * SPT + tq];
+            const float4 c = *(const float4*)&sp[2][h * SPT + tq];
+            const float4 d = *(const float4*)&sp[3][h * SPT + tq];
+            float x[4] = {((a.x + b.x) + c.x) + d.x, ((a.y + b.y) + c.y) + d.y,
+                          ((a.z + b.z) + c.z) + d.z, ((a.w + b.w) + c.w) + d.w};
             float mloc = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const bool valid = rowp[t0 + lq * 8 + e] != nullptr;
-                x[e] = valid ? x[e] * sm_log2e : -INFINITY;
+            for (int e = 0; e < 4; ++e) {
+                x[e] = (rowp[t0 + tq + e] & 1ull) ? -INFINITY : x[e] * sm_log2e;
                 mloc = fmaxf(mloc, x[e]);
             }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 1));
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 2));
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 4));
             const float m_new = fmaxf(m_run, mloc);
             const bool none = (m_new == -INFINITY);
             const float alpha = none ? 1.0f : exp2f(m_run - m_new);
-            float lsum = 0.0f;
-            uint32_t pk[4];
+            float p[4], lsum = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const float p0 = none ? 0.0f : exp2f(x[e] - m_new);
-                const float p1 = none ? 0.0f : exp2f(x[e + 1] - m_new);
-                lsum += p0 + p1;
-                pk[e / 2] = (uint32_t)f2bf(p0) | ((uint32_t)f2bf(p1) << 16);
+            for (int e = 0; e < 4; ++e) {
+                p[e] = none ? 0.0f : exp2f(x[e] - m_new);
+                lsum += p[e];
             }
-            lsum += __shfl_xor(lsum, 16);
-            lsum += __shfl_xor(lsum, 32);
+            lsum += __shfl_xor(lsum, 1);
+            lsum += __shfl_xor(lsum, 2);
+            lsum += __shfl_xor(lsum, 4);
             l_run = l_run * alpha + lsum;
             m_run = m_new;
-            *(uint4*)&pl[h][lq * 8] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-            if (lq == 0) alpha_s[h] = alpha;
+            *(uint2*)&pl[h][tq] = make_uint2((uint32_t)f2bf(p[0]) | ((uint32_t)f2bf(p[1]) << 16),
+                                             (uint32_t)f2bf(p[2]) | ((uint32_t)f2bf(p[3]) << 16));
+            if ((l & 7) == 0) alpha_s[h] = alpha;
         }
         __syncthreads();
-
         // ---- O[:, 128w .. 128w+128) = O * alpha + P V ----
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
@@ -243,18 +256,32 @@ __global__ __launch_bounds__(256) void k_attn_mla(GeomDev g, PosMap pm, const in
                 acc[hb][vb][1] *= a4.y;
                 acc[hb][vb][2] *= a4.z;
                 acc[hb][vb][3] *= a4.w;
-                const bf16x8_t vb8 = as_bf16x8(*(const uint4*)&vt[128 * w + vb * 16 + l16][lq * 8]);
+                const int off0 = (lq * 8 + (l16 >> 2)) * RBP + (128 * w + vb * 16 + 4 * (l16 & 3)) * 2;
+                const uint2 lo = lds_tr16(tile, off0);
+                const uint2 hi = lds_tr16(tile, off0 + 4 * RBP);
+                const bf16x8_t vb8 = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
                 acc[hb][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb8, acc[hb][vb], 0, 0, 0);
             }
         }
-        __syncthreads();
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int jj = 0; jj < 5; ++jj) Kb[tb][jj] = Kn[tb][jj];
+        __syncthreads();  // every wave is done with tile `it`
+        if (it + 1 < ntiles) {
+            {
+            u32x4_t* d_ = (u32x4_t*)ld_dst;
+            d_[0] = R0[0]; d_[8] = R0[1]; d_[16] = R0[2]; d_[24] = R0[3]; d_[32] = R0[4];
+            d_[40] = R0[5]; d_[48] = R0[6]; d_[56] = R0[7]; d_[64] = R0[8];
+        }
+            if (it + 2 < ntiles) {
+                const int T0_ = t0 + 2 * MT;
+                {
+            gu32x4_t* src_ = (gu32x4_t*)((rowp[T0_ + ld_row] & ~15ull) + ld_col);
+            R0[0] = src_[0]; R0[1] = src_[8]; R0[2] = src_[16]; R0[3] = src_[24];
+            R0[4] = src_[32]; R0[5] = src_[40]; R0[6] = src_[48]; R0[7] = src_[56];
+            R0[8] = src_[64];
+        }
+            }
+        }
     }
 
-    // ---- partial results ----
     const int64_t hbase = ((int64_t)r * n_splits + split) * Hq + hg * MH;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
@@ -263,9 +290,10 @@ __global__ __launch_bounds__(256) void k_attn_mla(GeomDev g, PosMap pm, const in
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 part_o[(hbase + hb * 16 + lq * 4 + i) * MDV + 128 * w + vb * 16 + l16] = acc[hb][vb][i];
-    if (w < 2 && lq == 0) {
-        part_ml[(hbase + w * 16 + l16) * 2 + 0] = m_run;
-        part_ml[(hbase + w * 16 + l16) * 2 + 1] = l_run;
+    if ((l & 7) == 0) {
+        const int h = 8 * w + (l >> 3);
+        part_ml[(hbase + h) * 2 + 0] = m_run;
+        part_ml[(hbase + h) * 2 + 1] = l_run;
     }
 }
 
@@ -520,7 +548,7 @@ hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, in
         const int units = g.B * plan.n_splits;
         const int grid = (units + 7) / 8 * 8 * plan.head_groups;
         timing_begin("k_attn_mla", s);
-        hipLaunchKernelGGL(k_attn_mla, dim3(grid), dim3(256), 0, s, g, pm, tcnt,
+        hipLaunchKernelGGL(k_attn_mla2, dim3(grid), dim3(256), 0, s, g, pm, tcnt,
                            (const uint16_t*)q, Hq, plan.n_splits, plan.per_split,
                            plan.head_groups, sm_log2e, part_o, part_ml);
         timing_end("k_attn_mla", s);
