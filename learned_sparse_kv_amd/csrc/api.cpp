@@ -124,7 +124,9 @@ lsa_status lsa_topk_refine(const lsa_geom* g, const int32_t* sel_ids, const int3
     if (!sel_cnt || !q || !w || !topk_idx || !topk_cnt || !ws) return LSA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return LSA_ERR_UNSUPPORTED;
     if (H < 1 || H > 128 || k < 1) return LSA_ERR_INVALID_ARG;
-    if (((int64_t)H * d + H) * 4 > 65536) return LSA_ERR_UNSUPPORTED;  // queries fit in LDS
+    // the VALU refine (every case the matrix-core path does not take) keeps the queries in LDS
+    if (!band_supported(idx_dt, q_dt, H, d) && ((int64_t)H * d + H) * 4 > 65536)
+        return LSA_ERR_UNSUPPORTED;
     if (q_dt != LSA_F32 && q_dt != LSA_BF16) return LSA_ERR_UNSUPPORTED;
     if (idx_dt != LSA_F32 && idx_dt != LSA_BF16 && idx_dt != LSA_FP8_E4M3FN)
         return LSA_ERR_UNSUPPORTED;
@@ -137,9 +139,10 @@ lsa_status lsa_topk_refine(const lsa_geom* g, const int32_t* sel_ids, const int3
     }
     if (ws_bytes < lsa_refine_ws_bytes(g, k)) return LSA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
-    if (n > 0 && band_supported(idx_dt, q_dt, H, d) && band_fits(gd)) {
+    if (n > 0 && band_supported(idx_dt, q_dt, H, d)) {
         LSA_HIP(launch_refine_band(gd, sel_ids, sel_cnt, pages, page_bytes, ikey_off, page_table,
-                                   idx_dt, ikey_scale, q, w, H, d, k, topk_idx, topk_cnt, ws, 0, s));
+                                   idx_dt, ikey_scale, q, w, H, d, k, topk_idx, topk_cnt, ws, false,
+                                   s));
         return LSA_OK;
     }
     float* scores = (float*)ws;

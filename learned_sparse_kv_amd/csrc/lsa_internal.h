@@ -70,11 +70,13 @@ void timing_end(const char* name, hipStream_t s);
 
 // Matrix-core refine with an exact re-score band (refine_band.hip).
 bool band_supported(lsa_dtype idx_dt, lsa_dtype q_dt, int H, int d);
-bool band_fits(const GeomDev& g);  // candidate slices per request within the kernels' limit
 size_t band_ws_bytes(const GeomDev& g);
 hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_t* cnt,
                               const void* pages, int64_t page_bytes, int64_t ikey_off,
                               const int32_t* page_table, lsa_dtype idx_dt,
                               const float* ikey_scale, const void* q, const float* w, int H,
-                              int d, int k, int32_t* topk, int32_t* tcnt, void* ws, int grid_hint,
+                              int d, int k, int32_t* topk, int32_t* tcnt, void* ws, bool ws_clean,
                               hipStream_t s);
+// Zeroes the part of a band workspace that must start at zero (every band
+// launch leaves it zero again).
+hipError_t launch_band_clear(const GeomDev& g, void* ws, hipStream_t s);

@@ -8,15 +8,31 @@
 //  K1 k_refine_mfma  every candidate token: a'_h = q_h . key on MFMA (bf16
 //     inputs, exact products, fp32 accumulation), I' = sum_h w_h ReLU(a'_h),
 //     and a rigorous bound E with |I' - I| <= E.  Writes L = I' - E and
-//     U = I' + E, and each block's range of L.
-//  K2 k_band         per request: a histogram of L over its range finds a
-//     key tau no larger than the k-th largest L; every candidate with
-//     U >= tau (the band: never fewer than k) is listed, ascending.
-//  K3 k_rescore      the listed candidates get the canonical score.
-//  K4 k_topk_list    exact top-k among them, ties to the lower token.
-// A candidate left out has I <= U < tau <= the k-th largest L <= the k-th
-// largest I among the listed ones, so it is strictly below k others and
-// cannot be in the top-k: the result is the canonical one.
+//     U = I' + E as order-preserving 32-bit keys and adds to the request's
+//     coarse histograms of L and U (top 12 key bits).  The last block of a
+//     request to finish finds the coarse bins holding the k-th largest L
+//     and the k-th largest U.
+//  K2 k_band_fine    fine histograms (256-key bins) of the keys inside those
+//     two coarse bins; the last block finds tau = lowest key of the fine bin
+//     holding the k-th largest L and edge = first key above the fine bin
+//     holding the k-th largest U.
+//  K3 k_band_list    candidates with U >= tau form the band (never fewer
+//     than k); each block lists its share in token order.  Those with
+//     L >= edge are certain to be in the top-k; the rest of the band
+//     (uncertain) gets the canonical score, by the same block.
+//  K4 k_topk_band    exact top-k over the band (certain ones rank first),
+//     ties to the lower token, emitted in token order.
+// Why it is exact.  A candidate outside the band has I <= U < tau, and at
+// least k candidates have I >= L >= tau: it is below k others.  A certain
+// candidate s has L_s >= edge; any t with I_t >= I_s has U_t >= L_s >= edge,
+// and fewer than k candidates (s included) have U >= edge: fewer than k
+// others can rank above s.  So the top-k is the certain set plus the best
+// of the uncertain ones, by canonical score and then by token.
+//
+// Blocks of one request meet through device-scope atomics: each adds its
+// histogram counts, then bumps the request's arrival counter; the block that
+// arrives last reads the totals, clears the histograms and the counter for
+// the next launch, and writes its result for the next kernel.
 //
 // The bound.  Both the canonical chain and the MFMA sum differ from the exact
 // dot product by at most gamma(n) * sum_i |q_i k_i| (any summation order,
@@ -26,12 +42,12 @@
 // the head sums add gamma(H) * sum_h |w_h| (ReLU(a'_h) + eps_h).
 #include "lsa_internal.h"
 
+#include <type_traits>
+
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf16f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 __device__ __forceinline__ uint32_t fkey(float f) {
     const uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
@@ -41,10 +57,13 @@ __device__ __forceinline__ uint32_t fkey(float f) {
 constexpr float kU2 = 2.384185791015625e-07f;  // 2^-22: two ulps of fp32 per operation
 __host__ __device__ constexpr float gam(int n) { return n * kU2 / (1.0f - n * kU2); }
 
-constexpr int kBandWaves = 4;
-constexpr int kBandBins = 4096;   // histogram bins over a request's range of L
-constexpr int kSlice = 4096;      // candidates per slice in the band kernels
-constexpr int kRedStride = 33;    // per-token row of 16 + 16 partial sums (+1 pad)
+constexpr int kWaves = 4;         // waves per block of K1 and K3
+constexpr int kBins = 4096;       // coarse bins (key >> 20) and fine bins ((key >> 8) & 4095)
+constexpr int kHist = 4 * kBins;  // per request: coarse L, coarse U, fine L, fine U
+constexpr int kRedStride = 33;    // per-token row: 16 + 16 partial sums, |key|^2
+constexpr int kT = 1024, kTW = kT / 64;
+constexpr int kMaxSeg = 1024;     // band list segments (K3 blocks) per request, at most
+constexpr int kListCap = 8192;    // band entries K4 keeps in LDS
 
 // 8 fp8 e4m3fn bytes -> 8 bf16 (exact: every e4m3 value is a bf16 value)
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 v) {
@@ -53,10 +72,10 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 v) {
     const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false);
     const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true);
     uint4 r;
-    r.x = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
-    r.y = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
-    r.z = (__float_as_uint(c[0]) >> 16) | (__float_as_uint(c[1]) & 0xffff0000u);
-    r.w = (__float_as_uint(d[0]) >> 16) | (__float_as_uint(d[1]) & 0xffff0000u);
+    r.x = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+    r.y = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+    r.z = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
+    r.w = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
     return r;
 }
 
@@ -72,103 +91,185 @@ __device__ __forceinline__ float sumsq_bf16x8(uint4 v) {
     return s;
 }
 
-// Work items: groups of kBandWaves selected chunks of one request.  The
-// counts are loaded by B threads at once, then prefix-summed by thread 0.
-// Must be called by every thread of the block.
-__device__ __forceinline__ void group_offsets(const GeomDev& g, const int32_t* cnt, int* goff) {
-    if ((int)threadIdx.x < g.B) goff[threadIdx.x + 1] = (cnt[threadIdx.x] + kBandWaves - 1) / kBandWaves;
+// ---------------------------------------------------------------------------
+template <int NW>
+__device__ __forceinline__ int block_scan(int v, int* wsum, int& total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wv] = incl;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        goff[0] = 0;
-        for (int r = 0; r < g.B; ++r) goff[r + 1] += goff[r];
+    int wpre = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int x = wsum[i];
+        wpre += (i < wv) ? x : 0;
+        tot += x;
+    }
+    __syncthreads();
+    total = tot;
+    return wpre + incl - v;
+}
+
+// Bin holding the k-th largest entry of hist[0, kBins) -> out[0], and the
+// number of entries in higher bins -> out[1].  Thread t owns the BPT bins
+// below kBins - t*BPT.  Every thread of the block (NW waves) must call; the
+// caller guarantees at least k entries.
+template <int NW>
+__device__ __forceinline__ void kth_bin(const uint32_t* hist, int k, int* wsum, int* out) {
+    constexpr int BPT = kBins / (64 * NW);
+    const int tid = threadIdx.x;
+    int c[BPT], sum = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        c[j] = (int)hist[kBins - 1 - (tid * BPT + j)];
+        sum += c[j];
+    }
+    int tot;
+    const int excl = block_scan<NW>(sum, wsum, tot);
+    if (excl < k && excl + sum >= k) {
+        int acc = excl, j = 0;
+        for (; j < BPT - 1; ++j) {
+            if (acc + c[j] >= k) break;
+            acc += c[j];
+        }
+        out[0] = kBins - 1 - (tid * BPT + j);
+        out[1] = acc;
     }
     __syncthreads();
 }
 
+__device__ __forceinline__ void hist_add(uint32_t* p, uint32_t v) {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrival of this block at a request's counter (n blocks in all); true in
+// the block that arrives last.  The histogram adds are device-scope atomics
+// and every thread waits for its own before the block arrives, so the last
+// block finds every other block's adds in place (no cache write-back
+// needed: nothing else is read across blocks).
+__device__ __forceinline__ bool last_arrival(uint32_t* ctr, uint32_t n, int* s_flag) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *s_flag = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
+    __syncthreads();
+    return *s_flag != 0;
+}
+
+// Moves a request's histogram pair (2 * kBins) into LDS, leaving zeros.
+__device__ __forceinline__ void take_hist(uint32_t* gh, uint32_t* lds, int nthreads) {
+    for (int i = threadIdx.x; i < 2 * kBins; i += nthreads)
+        lds[i] = __hip_atomic_exchange(&gh[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// K1.  Grid (X, B): block x of request r takes chunks x*4 + wave, stepping by
+// 4X, and prefetches the next chunk's key rows while the current one is on
+// the matrix cores.  The query operands, weights and the bound's query term
+// are set up once per block.  The block's coarse histograms go to the
+// request's (hist, zero on entry) with one atomic per nonzero bin; the last
+// block writes the coarse bins of the k-th largest L and U to cinfo.
 template <int KDT, int D, int H>
-__global__ __launch_bounds__(64 * kBandWaves) void k_refine_mfma(
+__global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_refine_mfma(
     GeomDev g, const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
     const uint8_t* __restrict__ pages, int64_t page_bytes, int64_t ikey_off,
     const int32_t* __restrict__ page_table, const float* __restrict__ ikey_scale,
-    const uint16_t* __restrict__ q, const float* __restrict__ w, float2* __restrict__ lu,
-    uint2* __restrict__ stats, uint32_t* __restrict__ band_hist) {
+    const uint16_t* __restrict__ q, const float* __restrict__ w, int k, uint2* __restrict__ lu,
+    uint32_t* __restrict__ hist, uint32_t* __restrict__ arrive, int4* __restrict__ cinfo) {
     constexpr int EB = KDT == LSA_BF16 ? 2 : 1;
     constexpr int ROWB = D * EB;
     constexpr int KS = D / 32;   // MFMA k-steps
     constexpr int HB = H / 16;   // head blocks
-    __shared__ int goff[LSA_MAX_BATCH + 1];
-    __shared__ uint32_t s_mn[kBandWaves], s_mx[kBandWaves];
-    __shared__ float red[kBandWaves][64 * kRedStride];
+    using Raw = std::conditional_t<KDT == LSA_BF16, uint4, uint2>;
+    __shared__ uint32_t hl[2 * kBins];  // coarse L bins, then coarse U bins
+    __shared__ float red[kWaves][64 * kRedStride];
+    __shared__ int wsum[kWaves], s_flag, s_out[4];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, lq = lane >> 4;
-    for (int e = blockIdx.x * blockDim.x + tid; e < g.B * kBandBins; e += gridDim.x * blockDim.x)
-        band_hist[e] = 0;  // histogram of the next kernel
-    group_offsets(g, cnt, goff);
-    const int total = goff[g.B];
-    int cur_r = -1;
-    uint4 qb[HB][KS];
-    float wl[HB], wa[HB];
-    float wq = 0.0f;
-    for (int gi = blockIdx.x; gi < total; gi += gridDim.x) {
-        int r = 0;
-        while (gi >= goff[r + 1]) ++r;
-        if (r != cur_r) {  // uniform across the block
-            const uint16_t* qr = q + (int64_t)r * H * D;
+    const int r = blockIdx.y, X = gridDim.x;
+    const int nc = cnt[r];
+    for (int i = tid; i < 2 * kBins; i += 64 * kWaves) hl[i] = 0;
+    __syncthreads();
+    if ((int)blockIdx.x * kWaves < nc) {  // uniform across the block
+        uint4 qb[HB][KS];
+        float wl[HB], wa[HB];
+        const uint16_t* qr = q + (int64_t)r * H * D;
 #pragma unroll
-            for (int hb = 0; hb < HB; ++hb) {
+        for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    qb[hb][ks] = *(const uint4*)(qr + (hb * 16 + l16) * D + ks * 32 + lq * 8);
-                wl[hb] = w[(int64_t)r * H + hb * 16 + l16];
-                wa[hb] = fabsf(wl[hb]);
-            }
-            // Wq = sum_h |w_h| * |q_h|_2 (rounded up), from the operands held:
-            // lane (l16, lq) has dims lq*8.. of every k-step of head hb*16 + l16
-            float part = 0.0f;
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) {
-                float ss = 0.0f;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) ss += sumsq_bf16x8(qb[hb][ks]);
-                ss += __shfl_xor(ss, 16);
-                ss += __shfl_xor(ss, 32);
-                part += wa[hb] * sqrtf(ss * (1.0f + gam(D + 8))) * (1.0f + 4 * kU2);
-            }
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) part += __shfl_xor(part, o);
-            wq = part * (1.0f + gam(H + 8));
-            cur_r = r;
+            for (int ks = 0; ks < KS; ++ks)
+                qb[hb][ks] = *(const uint4*)(qr + (hb * 16 + l16) * D + ks * 32 + lq * 8);
+            wl[hb] = w[(int64_t)r * H + hb * 16 + l16];
+            wa[hb] = fabsf(wl[hb]);
         }
-        const int i = (gi - goff[r]) * kBandWaves + wv;
-        uint32_t kmin = 0xffffffffu, kmax = 0u;
-        if (i < cnt[r]) {
-            const int64_t off = g.chunk_off[r];
-            const int c = sel[off + i];
-            const int64_t pg = page_table ? (int64_t)page_table[off + c] : off + c;
-            const uint8_t* base = pages + pg * page_bytes + ikey_off;
-            const float scale = (KDT == LSA_FP8_E4M3FN) ? ikey_scale[off + c] : 1.0f;
-            // A operands: key rows of tokens tb*16 + l16, dims ks*32 + lq*8 .. +8
-            uint4 ka[4][KS];
-            float kss[4];
+        // Wq = sum_h |w_h| * |q_h|_2 (rounded up), from the operands held:
+        // lane (l16, lq) has dims lq*8.. of every k-step of head hb*16 + l16
+        float part = 0.0f;
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const uint8_t* row = base + (int64_t)(tb * 16 + l16) * ROWB;
-                float ss = 0.0f;
+        for (int hb = 0; hb < HB; ++hb) {
+            float ss = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) ss += sumsq_bf16x8(qb[hb][ks]);
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            part += wa[hb] * sqrtf(ss * (1.0f + gam(D + 8))) * (1.0f + 4 * kU2);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) part += __shfl_xor(part, o);
+        const float wq = part * (1.0f + gam(H + 8));
+
+        const int64_t off = g.chunk_off[r];
+        const int stride = X * kWaves;
+        int i = blockIdx.x * kWaves + wv;
+        Raw raw[4][KS];
+        float scale_nx = 1.0f;
+        // key rows of chunk ci: A operands of tokens tb*16 + l16, dims ks*32 + lq*8 .. +8
+#define LSA_FETCH(ci)                                                                           \
+    {                                                                                           \
+        const int c_ = sel[off + (ci)];                                                         \
+        const int64_t pg_ = page_table ? (int64_t)page_table[off + c_] : off + c_;              \
+        const uint8_t* base_ = pages + pg_ * page_bytes + ikey_off;                             \
+        if constexpr (KDT == LSA_FP8_E4M3FN) scale_nx = ikey_scale[off + c_];                   \
+        _Pragma("unroll") for (int tb = 0; tb < 4; ++tb) {                                      \
+            _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) raw[tb][ks] =                     \
+                *(const Raw*)(base_ + (int64_t)(tb * 16 + l16) * ROWB + (ks * 32 + lq * 8) * EB); \
+        }                                                                                       \
+    }
+        if (i < nc) LSA_FETCH(i)
+        float* pr = red[wv];
+        for (; i < nc; i += stride) {
+            uint4 ka[4][KS];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    if constexpr (KDT == LSA_BF16)
-                        ka[tb][ks] = *(const uint4*)(row + (ks * 32 + lq * 8) * 2);
-                    else
-                        ka[tb][ks] = fp8x8_to_bf16x8(*(const uint2*)(row + ks * 32 + lq * 8));
-                    ss += sumsq_bf16x8(ka[tb][ks]);
+                    if constexpr (KDT == LSA_BF16) ka[tb][ks] = raw[tb][ks];
+                    else ka[tb][ks] = fp8x8_to_bf16x8(raw[tb][ks]);
                 }
-                ss += __shfl_xor(ss, 16);
-                ss += __shfl_xor(ss, 32);
-                kss[tb] = ss;  // |key|^2 of token tb*16 + l16 (every lq)
+            const float scale = scale_nx;
+            if (i + stride < nc) LSA_FETCH(i + stride)
+            // |key|^2 on the matrix cores: the diagonal of the 16x16 Gram block
+            // of tokens tb*16..; lane (l16, lq) holds rows 4lq..4lq+3 of column l16
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                f32x4_t gm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, ka[tb][ks]),
+                        __builtin_bit_cast(bf16x8_t, ka[tb][ks]), gm, 0, 0, 0);
+                const int e = l16 & 3;
+                const float dv = e == 0 ? gm[0] : (e == 1 ? gm[1] : (e == 2 ? gm[2] : gm[3]));
+                if ((l16 >> 2) == lq) pr[(tb * 16 + l16) * kRedStride + 32] = dv;
             }
             // partial head sums per lane (heads hb*16 + l16), then through LDS
             // to one lane per token: red[token][l16], fixed summation order
-            float* pr = red[wv];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
                 f32x4_t acc[HB];
@@ -206,369 +307,312 @@ __global__ __launch_bounds__(64 * kBandWaves) void k_refine_mfma(
                 sI += pr[lane * kRedStride + j];
                 sW += pr[lane * kRedStride + 16 + j];
             }
-            const float kn2 = lq == 0 ? kss[0] : (lq == 1 ? kss[1] : (lq == 2 ? kss[2] : kss[3]));
+            const float kn2 = pr[lane * kRedStride + 32];
             const float kn = sqrtf(kn2 * (1.0f + gam(D + 8))) * (1.0f + 4 * kU2);
             const float ek = gam(D) * 2.0f * kn * wq;  // sum_h |w_h| eps_h
             float E = ek + 2.0f * gam(H + 24) * (sW + ek);
             const float Is = sI * scale;
             E = (E * scale + 4 * kU2 * (fabsf(Is) + E * scale)) * (1.0f + 16 * kU2) + 1e-30f;
-            const float L = Is - E, U = Is + E;
-            lu[(off * 64) + (int64_t)i * 64 + lane] = make_float2(L, U);
-            kmin = fkey(L);
-            kmax = kmin;
+            const uint32_t kL = fkey(Is - E), kU = fkey(Is + E);
+            lu[(off + i) * 64 + lane] = make_uint2(kL, kU);
+            atomicAdd(&hl[kL >> 20], 1u);
+            atomicAdd(&hl[kBins + (kU >> 20)], 1u);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();  // red[] is rewritten by the next chunk
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-            kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-        }
-        if (lane == 0) {
-            s_mn[wv] = kmin;
-            s_mx[wv] = kmax;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            uint32_t a = s_mn[0], b = s_mx[0];
-            for (int j = 1; j < kBandWaves; ++j) {
-                a = min(a, s_mn[j]);
-                b = max(b, s_mx[j]);
-            }
-            stats[gi] = make_uint2(a, b);
-        }
-        __syncthreads();
+#undef LSA_FETCH
     }
+    __syncthreads();
+    uint32_t* gh = hist + (int64_t)r * kHist;
+    for (int i = tid; i < 2 * kBins; i += 64 * kWaves)
+        if (hl[i]) hist_add(&gh[i], hl[i]);
+    if (!last_arrival(&arrive[2 * r], X, &s_flag)) return;
+    take_hist(gh, hl, 64 * kWaves);
+    if (nc * 64 > k) {
+        kth_bin<kWaves>(hl, k, wsum, &s_out[0]);
+        kth_bin<kWaves>(hl + kBins, k, wsum, &s_out[2]);
+        if (tid == 0) cinfo[r] = make_int4(s_out[0], s_out[1], s_out[2], s_out[3]);
+    }
+    if (tid == 0) __hip_atomic_store(&arrive[2 * r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---------------------------------------------------------------------------
-constexpr int kT = 1024, kTW = kT / 64;
 
-template <int NW>
-__device__ __forceinline__ int block_scan(int v, int* wsum, int& total) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-    }
-    if (lane == 63) wsum[wv] = incl;
-    __syncthreads();
-    int wpre = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const int x = wsum[i];
-        wpre += (i < wv) ? x : 0;
-        tot += x;
-    }
-    __syncthreads();
-    total = tot;
-    return wpre + incl - v;
+// Chunks [c0, c1) of a request that block x of X takes in K2 and K3.
+__device__ __forceinline__ void block_chunks(int nc, int X, int x, int& c0, int& c1) {
+    const int C = (nc + X - 1) / X;
+    c0 = min(nc, x * C);
+    c1 = min(nc, c0 + C);
 }
 
-// Range [lo, hi] of the L keys of request r, from K1's per-block ranges.
-__device__ __forceinline__ void band_range(const GeomDev& g, const int32_t* cnt,
-                                           const uint2* stats, int r, int* goff, uint32_t* red,
-                                           uint32_t& lo, uint32_t& hi) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
-    group_offsets(g, cnt, goff);
-    uint32_t mn = 0xffffffffu, mx = 0u;
-    for (int j = goff[r] + tid; j < goff[r + 1]; j += blockDim.x) {
-        const uint2 st = stats[j];
-        mn = min(mn, st.x);
-        mx = max(mx, st.y);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-    }
-    if (lane == 0) {
-        red[wv] = mn;
-        red[16 + wv] = mx;
-    }
-    __syncthreads();
-    lo = red[0];
-    hi = red[16];
-    for (int i = 1; i < nw; ++i) {
-        lo = min(lo, red[i]);
-        hi = max(hi, red[16 + i]);
-    }
-    __syncthreads();
-}
-
-__device__ __forceinline__ int band_shift(uint32_t lo, uint32_t hi) {
-    const uint64_t width = (uint64_t)hi - lo + 1;
-    int shift = 0;
-    while ((width + (1ull << shift) - 1) >> shift > (uint64_t)kBandBins) ++shift;
-    return shift;
-}
-
-// K2a: histogram of L over [lo, hi] (kBandBins bins), one block per slice of
-// kSlice candidates; block counts are added to the request's histogram.
-__global__ __launch_bounds__(256) void k_band_hist(GeomDev g, const int32_t* __restrict__ cnt,
-                                                   const float2* __restrict__ lu,
-                                                   const uint2* __restrict__ stats, int k,
-                                                   uint32_t* __restrict__ band_hist) {
-    __shared__ uint32_t hist[kBandBins];
-    __shared__ int goff[LSA_MAX_BATCH + 1];
-    __shared__ uint32_t red[32];
-    const int r = blockIdx.y, tid = threadIdx.x;
-    const int n = cnt[r] * 64;
-    const int p0 = blockIdx.x * kSlice;
-    if (n <= k || p0 >= n) return;
-    uint32_t lo, hi;
-    band_range(g, cnt, stats, r, goff, red, lo, hi);
-    const int shift = band_shift(lo, hi);
-    for (int i = tid; i < kBandBins; i += 256) hist[i] = 0;
-    __syncthreads();
-    const float2* v = lu + g.chunk_off[r] * 64;
-    const int p1 = min(n, p0 + kSlice);
-#pragma unroll 4
-    for (int p = p0 + tid; p < p1; p += 256) atomicAdd(&hist[(fkey(v[p].x) - lo) >> shift], 1u);
-    __syncthreads();
-    uint32_t* gh = band_hist + (int64_t)r * kBandBins;
-    for (int i = tid; i < kBandBins; i += 256)
-        if (hist[i]) atomicAdd(&gh[i], hist[i]);
-}
-
-// K2b: the request's threshold tau (lowest key of the histogram bin holding
-// the k-th largest L), then each block lists, in order, the candidates of its
-// slice with U >= tau.  Requests with no more than k candidates keep them all.
-__global__ __launch_bounds__(256) void k_band_list(GeomDev g, const int32_t* __restrict__ sel,
-                                                   const int32_t* __restrict__ cnt,
-                                                   const float2* __restrict__ lu,
-                                                   const uint2* __restrict__ stats, int k,
-                                                   const uint32_t* __restrict__ band_hist,
-                                                   int32_t* __restrict__ ulist,
-                                                   int32_t* __restrict__ scnt,
-                                                   int32_t* __restrict__ topk,
-                                                   int32_t* __restrict__ tcnt, int nslices) {
-    __shared__ int wsum[4];
-    __shared__ int goff[LSA_MAX_BATCH + 1];
-    __shared__ uint32_t red[32];
-    __shared__ uint32_t s_tau;
-    const int r = blockIdx.y, tid = threadIdx.x;
-    const int n = cnt[r] * 64;
-    const int p0 = blockIdx.x * kSlice;
+// K2.  Grid (X, B).  Requests with no more than k candidates keep them all
+// here.  Otherwise each block adds the fine histograms of its chunks' keys
+// that fall in the coarse bins of cinfo, and the last block turns them into
+// tau and edge (tinfo: tau, edge low word, edge high word).
+__global__ __launch_bounds__(64 * kWaves) void k_band_fine(
+    GeomDev g, const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
+    const uint2* __restrict__ lu, const int4* __restrict__ cinfo, int k,
+    uint32_t* __restrict__ hist, uint32_t* __restrict__ arrive, int4* __restrict__ tinfo,
+    int32_t* __restrict__ topk, int32_t* __restrict__ tcnt) {
+    __shared__ uint32_t hf[2 * kBins];
+    __shared__ int wsum[kWaves], s_flag, s_out[4];
+    const int r = blockIdx.y, X = gridDim.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nc = cnt[r], n = nc * 64;
     const int64_t off = g.chunk_off[r];
-    int32_t* sc_out = scnt + (int64_t)r * nslices;
-    if (p0 >= n) {
-        if (blockIdx.x < nslices) sc_out[blockIdx.x] = 0;
-        return;
-    }
-    const int p1 = min(n, p0 + kSlice);
-    if (n <= k) {  // every candidate is kept, already ascending
-        for (int p = p0 + tid; p < p1; p += 256)
+    if (n <= k) {  // every candidate is kept, already in token order
+        for (int p = blockIdx.x * blockDim.x + tid; p < n; p += X * blockDim.x)
             topk[(int64_t)r * k + p] = sel[off + (p >> 6)] * 64 + (p & 63);
         if (blockIdx.x == 0 && tid == 0) tcnt[r] = n;
-        if (tid == 0) sc_out[blockIdx.x] = 0;
         return;
     }
-    uint32_t lo, hi;
-    band_range(g, cnt, stats, r, goff, red, lo, hi);
-    const int shift = band_shift(lo, hi);
-    const int nb = (int)((((uint64_t)hi - lo + 1) + (1ull << shift) - 1) >> shift);
-    const uint32_t* gh = band_hist + (int64_t)r * kBandBins;
-    // suffix scan from the top bin: thread t owns 16 bins
-    int c16[16], s16 = 0;
+    const int4 ci = cinfo[r];
+    const uint32_t cL = (uint32_t)ci.x, cU = (uint32_t)ci.z;
+    for (int i = tid; i < 2 * kBins; i += blockDim.x) hf[i] = 0;
+    __syncthreads();
+    int c0, c1;
+    block_chunks(nc, X, blockIdx.x, c0, c1);
+    constexpr int U4 = 4;
+    for (int cb = c0 + wv; cb < c1; cb += kWaves * U4) {
+        uint2 f[U4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int bn = nb - 1 - (16 * tid + j);
-        c16[j] = bn >= 0 ? (int)gh[bn] : 0;
-        s16 += c16[j];
-    }
-    int tot;
-    const int excl = block_scan<4>(s16, wsum, tot);
-    if (excl < k && excl + s16 >= k) {
-        int acc = excl, j = 0;
-        for (; j < 15; ++j) {
-            if (acc + c16[j] >= k) break;
-            acc += c16[j];
+        for (int u = 0; u < U4; ++u) {
+            const int c = cb + kWaves * u;
+            f[u] = c < c1 ? lu[(off + c) * 64 + lane] : make_uint2(0u, 0u);
         }
-        s_tau = lo + ((uint32_t)(nb - 1 - (16 * tid + j)) << shift);
+#pragma unroll
+        for (int u = 0; u < U4; ++u) {
+            if (cb + kWaves * u >= c1) break;
+            if ((f[u].x >> 20) == cL) atomicAdd(&hf[(f[u].x >> 8) & (kBins - 1)], 1u);
+            if ((f[u].y >> 20) == cU) atomicAdd(&hf[kBins + ((f[u].y >> 8) & (kBins - 1))], 1u);
+        }
     }
     __syncthreads();
-    const uint32_t tau = s_tau;
-    const float2* v = lu + off * 64;
-    int32_t* ul = ulist + off * 64 + p0;  // this slice's list
-    int base = 0;
-    for (int q0 = p0; q0 < p1; q0 += 4 * 256) {
-        const int pb = q0 + 4 * tid;
-        bool take[4];
-        int tc = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            take[j] = pb + j < p1 && fkey(v[pb + j].y) >= tau;
-            tc += take[j];
-        }
-        int pos = base + block_scan<4>(tc, wsum, tot);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (take[j]) ul[pos++] = pb + j;
-        base += tot;
+    uint32_t* gh = hist + (int64_t)r * kHist + 2 * kBins;
+    for (int i = tid; i < 2 * kBins; i += blockDim.x)
+        if (hf[i]) hist_add(&gh[i], hf[i]);
+    if (!last_arrival(&arrive[2 * r + 1], X, &s_flag)) return;
+    take_hist(gh, hf, blockDim.x);
+    kth_bin<kWaves>(hf, k - ci.y, wsum, &s_out[0]);
+    kth_bin<kWaves>(hf + kBins, k - ci.w, wsum, &s_out[2]);
+    if (tid == 0) {
+        const uint32_t tau = (cL << 20) | ((uint32_t)s_out[0] << 8);
+        const uint64_t edge = ((uint64_t)cU << 20) + ((uint64_t)(s_out[2] + 1) << 8);
+        tinfo[r] = make_int4((int)tau, (int)(uint32_t)edge, (int)(uint32_t)(edge >> 32), 0);
+        __hip_atomic_store(&arrive[2 * r + 1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tid == 0) sc_out[blockIdx.x] = base;
 }
 
-// K3: canonical scores of the listed candidates of one slice.  Block = 32
-// candidates x 8 head groups; each thread runs its heads' fma chains in
-// element order, the head sum then runs in head order on one thread per
-// candidate.
+// K3.  Grid (X, B).  Block x lists, in token order, the band candidates of
+// its chunks at (off + c0) * 64 (positions p into the request's candidates;
+// key 0xffffffff for certain ones) and its count at scnt[r][x]; its
+// uncertain ones get the canonical score as their key.  For the score each
+// token is taken by TPT = min(H, 64) lanes, one or two heads per lane, with
+// the lane's query rows held in registers (bf16 pairs); the key row goes
+// through LDS as fp32, each head runs its fma chain in element order, then
+// one lane runs the head sum in head order.
 template <int KDT, int D, int H>
-__global__ __launch_bounds__(256) void k_rescore(
+__global__ __launch_bounds__(64 * kWaves) void k_band_list(
     GeomDev g, const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
-    const int32_t* __restrict__ ulist, const int32_t* __restrict__ scnt, int nslices, int k,
+    const uint2* __restrict__ lu, const int4* __restrict__ tinfo, int k,
     const uint8_t* __restrict__ pages, int64_t page_bytes, int64_t ikey_off,
     const int32_t* __restrict__ page_table, const float* __restrict__ ikey_scale,
-    const uint16_t* __restrict__ q, const float* __restrict__ w, float* __restrict__ exact) {
+    const uint16_t* __restrict__ q, const float* __restrict__ w, int32_t* __restrict__ bl,
+    uint32_t* __restrict__ bk, int32_t* __restrict__ ul, int32_t* __restrict__ scnt) {
+    constexpr int TPT = H < 64 ? H : 64;  // lanes per token
+    constexpr int HPT = H / TPT;          // heads per lane
+    constexpr int TPW = 64 / TPT;         // tokens per wave
     constexpr int EB = KDT == LSA_BF16 ? 2 : 1;
     constexpr int ROWB = D * EB;
-    constexpr int HPG = H / 8;  // heads per thread
-    constexpr int GS = HPG * D + 4;  // head-group stride: the 8 groups hit distinct banks
-    __shared__ __attribute__((aligned(16))) float qf[8 * GS];
+    __shared__ __attribute__((aligned(16))) float kf[kWaves][TPW][D];
+    __shared__ float rel[kWaves][TPW][H];
     __shared__ float wf[H];
-    __shared__ float rel[32][H + 1];
-    const int r = blockIdx.y, tid = threadIdx.x;
-    const int n = cnt[r] * 64;
-    if (n <= k || blockIdx.x * kSlice >= n) return;
-    const int m = scnt[(int64_t)r * nslices + blockIdx.x];
-    if (m == 0) return;
-    const uint32_t* qs = (const uint32_t*)(q + (int64_t)r * H * D);
-#pragma unroll 4
-    for (int e = tid; e < H * D / 8; e += 256) {
-        const uint4 x = ((const uint4*)qs)[e];
-        const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
-        const int f0 = 8 * e;  // element index h*D + i; group h / HPG
-        const int dst = (f0 / (HPG * D)) * GS + f0 % (HPG * D);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            qf[dst + 2 * j] = __uint_as_float(w4[j] << 16);
-            qf[dst + 2 * j + 1] = __uint_as_float(w4[j] & 0xffff0000u);
+    __shared__ int s_nb[kWaves], s_nu[kWaves];
+    const int r = blockIdx.y, X = gridDim.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nc = cnt[r];
+    if (nc * 64 <= k) return;
+    const int64_t off = g.chunk_off[r];
+    const int4 ti = tinfo[r];
+    const uint32_t tau = (uint32_t)ti.x;
+    const uint64_t edge = (uint64_t)(uint32_t)ti.y | ((uint64_t)(uint32_t)ti.z << 32);
+    int c0, c1;
+    block_chunks(nc, X, blockIdx.x, c0, c1);
+    const int64_t seg = (off + c0) * 64;
+    const uint64_t lt = (1ull << lane) - 1;
+    // ordered lists: round j takes chunk c0 + 4j + wave
+    int nb = 0, nu = 0;
+    uint2 f = make_uint2(0u, 0u);
+    if (c0 + wv < c1) f = lu[(off + c0 + wv) * 64 + lane];
+    for (int cb = c0; cb < c1; cb += kWaves) {
+        const int c = cb + wv;
+        const bool have = c < c1;
+        const uint2 cur = f;
+        if (c + kWaves < c1) f = lu[(off + c + kWaves) * 64 + lane];
+        const bool band = have && cur.y >= tau;
+        const bool sure = band && (uint64_t)cur.x >= edge;
+        const bool unc = band && !sure;
+        const uint64_t mb = __ballot(band), mu = __ballot(unc);
+        if (lane == 0) {
+            s_nb[wv] = __popcll(mb);
+            s_nu[wv] = __popcll(mu);
+        }
+        __syncthreads();
+        int pb = nb, pu = nu;
+        for (int i = 0; i < kWaves; ++i) {
+            pb += i < wv ? s_nb[i] : 0;
+            pu += i < wv ? s_nu[i] : 0;
+            nb += s_nb[i];
+            nu += s_nu[i];
+        }
+        __syncthreads();
+        if (band) {
+            const int j = pb + __popcll(mb & lt);
+            bl[seg + j] = c * 64 + lane;
+            bk[seg + j] = sure ? 0xffffffffu : 0u;
+            if (unc) ul[seg + pu + __popcll(mu & lt)] = j;
         }
     }
-    for (int e = tid; e < H; e += 256) wf[e] = w[(int64_t)r * H + e];
+    if (tid == 0) scnt[(int64_t)r * X + blockIdx.x] = nb;
+    if (nu == 0) return;  // uniform
+    // canonical scores of this block's uncertain entries
+    __threadfence_block();
+    for (int e = tid; e < H; e += blockDim.x) wf[e] = w[(int64_t)r * H + e];
     __syncthreads();
-    const int64_t off = g.chunk_off[r];
-    const int32_t* ul = ulist + off * 64 + blockIdx.x * kSlice;
-    float* ex = exact + off * 64 + blockIdx.x * kSlice;
-    const int tok = tid >> 3, hg = tid & 7;
-    for (int j0 = 0; j0 < m; j0 += 32) {
-        const int j = j0 + tok;
-        const bool valid = j < m;
-        int p = 0;
+    const int lt2 = lane % TPT, ts = lane / TPT;
+    uint32_t qp[HPT][D / 2];
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) {
+        const uint4* src = (const uint4*)(q + ((int64_t)r * H + lt2 + TPT * j) * D);
+#pragma unroll
+        for (int x = 0; x < D / 8; ++x) {
+            const uint4 v = src[x];
+            qp[j][4 * x] = v.x;
+            qp[j][4 * x + 1] = v.y;
+            qp[j][4 * x + 2] = v.z;
+            qp[j][4 * x + 3] = v.w;
+        }
+    }
+    float* kr = kf[wv][ts];
+    float* rr = rel[wv][ts];
+    for (int u0 = wv * TPW; u0 < nu; u0 += kWaves * TPW) {
+        const int u = u0 + ts;
+        const bool valid = u < nu;
+        int64_t e = 0;
+        float scale = 1.0f;
         if (valid) {
-            p = ul[j];
+            e = seg + ul[seg + u];
+            const int p = bl[e];
             const int c = sel[off + (p >> 6)];
             const int64_t pg = page_table ? (int64_t)page_table[off + c] : off + c;
             const uint8_t* row = pages + pg * page_bytes + ikey_off + (int64_t)(p & 63) * ROWB;
-            float kf[D];
-#pragma unroll
-            for (int x = 0; x < ROWB / 16; ++x) {
-                const uint4 v = *(const uint4*)(row + 16 * x);
-                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (KDT == LSA_BF16) {
-                        kf[8 * x + 2 * e] = __uint_as_float(w4[e] << 16);
-                        kf[8 * x + 2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
-                    } else {
-                        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[e], false);
-                        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w4[e], true);
-                        kf[16 * x + 4 * e + 0] = lo[0];
-                        kf[16 * x + 4 * e + 1] = lo[1];
-                        kf[16 * x + 4 * e + 2] = hi[0];
-                        kf[16 * x + 4 * e + 3] = hi[1];
-                    }
+            if constexpr (KDT == LSA_FP8_E4M3FN) scale = ikey_scale[off + c];
+            for (int e4 = lt2; e4 < D / 4; e4 += TPT) {
+                float4 x;
+                if constexpr (KDT == LSA_BF16) {
+                    const uint2 b = *(const uint2*)(row + 8 * e4);
+                    x = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
+                                    __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u));
+                } else {
+                    const uint32_t b = *(const uint32_t*)(row + 4 * e4);
+                    const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, false);
+                    const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, true);
+                    x = make_float4(lo2[0], lo2[1], hi2[0], hi2[1]);
                 }
+                *(float4*)&kr[4 * e4] = x;
             }
-            float a[HPG];
-#pragma unroll
-            for (int u = 0; u < HPG; ++u) a[u] = 0.0f;
-#pragma unroll
-            for (int e = 0; e < D; e += 4) {
-#pragma unroll
-                for (int u = 0; u < HPG; ++u) {
-                    const float4 x = *(const float4*)&qf[hg * GS + u * D + e];
-                    a[u] = __builtin_fmaf(x.x, kf[e], a[u]);
-                    a[u] = __builtin_fmaf(x.y, kf[e + 1], a[u]);
-                    a[u] = __builtin_fmaf(x.z, kf[e + 2], a[u]);
-                    a[u] = __builtin_fmaf(x.w, kf[e + 3], a[u]);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < HPG; ++u) rel[tok][hg * HPG + u] = a[u] > 0.0f ? a[u] : 0.0f;
         }
-        __syncthreads();
-        if (valid && hg == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (valid) {
+#pragma unroll
+            for (int j = 0; j < HPT; ++j) {
+                float a = 0.0f;
+#pragma unroll
+                for (int i = 0; i < D; i += 4) {
+                    const float4 x = *(const float4*)&kr[i];
+                    const uint32_t q01 = qp[j][i / 2], q23 = qp[j][i / 2 + 1];
+                    a = __builtin_fmaf(__uint_as_float(q01 << 16), x.x, a);
+                    a = __builtin_fmaf(__uint_as_float(q01 & 0xffff0000u), x.y, a);
+                    a = __builtin_fmaf(__uint_as_float(q23 << 16), x.z, a);
+                    a = __builtin_fmaf(__uint_as_float(q23 & 0xffff0000u), x.w, a);
+                }
+                rr[lt2 + TPT * j] = a > 0.0f ? a : 0.0f;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (valid && lt2 == 0) {
             float I = 0.0f;
-            for (int h = 0; h < H; ++h) I = __builtin_fmaf(wf[h], rel[tok][h], I);
-            if constexpr (KDT == LSA_FP8_E4M3FN) I = I * ikey_scale[off + sel[off + (p >> 6)]];
-            ex[j] = I;
+#pragma unroll 8
+            for (int h = 0; h < H; ++h) I = __builtin_fmaf(wf[h], rr[h], I);
+            if constexpr (KDT == LSA_FP8_E4M3FN) I = I * scale;
+            bk[e] = fkey(I);
         }
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();  // kf / rel are rewritten next round
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
-// K4: exact top-k among the listed candidates of one request (one block).
-// The slice lists are gathered in order into LDS (up to kListCap entries),
-// the k-th largest key is found by 12/12/8-bit radix select on LDS, then the
-// emit keeps keys above it and the lowest-index ties.  Larger lists (only
-// with massive ties) take the same steps reading global memory.
-constexpr int kListCap = 8192;
-
-__global__ __launch_bounds__(kT) void k_topk_list(GeomDev g, const int32_t* __restrict__ sel,
+// K4.  Exact top-k over the band of one request (one block).  The block
+// lists of K3 are gathered in order into LDS (up to kListCap entries), the
+// k-th largest key is found by 12/12/8-bit radix select, then the emit keeps
+// keys above it and the lowest-index ties.  Larger bands (only with massive
+// ties) take the same steps reading global memory.
+__global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __restrict__ sel,
                                                   const int32_t* __restrict__ cnt,
-                                                  const int32_t* __restrict__ ulist,
-                                                  const int32_t* __restrict__ scnt, int nslices,
-                                                  const float* __restrict__ exact, int k,
+                                                  const int32_t* __restrict__ scnt, int X,
+                                                  const int32_t* __restrict__ bl,
+                                                  const uint32_t* __restrict__ bk, int k,
                                                   int32_t* __restrict__ topk,
                                                   int32_t* __restrict__ tcnt) {
     __shared__ uint32_t hist[4096];
     __shared__ uint32_t lkey[kListCap];
     __shared__ int32_t lpos[kListCap];
-    __shared__ int soff[1024 + 1];
+    __shared__ int boff[kMaxSeg + 1];
     __shared__ int wsum[kTW];
     __shared__ uint32_t s_prefix;
     __shared__ int s_remaining, s_eq;
     const int r = blockIdx.x, tid = threadIdx.x;
-    const int n = cnt[r] * 64;
-    if (n <= k) return;  // k_band_list already wrote the result
+    const int nc = cnt[r];
+    if (nc * 64 <= k) return;  // k_band_fine already wrote the result
     const int64_t off = g.chunk_off[r];
-    const int ns = (n + kSlice - 1) / kSlice;
-    // slice offsets (ns <= nslices <= 1024)
-    int cnt_t = tid < ns ? scnt[(int64_t)r * nslices + tid] : 0;
+    const int C = (nc + X - 1) / X;  // chunks per K3 block
     int tot;
-    const int ex0 = block_scan<kTW>(cnt_t, wsum, tot);
-    if (tid < ns) soff[tid] = ex0;
-    if (tid == 0) soff[ns] = tot;
+    {
+        const int v = tid < X ? scnt[(int64_t)r * X + tid] : 0;
+        const int ex = block_scan<kTW>(v, wsum, tot);
+        if (tid < X) boff[tid] = ex;
+        if (tid == 0) boff[X] = tot;
+    }
     __syncthreads();
-    const int m = soff[ns];
+    const int m = boff[X];
     const bool in_lds = m <= kListCap;
-    // position j of the ordered list -> (slice, index)
+    auto gidx = [&](int j) -> int64_t {  // list position j -> workspace index
+        int lo = 0, hi = X - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (boff[mid] <= j) lo = mid;
+            else hi = mid - 1;
+        }
+        return (off + (int64_t)lo * C) * 64 + (j - boff[lo]);
+    };
     auto at = [&](int j, uint32_t& key, int32_t& pos) {
         if (in_lds) {
             key = lkey[j];
             pos = lpos[j];
             return;
         }
-        int lo = 0, hi = ns - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (soff[mid] <= j) lo = mid;
-            else hi = mid - 1;
-        }
-        const int64_t e = off * 64 + (int64_t)lo * kSlice + (j - soff[lo]);
-        key = fkey(exact[e]);
-        pos = ulist[e];
+        const int64_t e = gidx(j);
+        key = bk[e];
+        pos = bl[e];
     };
     if (in_lds) {
-        for (int sidx = 0; sidx < ns; ++sidx) {
-            const int c = soff[sidx + 1] - soff[sidx];
-            const int64_t e0 = off * 64 + (int64_t)sidx * kSlice;
-            for (int j = tid; j < c; j += kT) {
-                lkey[soff[sidx] + j] = fkey(exact[e0 + j]);
-                lpos[soff[sidx] + j] = ulist[e0 + j];
-            }
+        for (int j = tid; j < m; j += kT) {
+            const int64_t e = gidx(j);
+            lkey[j] = bk[e];
+            lpos[j] = bl[e];
         }
         __syncthreads();
     }
@@ -657,69 +701,97 @@ __global__ __launch_bounds__(kT) void k_topk_list(GeomDev g, const int32_t* __re
     if (tid == 0) tcnt[r] = base;
 }
 
+__global__ void k_zero_u32(uint32_t* __restrict__ p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
 }  // namespace
 
-static int max_slices(const GeomDev& g);
-
-bool band_fits(const GeomDev& g) { return max_slices(g) <= 1024; }
-
 bool band_supported(lsa_dtype idx_dt, lsa_dtype q_dt, int H, int d) {
-    // k_rescore keeps the queries (fp32) and the ReLU outputs in LDS
-    const size_t lds = (size_t)H * d * 4 + 32 * (H + 1) * 4 + 1024;
     return (idx_dt == LSA_BF16 || idx_dt == LSA_FP8_E4M3FN) && q_dt == LSA_BF16 &&
-           (d == 64 || d == 128) && (H == 16 || H == 32 || H == 64 || H == 128) &&
-           lds <= 64 * 1024;
+           (d == 64 || d == 128) && (H == 16 || H == 32 || H == 64 || H == 128);
 }
 
-static int max_slices(const GeomDev& g) {
+static int max_hist(const GeomDev& g) {
     int mx = 0;
     for (int r = 0; r < g.B; ++r) mx = g.nhist[r] > mx ? g.nhist[r] : mx;
-    return (mx * 64 + kSlice - 1) / kSlice;
+    return mx;
 }
+
+// K1 blocks per request: about two blocks per CU over the whole batch, no
+// more than the longest history needs.
+static int k1_blocks(const GeomDev& g) {
+    int x = (512 + g.B - 1) / g.B;
+    const int need = (max_hist(g) + kWaves - 1) / kWaves;
+    if (x > need) x = need;
+    return x < 1 ? 1 : x;
+}
+
+// K2 / K3 blocks per request: about one per CU over the batch, at least one
+// chunk each, no more than K4 gathers.
+static int k23_blocks(const GeomDev& g) {
+    int x = (256 + g.B - 1) / g.B;
+    const int mh = max_hist(g);
+    if (x > mh) x = mh;
+    if (x > kMaxSeg) x = kMaxSeg;
+    return x < 1 ? 1 : x;
+}
+
+// Workspace: the histograms and arrival counters first (zero on entry
+// unless the caller knows they are; every launch leaves them zero), then the
+// rest.
+static size_t clean_words(const GeomDev& g) { return (size_t)g.B * (kHist + 2); }
 
 size_t band_ws_bytes(const GeomDev& g) {
     const size_t nc = (size_t)g.chunk_off[g.B] * 64 + 64;
-    const size_t items = (size_t)g.chunk_off[g.B] / kBandWaves + g.B + 1;
-    const size_t ns = (size_t)g.B * (max_slices(g) + 1);
-    return align_up(nc * sizeof(float2), 256) + align_up(items * sizeof(uint2), 256) +
-           2 * align_up(nc * 4, 256) + align_up(ns * 4, 256) +
-           align_up((size_t)g.B * kBandBins * 4, 256);
+    return align_up(clean_words(g) * 4, 256) + 2 * align_up((size_t)g.B * sizeof(int4), 256) +
+           align_up(nc * sizeof(uint2), 256) + 3 * align_up(nc * 4, 256) +
+           align_up((size_t)g.B * k23_blocks(g) * 4, 256);
+}
+
+hipError_t launch_band_clear(const GeomDev& g, void* ws, hipStream_t s) {
+    const int n = (int)clean_words(g);
+    hipLaunchKernelGGL(k_zero_u32, dim3((n + 255) / 256), dim3(256), 0, s, (uint32_t*)ws, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_t* cnt,
                               const void* pages, int64_t page_bytes, int64_t ikey_off,
                               const int32_t* page_table, lsa_dtype idx_dt,
                               const float* ikey_scale, const void* q, const float* w, int H,
-                              int d, int k, int32_t* topk, int32_t* tcnt, void* ws, int grid_hint,
+                              int d, int k, int32_t* topk, int32_t* tcnt, void* ws, bool ws_clean,
                               hipStream_t s) {
     const size_t nc = (size_t)g.chunk_off[g.B] * 64 + 64;
-    const size_t items = (size_t)g.chunk_off[g.B] / kBandWaves + g.B + 1;
-    const int nslices = max_slices(g) > 0 ? max_slices(g) : 1;
+    const int X1 = k1_blocks(g), X2 = k23_blocks(g);
+    hipError_t e;
+    if (!ws_clean && (e = launch_band_clear(g, ws, s)) != hipSuccess) return e;
     uint8_t* b = (uint8_t*)ws;
-    float2* lu = (float2*)b;
-    b += align_up(nc * sizeof(float2), 256);
-    uint2* stats = (uint2*)b;
-    b += align_up(items * sizeof(uint2), 256);
-    int32_t* ulist = (int32_t*)b;
+    uint32_t* hist = (uint32_t*)b;
+    uint32_t* arrive = hist + (size_t)g.B * kHist;
+    b += align_up(clean_words(g) * 4, 256);
+    int4* cinfo = (int4*)b;
+    b += align_up((size_t)g.B * sizeof(int4), 256);
+    int4* tinfo = (int4*)b;
+    b += align_up((size_t)g.B * sizeof(int4), 256);
+    uint2* lu = (uint2*)b;
+    b += align_up(nc * sizeof(uint2), 256);
+    int32_t* bl = (int32_t*)b;
     b += align_up(nc * 4, 256);
-    float* exact = (float*)b;
+    uint32_t* bk = (uint32_t*)b;
+    b += align_up(nc * 4, 256);
+    int32_t* ul = (int32_t*)b;
     b += align_up(nc * 4, 256);
     int32_t* scnt = (int32_t*)b;
-    b += align_up((size_t)g.B * (max_slices(g) + 1) * 4, 256);
-    uint32_t* bhist = (uint32_t*)b;
     const uint8_t* pg = (const uint8_t*)pages;
     const uint16_t* qq = (const uint16_t*)q;
-    int grid = grid_hint;
-    if (grid <= 0) grid = (int)(items < 4096 ? items : 4096);
-    if (grid < 1) grid = 1;
     const int Hh = H;
-    hipError_t e = hipErrorInvalidValue;
+    e = hipErrorInvalidValue;
     timing_begin("k_refine_mfma", s);
 #define LSA_K1(KDT, D, HH)                                                                        \
     if (idx_dt == KDT && d == D && Hh == HH) {                                                    \
-        hipLaunchKernelGGL((k_refine_mfma<KDT, D, HH>), dim3(grid), dim3(64 * kBandWaves), 0, s, g, \
-                           sel, cnt, pg, page_bytes, ikey_off, page_table, ikey_scale, qq, w, lu,  \
-                           stats, bhist);                                                         \
+        hipLaunchKernelGGL((k_refine_mfma<KDT, D, HH>), dim3(X1, g.B), dim3(64 * kWaves), 0, s, g, \
+                           sel, cnt, pg, page_bytes, ikey_off, page_table, ikey_scale, qq, w, k,   \
+                           lu, hist, arrive, cinfo);                                              \
         e = hipGetLastError();                                                                    \
     }
     LSA_K1(LSA_BF16, 128, 16) LSA_K1(LSA_BF16, 128, 32) LSA_K1(LSA_BF16, 128, 64)
@@ -731,37 +803,32 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
 #undef LSA_K1
     timing_end("k_refine_mfma", s);
     if (e != hipSuccess) return e;
-    const dim3 sg(nslices, g.B);
-    timing_begin("k_band_hist", s);
-    hipLaunchKernelGGL(k_band_hist, sg, dim3(256), 0, s, g, cnt, lu, stats, k, bhist);
-    timing_end("k_band_hist", s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    timing_begin("k_band_list", s);
-    hipLaunchKernelGGL(k_band_list, sg, dim3(256), 0, s, g, sel, cnt, lu, stats, k, bhist, ulist,
-                       scnt, topk, tcnt, nslices);
-    timing_end("k_band_list", s);
+    timing_begin("k_band_fine", s);
+    hipLaunchKernelGGL(k_band_fine, dim3(X2, g.B), dim3(64 * kWaves), 0, s, g, sel, cnt, lu, cinfo,
+                       k, hist, arrive, tinfo, topk, tcnt);
+    timing_end("k_band_fine", s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = hipErrorInvalidValue;
-    timing_begin("k_rescore", s);
+    timing_begin("k_band_list", s);
 #define LSA_K3(KDT, D, HH)                                                                        \
     if (idx_dt == KDT && d == D && Hh == HH) {                                                    \
-        hipLaunchKernelGGL((k_rescore<KDT, D, HH>), sg, dim3(256), 0, s, g, sel, cnt, ulist, scnt, \
-                           nslices, k, pg, page_bytes, ikey_off, page_table, ikey_scale, qq, w,   \
-                           exact);                                                                \
+        hipLaunchKernelGGL((k_band_list<KDT, D, HH>), dim3(X2, g.B), dim3(64 * kWaves), 0, s, g,   \
+                           sel, cnt, lu, tinfo, k, pg, page_bytes, ikey_off, page_table,          \
+                           ikey_scale, qq, w, bl, bk, ul, scnt);                                  \
         e = hipGetLastError();                                                                    \
     }
     LSA_K3(LSA_BF16, 128, 16) LSA_K3(LSA_BF16, 128, 32) LSA_K3(LSA_BF16, 128, 64)
-    LSA_K3(LSA_BF16, 64, 16) LSA_K3(LSA_BF16, 64, 32) LSA_K3(LSA_BF16, 64, 64)
-    LSA_K3(LSA_BF16, 64, 128)
+    LSA_K3(LSA_BF16, 128, 128) LSA_K3(LSA_BF16, 64, 16) LSA_K3(LSA_BF16, 64, 32)
+    LSA_K3(LSA_BF16, 64, 64) LSA_K3(LSA_BF16, 64, 128)
     LSA_K3(LSA_FP8_E4M3FN, 128, 16) LSA_K3(LSA_FP8_E4M3FN, 128, 32) LSA_K3(LSA_FP8_E4M3FN, 128, 64)
-    LSA_K3(LSA_FP8_E4M3FN, 64, 16) LSA_K3(LSA_FP8_E4M3FN, 64, 32) LSA_K3(LSA_FP8_E4M3FN, 64, 64)
-    LSA_K3(LSA_FP8_E4M3FN, 64, 128)
+    LSA_K3(LSA_FP8_E4M3FN, 128, 128) LSA_K3(LSA_FP8_E4M3FN, 64, 16) LSA_K3(LSA_FP8_E4M3FN, 64, 32)
+    LSA_K3(LSA_FP8_E4M3FN, 64, 64) LSA_K3(LSA_FP8_E4M3FN, 64, 128)
 #undef LSA_K3
-    timing_end("k_rescore", s);
+    timing_end("k_band_list", s);
     if (e != hipSuccess) return e;
-    timing_begin("k_topk_list", s);
-    hipLaunchKernelGGL(k_topk_list, dim3(g.B), dim3(kT), 0, s, g, sel, cnt, ulist, scnt, nslices,
-                       exact, k, topk, tcnt);
-    timing_end("k_topk_list", s);
+    timing_begin("k_topk_band", s);
+    hipLaunchKernelGGL(k_topk_band, dim3(g.B), dim3(kT), 0, s, g, sel, cnt, scnt, X2, bl, bk, k,
+                       topk, tcnt);
+    timing_end("k_topk_band", s);
     return hipGetLastError();
 }

@@ -27,6 +27,7 @@ struct lsa_ctx {
     int32_t* sel[2] = {nullptr, nullptr};
     int32_t* cnt[2] = {nullptr, nullptr};
     float* scores = nullptr;
+    bool band_clean = false;  // band workspace histograms known to be zero
     int32_t* topk_tmp = nullptr;
     int32_t* tcnt_tmp = nullptr;
     void* attn_ws = nullptr;
@@ -124,7 +125,9 @@ lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc) {
     if (desc->idx_dt == LSA_FP8_E4M3FN && !desc->ikey_scale && g.chunk_off[g.B] > 0)
         return LSA_ERR_INVALID_ARG;
     if (desc->kv.ikey_off % 16 || desc->kv.page_bytes % 16) return LSA_ERR_INVALID_ARG;
-    if (((int64_t)desc->H * desc->d + desc->H) * 4 > 65536) return LSA_ERR_UNSUPPORTED;
+    if (!band_supported(desc->idx_dt, desc->q_dt, desc->H, desc->d) &&
+        ((int64_t)desc->H * desc->d + desc->H) * 4 > 65536)
+        return LSA_ERR_UNSUPPORTED;
     if (desc->kv.ikey_off < (int64_t)LSA_CHUNK * desc->kv.row_bytes ||
         desc->kv.page_bytes < desc->kv.ikey_off + (int64_t)LSA_CHUNK * desc->d * esz(desc->idx_dt))
         return LSA_ERR_INVALID_ARG;
@@ -237,12 +240,15 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
         int32_t* tc = out->topk_cnt ? out->topk_cnt + (size_t)j * g.B : x->tcnt_tmp;
         const uint8_t* qr = (const uint8_t*)in->q_refine + j * qr_step;
         const float* wr = in->w_refine + (size_t)j * g.B * d.H;
-        if (groups > 0 && band_supported(d.idx_dt, d.q_dt, d.H, d.d) && band_fits(g)) {
+        if (groups > 0 && band_supported(d.idx_dt, d.q_dt, d.H, d.d)) {
+            const bool clean = x->band_clean;
+            x->band_clean = false;  // until the chain is queued whole
             if (launch_refine_band(g, x->sel[cur], x->cnt[cur], lsa_pool_slots(d.pool),
                                    d.kv.page_bytes, d.kv.ikey_off, x->pt[cur], d.idx_dt,
-                                   d.ikey_scale, qr, wr, d.H, d.d, d.k, tk, tc, x->scores, groups,
+                                   d.ikey_scale, qr, wr, d.H, d.d, d.k, tk, tc, x->scores, clean,
                                    ms) != hipSuccess)
                 return LSA_ERR_HIP;
+            x->band_clean = true;
         } else {
             if (groups > 0 &&
                 launch_refine(g, x->sel[cur], x->cnt[cur], lsa_pool_slots(d.pool), d.kv.page_bytes,

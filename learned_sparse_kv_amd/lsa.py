@@ -280,7 +280,7 @@ def lsa_step64(ctx: Ctx, win, out, main=None, copy=None):
 
 # ---------------------------------------------------------------- diagnostics
 KERNELS = ("k_fuse_query", "k_score", "k_select", "k_refine", "k_topk", "k_refine_mfma",
-           "k_band_hist", "k_band_list", "k_rescore", "k_topk_list", "k_attn_mla", "k_attn_f32", "k_attn_merge",
+           "k_band_fine", "k_band_list", "k_topk_band", "k_attn_mla", "k_attn_f32", "k_attn_merge",
            "k_gather")
 
 
