@@ -9,30 +9,25 @@
 //     inputs, exact products, fp32 accumulation), I' = sum_h w_h ReLU(a'_h),
 //     and a rigorous bound E with |I' - I| <= E.  Writes L = I' - E and
 //     U = I' + E as order-preserving 32-bit keys and adds to the request's
-//     coarse histograms of L and U (top 12 key bits).  The last block of a
-//     request to finish finds the coarse bins holding the k-th largest L
-//     and the k-th largest U.
-//  K2 k_band_fine    fine histograms (256-key bins) of the keys inside those
-//     two coarse bins; the last block finds tau = lowest key of the fine bin
+//     coarse histograms of L and U (top 10 key bits).
+//  K2 k_band_fine    every block finds the coarse bins holding the k-th
+//     largest L and the k-th largest U, then adds fine histograms (1024-key
+//     bins) of the keys inside those two coarse bins.
+//  K3 k_band_list    every block finds tau = lowest key of the fine bin
 //     holding the k-th largest L and edge = first key above the fine bin
-//     holding the k-th largest U.
-//  K3 k_band_list    candidates with U >= tau form the band (never fewer
-//     than k); each block lists its share in token order.  Those with
-//     L >= edge are certain to be in the top-k; the rest of the band
-//     (uncertain) gets the canonical score, by the same block.
+//     holding the k-th largest U.  Candidates with U >= tau form the band
+//     (never fewer than k); each block lists its share in token order.
+//     Those with L >= edge are certain to be in the top-k; the rest of the
+//     band (uncertain) gets the canonical score, by the same block.
 //  K4 k_topk_band    exact top-k over the band (certain ones rank first),
-//     ties to the lower token, emitted in token order.
+//     ties to the lower token, emitted in token order; clears the
+//     histograms for the next launch.
 // Why it is exact.  A candidate outside the band has I <= U < tau, and at
 // least k candidates have I >= L >= tau: it is below k others.  A certain
 // candidate s has L_s >= edge; any t with I_t >= I_s has U_t >= L_s >= edge,
 // and fewer than k candidates (s included) have U >= edge: fewer than k
 // others can rank above s.  So the top-k is the certain set plus the best
 // of the uncertain ones, by canonical score and then by token.
-//
-// Blocks of one request meet through device-scope atomics: each adds its
-// histogram counts, then bumps the request's arrival counter; the block that
-// arrives last reads the totals, clears the histograms and the counter for
-// the next launch, and writes its result for the next kernel.
 //
 // The bound.  Both the canonical chain and the MFMA sum differ from the exact
 // dot product by at most gamma(n) * sum_i |q_i k_i| (any summation order,
@@ -58,8 +53,9 @@ constexpr float kU2 = 2.384185791015625e-07f;  // 2^-22: two ulps of fp32 per op
 __host__ __device__ constexpr float gam(int n) { return n * kU2 / (1.0f - n * kU2); }
 
 constexpr int kWaves = 4;         // waves per block of K1 and K3
-constexpr int kBins = 4096;       // coarse bins (key >> 20) and fine bins ((key >> 8) & 4095)
-constexpr int kHist = 4 * kBins;  // per request: coarse L, coarse U, fine L, fine U
+constexpr int kCoarse = 1024;     // coarse bins: key >> 22
+constexpr int kFine = 4096;       // fine bins inside one coarse bin: (key >> 10) & 4095
+constexpr int kHist = 2 * kCoarse + 2 * kFine;  // per request: coarse L, U, then fine L, U
 constexpr int kRedStride = 33;    // per-token row: 16 + 16 partial sums, |key|^2
 constexpr int kT = 1024, kTW = kT / 64;
 constexpr int kMaxSeg = 1024;     // band list segments (K3 blocks) per request, at most
@@ -115,18 +111,18 @@ __device__ __forceinline__ int block_scan(int v, int* wsum, int& total) {
     return wpre + incl - v;
 }
 
-// Bin holding the k-th largest entry of hist[0, kBins) -> out[0], and the
+// Bin holding the k-th largest entry of hist[0, NB) -> out[0], and the
 // number of entries in higher bins -> out[1].  Thread t owns the BPT bins
-// below kBins - t*BPT.  Every thread of the block (NW waves) must call; the
+// below NB - t*BPT.  Every thread of the block (NW waves) must call; the
 // caller guarantees at least k entries.
-template <int NW>
+template <int NB, int NW>
 __device__ __forceinline__ void kth_bin(const uint32_t* hist, int k, int* wsum, int* out) {
-    constexpr int BPT = kBins / (64 * NW);
+    constexpr int BPT = NB / (64 * NW);
     const int tid = threadIdx.x;
     int c[BPT], sum = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
-        c[j] = (int)hist[kBins - 1 - (tid * BPT + j)];
+        c[j] = (int)hist[NB - 1 - (tid * BPT + j)];
         sum += c[j];
     }
     int tot;
@@ -137,34 +133,16 @@ __device__ __forceinline__ void kth_bin(const uint32_t* hist, int k, int* wsum, 
             if (acc + c[j] >= k) break;
             acc += c[j];
         }
-        out[0] = kBins - 1 - (tid * BPT + j);
+        out[0] = NB - 1 - (tid * BPT + j);
         out[1] = acc;
     }
     __syncthreads();
 }
 
-__device__ __forceinline__ void hist_add(uint32_t* p, uint32_t v) {
-    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Arrival of this block at a request's counter (n blocks in all); true in
-// the block that arrives last.  The histogram adds are device-scope atomics
-// and every thread waits for its own before the block arrives, so the last
-// block finds every other block's adds in place (no cache write-back
-// needed: nothing else is read across blocks).
-__device__ __forceinline__ bool last_arrival(uint32_t* ctr, uint32_t n, int* s_flag) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
-    if (threadIdx.x == 0)
-        *s_flag = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
-    __syncthreads();
-    return *s_flag != 0;
-}
-
-// Moves a request's histogram pair (2 * kBins) into LDS, leaving zeros.
-__device__ __forceinline__ void take_hist(uint32_t* gh, uint32_t* lds, int nthreads) {
-    for (int i = threadIdx.x; i < 2 * kBins; i += nthreads)
-        lds[i] = __hip_atomic_exchange(&gh[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Copies n words of a histogram into LDS.
+__device__ __forceinline__ void load_hist(const uint32_t* gh, uint32_t* lds, int n) {
+#pragma unroll 8
+    for (int i = threadIdx.x; i < n; i += blockDim.x) lds[i] = gh[i];
     __syncthreads();
 }
 
@@ -173,28 +151,26 @@ __device__ __forceinline__ void take_hist(uint32_t* gh, uint32_t* lds, int nthre
 // 4X, and prefetches the next chunk's key rows while the current one is on
 // the matrix cores.  The query operands, weights and the bound's query term
 // are set up once per block.  The block's coarse histograms go to the
-// request's (hist, zero on entry) with one atomic per nonzero bin; the last
-// block writes the coarse bins of the k-th largest L and U to cinfo.
+// request's (hist, zero on entry) with one atomic per nonzero bin.
 template <int KDT, int D, int H>
 __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_refine_mfma(
     GeomDev g, const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
     const uint8_t* __restrict__ pages, int64_t page_bytes, int64_t ikey_off,
     const int32_t* __restrict__ page_table, const float* __restrict__ ikey_scale,
-    const uint16_t* __restrict__ q, const float* __restrict__ w, int k, uint2* __restrict__ lu,
-    uint32_t* __restrict__ hist, uint32_t* __restrict__ arrive, int4* __restrict__ cinfo) {
+    const uint16_t* __restrict__ q, const float* __restrict__ w, uint2* __restrict__ lu,
+    uint32_t* __restrict__ hist) {
     constexpr int EB = KDT == LSA_BF16 ? 2 : 1;
     constexpr int ROWB = D * EB;
     constexpr int KS = D / 32;   // MFMA k-steps
     constexpr int HB = H / 16;   // head blocks
     using Raw = std::conditional_t<KDT == LSA_BF16, uint4, uint2>;
-    __shared__ uint32_t hl[2 * kBins];  // coarse L bins, then coarse U bins
+    __shared__ uint32_t hl[2 * kCoarse];  // coarse L bins, then coarse U bins
     __shared__ float red[kWaves][64 * kRedStride];
-    __shared__ int wsum[kWaves], s_flag, s_out[4];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, lq = lane >> 4;
     const int r = blockIdx.y, X = gridDim.x;
     const int nc = cnt[r];
-    for (int i = tid; i < 2 * kBins; i += 64 * kWaves) hl[i] = 0;
+    for (int i = tid; i < 2 * kCoarse; i += 64 * kWaves) hl[i] = 0;
     __syncthreads();
     if ((int)blockIdx.x * kWaves < nc) {  // uniform across the block
         uint4 qb[HB][KS];
@@ -226,24 +202,38 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
 
         const int64_t off = g.chunk_off[r];
         const int stride = X * kWaves;
-        int i = blockIdx.x * kWaves + wv;
+        const int i0 = blockIdx.x * kWaves + wv;  // this wave's chunks: i0 + j * stride
+        const int nj = i0 < nc ? (nc - i0 + stride - 1) / stride : 0;
+        // chunk j0 + lane: page (slot) index and scale, 64 chunks at a time
+        int64_t pg_l = 0;
+        float sc_l = 1.0f;
+        auto load_idx = [&](int j0) {
+            if (j0 + lane < nj) {
+                const int c = sel[off + i0 + (j0 + lane) * stride];
+                pg_l = page_table ? (int64_t)page_table[off + c] : off + c;
+                if constexpr (KDT == LSA_FP8_E4M3FN) sc_l = ikey_scale[off + c];
+            }
+        };
         Raw raw[4][KS];
-        float scale_nx = 1.0f;
-        // key rows of chunk ci: A operands of tokens tb*16 + l16, dims ks*32 + lq*8 .. +8
-#define LSA_FETCH(ci)                                                                           \
-    {                                                                                           \
-        const int c_ = sel[off + (ci)];                                                         \
-        const int64_t pg_ = page_table ? (int64_t)page_table[off + c_] : off + c_;              \
-        const uint8_t* base_ = pages + pg_ * page_bytes + ikey_off;                             \
-        if constexpr (KDT == LSA_FP8_E4M3FN) scale_nx = ikey_scale[off + c_];                   \
-        _Pragma("unroll") for (int tb = 0; tb < 4; ++tb) {                                      \
-            _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) raw[tb][ks] =                     \
-                *(const Raw*)(base_ + (int64_t)(tb * 16 + l16) * ROWB + (ks * 32 + lq * 8) * EB); \
-        }                                                                                       \
-    }
-        if (i < nc) LSA_FETCH(i)
+        // key rows of chunk j: A operands of tokens tb*16 + l16, dims ks*32 + lq*8 .. +8
+        auto fetch = [&](int j) {
+            const int src = j & 63;
+            const int64_t pgo = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pg_l, src) |
+                                ((int64_t)__builtin_amdgcn_readlane((int)(pg_l >> 32), src) << 32);
+            const uint8_t* base = pages + pgo * page_bytes + ikey_off;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    raw[tb][ks] = *(const Raw*)(base + (tb * 16 + l16) * ROWB + (ks * 32 + lq * 8) * EB);
+        };
+        if (nj > 0) {
+            load_idx(0);
+            fetch(0);
+        }
         float* pr = red[wv];
-        for (; i < nc; i += stride) {
+        for (int j = 0; j < nj; ++j) {
+            const int i = i0 + j * stride;
             uint4 ka[4][KS];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
@@ -252,8 +242,11 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
                     if constexpr (KDT == LSA_BF16) ka[tb][ks] = raw[tb][ks];
                     else ka[tb][ks] = fp8x8_to_bf16x8(raw[tb][ks]);
                 }
-            const float scale = scale_nx;
-            if (i + stride < nc) LSA_FETCH(i + stride)
+            const float scale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), j & 63));
+            if (j + 1 < nj) {
+                if (((j + 1) & 63) == 0) load_idx(j + 1);
+                fetch(j + 1);
+            }
             // |key|^2 on the matrix cores: the diagonal of the 16x16 Gram block
             // of tokens tb*16..; lane (l16, lq) holds rows 4lq..4lq+3 of column l16
 #pragma unroll
@@ -315,28 +308,18 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
             E = (E * scale + 4 * kU2 * (fabsf(Is) + E * scale)) * (1.0f + 16 * kU2) + 1e-30f;
             const uint32_t kL = fkey(Is - E), kU = fkey(Is + E);
             lu[(off + i) * 64 + lane] = make_uint2(kL, kU);
-            atomicAdd(&hl[kL >> 20], 1u);
-            atomicAdd(&hl[kBins + (kU >> 20)], 1u);
+            atomicAdd(&hl[kL >> 22], 1u);
+            atomicAdd(&hl[kCoarse + (kU >> 22)], 1u);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();  // red[] is rewritten by the next chunk
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-#undef LSA_FETCH
     }
     __syncthreads();
     uint32_t* gh = hist + (int64_t)r * kHist;
-    for (int i = tid; i < 2 * kBins; i += 64 * kWaves)
-        if (hl[i]) hist_add(&gh[i], hl[i]);
-    if (!last_arrival(&arrive[2 * r], X, &s_flag)) return;
-    take_hist(gh, hl, 64 * kWaves);
-    if (nc * 64 > k) {
-        kth_bin<kWaves>(hl, k, wsum, &s_out[0]);
-        kth_bin<kWaves>(hl + kBins, k, wsum, &s_out[2]);
-        if (tid == 0) cinfo[r] = make_int4(s_out[0], s_out[1], s_out[2], s_out[3]);
-    }
-    if (tid == 0) __hip_atomic_store(&arrive[2 * r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = tid; i < 2 * kCoarse; i += 64 * kWaves)
+        if (hl[i]) atomicAdd(&gh[i], hl[i]);
 }
-
 
 // Chunks [c0, c1) of a request that block x of X takes in K2 and K3.
 __device__ __forceinline__ void block_chunks(int nc, int X, int x, int& c0, int& c1) {
@@ -346,16 +329,16 @@ __device__ __forceinline__ void block_chunks(int nc, int X, int x, int& c0, int&
 }
 
 // K2.  Grid (X, B).  Requests with no more than k candidates keep them all
-// here.  Otherwise each block adds the fine histograms of its chunks' keys
-// that fall in the coarse bins of cinfo, and the last block turns them into
-// tau and edge (tinfo: tau, edge low word, edge high word).
+// here.  Otherwise every block finds the coarse bins cL, cU holding the k-th
+// largest L and U (block 0 keeps them, with the counts above them, in
+// cinfo), then adds the fine histograms of its chunks' keys that fall in
+// those bins.
 __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
     GeomDev g, const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
-    const uint2* __restrict__ lu, const int4* __restrict__ cinfo, int k,
-    uint32_t* __restrict__ hist, uint32_t* __restrict__ arrive, int4* __restrict__ tinfo,
+    const uint2* __restrict__ lu, int k, uint32_t* __restrict__ hist, int4* __restrict__ cinfo,
     int32_t* __restrict__ topk, int32_t* __restrict__ tcnt) {
-    __shared__ uint32_t hf[2 * kBins];
-    __shared__ int wsum[kWaves], s_flag, s_out[4];
+    __shared__ uint32_t hf[2 * kFine];
+    __shared__ int wsum[kWaves], s_out[4];
     const int r = blockIdx.y, X = gridDim.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nc = cnt[r], n = nc * 64;
     const int64_t off = g.chunk_off[r];
@@ -365,9 +348,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
         if (blockIdx.x == 0 && tid == 0) tcnt[r] = n;
         return;
     }
-    const int4 ci = cinfo[r];
-    const uint32_t cL = (uint32_t)ci.x, cU = (uint32_t)ci.z;
-    for (int i = tid; i < 2 * kBins; i += blockDim.x) hf[i] = 0;
+    uint32_t* gh = hist + (int64_t)r * kHist;
+    load_hist(gh, hf, 2 * kCoarse);
+    kth_bin<kCoarse, kWaves>(hf, k, wsum, &s_out[0]);
+    kth_bin<kCoarse, kWaves>(hf + kCoarse, k, wsum, &s_out[2]);
+    const uint32_t cL = (uint32_t)s_out[0], cU = (uint32_t)s_out[2];
+    if (blockIdx.x == 0 && tid == 0) cinfo[r] = make_int4(s_out[0], s_out[1], s_out[2], s_out[3]);
+    for (int i = tid; i < 2 * kFine; i += blockDim.x) hf[i] = 0;
     __syncthreads();
     int c0, c1;
     block_chunks(nc, X, blockIdx.x, c0, c1);
@@ -382,24 +369,14 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
 #pragma unroll
         for (int u = 0; u < U4; ++u) {
             if (cb + kWaves * u >= c1) break;
-            if ((f[u].x >> 20) == cL) atomicAdd(&hf[(f[u].x >> 8) & (kBins - 1)], 1u);
-            if ((f[u].y >> 20) == cU) atomicAdd(&hf[kBins + ((f[u].y >> 8) & (kBins - 1))], 1u);
+            if ((f[u].x >> 22) == cL) atomicAdd(&hf[(f[u].x >> 10) & (kFine - 1)], 1u);
+            if ((f[u].y >> 22) == cU) atomicAdd(&hf[kFine + ((f[u].y >> 10) & (kFine - 1))], 1u);
         }
     }
     __syncthreads();
-    uint32_t* gh = hist + (int64_t)r * kHist + 2 * kBins;
-    for (int i = tid; i < 2 * kBins; i += blockDim.x)
-        if (hf[i]) hist_add(&gh[i], hf[i]);
-    if (!last_arrival(&arrive[2 * r + 1], X, &s_flag)) return;
-    take_hist(gh, hf, blockDim.x);
-    kth_bin<kWaves>(hf, k - ci.y, wsum, &s_out[0]);
-    kth_bin<kWaves>(hf + kBins, k - ci.w, wsum, &s_out[2]);
-    if (tid == 0) {
-        const uint32_t tau = (cL << 20) | ((uint32_t)s_out[0] << 8);
-        const uint64_t edge = ((uint64_t)cU << 20) + ((uint64_t)(s_out[2] + 1) << 8);
-        tinfo[r] = make_int4((int)tau, (int)(uint32_t)edge, (int)(uint32_t)(edge >> 32), 0);
-        __hip_atomic_store(&arrive[2 * r + 1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    uint32_t* gf = gh + 2 * kCoarse;
+    for (int i = tid; i < 2 * kFine; i += blockDim.x)
+        if (hf[i]) atomicAdd(&gf[i], hf[i]);
 }
 
 // K3.  Grid (X, B).  Block x lists, in token order, the band candidates of
@@ -413,7 +390,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
 template <int KDT, int D, int H>
 __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     GeomDev g, const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
-    const uint2* __restrict__ lu, const int4* __restrict__ tinfo, int k,
+    const uint2* __restrict__ lu, const uint32_t* __restrict__ hist,
+    const int4* __restrict__ cinfo, int k,
     const uint8_t* __restrict__ pages, int64_t page_bytes, int64_t ikey_off,
     const int32_t* __restrict__ page_table, const float* __restrict__ ikey_scale,
     const uint16_t* __restrict__ q, const float* __restrict__ w, int32_t* __restrict__ bl,
@@ -427,13 +405,20 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     __shared__ float rel[kWaves][TPW][H];
     __shared__ float wf[H];
     __shared__ int s_nb[kWaves], s_nu[kWaves];
+    __shared__ uint32_t hf[2 * kFine];
+    __shared__ int wsum[kWaves], s_out[4];
     const int r = blockIdx.y, X = gridDim.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nc = cnt[r];
     if (nc * 64 <= k) return;
     const int64_t off = g.chunk_off[r];
-    const int4 ti = tinfo[r];
-    const uint32_t tau = (uint32_t)ti.x;
-    const uint64_t edge = (uint64_t)(uint32_t)ti.y | ((uint64_t)(uint32_t)ti.z << 32);
+    // tau: lowest key of the fine bin holding the k-th largest L; edge: first
+    // key above the fine bin holding the k-th largest U
+    const int4 ci = cinfo[r];
+    load_hist(hist + (int64_t)r * kHist + 2 * kCoarse, hf, 2 * kFine);
+    kth_bin<kFine, kWaves>(hf, k - ci.y, wsum, &s_out[0]);
+    kth_bin<kFine, kWaves>(hf + kFine, k - ci.w, wsum, &s_out[2]);
+    const uint32_t tau = ((uint32_t)ci.x << 22) | ((uint32_t)s_out[0] << 10);
+    const uint64_t edge = ((uint64_t)(uint32_t)ci.z << 22) + ((uint64_t)(s_out[2] + 1) << 10);
     int c0, c1;
     block_chunks(nc, X, blockIdx.x, c0, c1);
     const int64_t seg = (off + c0) * 64;
@@ -555,7 +540,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     }
 }
 
-// K4.  Exact top-k over the band of one request (one block).  The block
+// K4.  Exact top-k over the band of one request (one block); also clears
+// the request's histograms.  The block
 // lists of K3 are gathered in order into LDS (up to kListCap entries), the
 // k-th largest key is found by 12/12/8-bit radix select, then the emit keeps
 // keys above it and the lowest-index ties.  Larger bands (only with massive
@@ -566,7 +552,8 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
                                                   const int32_t* __restrict__ bl,
                                                   const uint32_t* __restrict__ bk, int k,
                                                   int32_t* __restrict__ topk,
-                                                  int32_t* __restrict__ tcnt) {
+                                                  int32_t* __restrict__ tcnt,
+                                                  uint32_t* __restrict__ bhist) {
     __shared__ uint32_t hist[4096];
     __shared__ uint32_t lkey[kListCap];
     __shared__ int32_t lpos[kListCap];
@@ -576,6 +563,9 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
     __shared__ int s_remaining, s_eq;
     const int r = blockIdx.x, tid = threadIdx.x;
     const int nc = cnt[r];
+    // the request's histograms were last read by the previous kernel: clear
+    // them for the next launch
+    for (int i = tid; i < kHist; i += kT) bhist[(int64_t)r * kHist + i] = 0;
     if (nc * 64 <= k) return;  // k_band_fine already wrote the result
     const int64_t off = g.chunk_off[r];
     const int C = (nc + X - 1) / X;  // chunks per K3 block
@@ -737,14 +727,13 @@ static int k23_blocks(const GeomDev& g) {
     return x < 1 ? 1 : x;
 }
 
-// Workspace: the histograms and arrival counters first (zero on entry
-// unless the caller knows they are; every launch leaves them zero), then the
-// rest.
-static size_t clean_words(const GeomDev& g) { return (size_t)g.B * (kHist + 2); }
+// Workspace: the histograms first (zero on entry unless the caller knows
+// they are; every launch leaves them zero), then the rest.
+static size_t clean_words(const GeomDev& g) { return (size_t)g.B * kHist; }
 
 size_t band_ws_bytes(const GeomDev& g) {
     const size_t nc = (size_t)g.chunk_off[g.B] * 64 + 64;
-    return align_up(clean_words(g) * 4, 256) + 2 * align_up((size_t)g.B * sizeof(int4), 256) +
+    return align_up(clean_words(g) * 4, 256) + align_up((size_t)g.B * sizeof(int4), 256) +
            align_up(nc * sizeof(uint2), 256) + 3 * align_up(nc * 4, 256) +
            align_up((size_t)g.B * k23_blocks(g) * 4, 256);
 }
@@ -767,11 +756,8 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
     if (!ws_clean && (e = launch_band_clear(g, ws, s)) != hipSuccess) return e;
     uint8_t* b = (uint8_t*)ws;
     uint32_t* hist = (uint32_t*)b;
-    uint32_t* arrive = hist + (size_t)g.B * kHist;
     b += align_up(clean_words(g) * 4, 256);
     int4* cinfo = (int4*)b;
-    b += align_up((size_t)g.B * sizeof(int4), 256);
-    int4* tinfo = (int4*)b;
     b += align_up((size_t)g.B * sizeof(int4), 256);
     uint2* lu = (uint2*)b;
     b += align_up(nc * sizeof(uint2), 256);
@@ -790,8 +776,8 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
 #define LSA_K1(KDT, D, HH)                                                                        \
     if (idx_dt == KDT && d == D && Hh == HH) {                                                    \
         hipLaunchKernelGGL((k_refine_mfma<KDT, D, HH>), dim3(X1, g.B), dim3(64 * kWaves), 0, s, g, \
-                           sel, cnt, pg, page_bytes, ikey_off, page_table, ikey_scale, qq, w, k,   \
-                           lu, hist, arrive, cinfo);                                              \
+                           sel, cnt, pg, page_bytes, ikey_off, page_table, ikey_scale, qq, w,      \
+                           lu, hist);                                                             \
         e = hipGetLastError();                                                                    \
     }
     LSA_K1(LSA_BF16, 128, 16) LSA_K1(LSA_BF16, 128, 32) LSA_K1(LSA_BF16, 128, 64)
@@ -804,8 +790,8 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
     timing_end("k_refine_mfma", s);
     if (e != hipSuccess) return e;
     timing_begin("k_band_fine", s);
-    hipLaunchKernelGGL(k_band_fine, dim3(X2, g.B), dim3(64 * kWaves), 0, s, g, sel, cnt, lu, cinfo,
-                       k, hist, arrive, tinfo, topk, tcnt);
+    hipLaunchKernelGGL(k_band_fine, dim3(X2, g.B), dim3(64 * kWaves), 0, s, g, sel, cnt, lu, k,
+                       hist, cinfo, topk, tcnt);
     timing_end("k_band_fine", s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = hipErrorInvalidValue;
@@ -813,7 +799,7 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
 #define LSA_K3(KDT, D, HH)                                                                        \
     if (idx_dt == KDT && d == D && Hh == HH) {                                                    \
         hipLaunchKernelGGL((k_band_list<KDT, D, HH>), dim3(X2, g.B), dim3(64 * kWaves), 0, s, g,   \
-                           sel, cnt, lu, tinfo, k, pg, page_bytes, ikey_off, page_table,          \
+                           sel, cnt, lu, hist, cinfo, k, pg, page_bytes, ikey_off, page_table,   \
                            ikey_scale, qq, w, bl, bk, ul, scnt);                                  \
         e = hipGetLastError();                                                                    \
     }
@@ -828,7 +814,7 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
     if (e != hipSuccess) return e;
     timing_begin("k_topk_band", s);
     hipLaunchKernelGGL(k_topk_band, dim3(g.B), dim3(kT), 0, s, g, sel, cnt, scnt, X2, bl, bk, k,
-                       topk, tcnt);
+                       topk, tcnt, hist);
     timing_end("k_topk_band", s);
     return hipGetLastError();
 }
