@@ -99,21 +99,187 @@ def traffic_for(kernel, workload, launches_per_window):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(inp, cfg, sel_o_cnt, threads):
-    """The oracle on one decode step of every request plus the trigger."""
-    import numpy as np
+def cpu_baseline(inp, cfg, threads, requests=None):
+    """The oracle on one trigger (score + select) and one decode step (refine,
+    top-k, attention) of the given requests (default: all)."""
     from oracle import oracle
+    reqs = list(range(cfg.batch)) if requests is None else list(requests)
     o = oracle.Oracle(inp)
     t0 = time.perf_counter()
     _, sel, cnt = o.score_select()
-    units = [(r, 0) for r in range(cfg.batch)]
+    units = [(r, 0) for r in reqs]
     o.decode_units(units, sel, cnt, cfg.topk, cfg.sm_scale, threads=threads)
     dt = time.perf_counter() - t0
-    return {"value": round(1.0 / dt, 4), "unit": "decode steps/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"one trigger (score+select, {cfg.batch} requests) and one decode step "
-                      f"(refine+top-k+attention) of all {cfg.batch} requests of {cfg.name}; "
-                      f"{dt:.1f} s wall on {threads} threads"}
+    frac = len(reqs) / cfg.batch  # share of one decode step of the whole batch
+    return {"value": round(frac / dt, 4), "unit": "decode steps/s", "cores": threads,
+            "kind": "oracle", "cpu": _cpu_model(),
+            "sample": f"one trigger (score+select, all {cfg.batch} requests) and one decode step "
+                      f"(refine+top-k+attention) of {len(reqs)} of the {cfg.batch} requests of "
+                      f"{cfg.name}, scaled to whole-batch steps; {dt:.1f} s wall on {threads} "
+                      f"thread(s)"}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def hbm_calibration(nbytes=1 << 30, reps=5):
+    """Plain device copy (read + write) and plain reduction (read) of a large
+    buffer with torch, for the achievable-bandwidth line beside the kernels."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_s = e0.elapsed_time(e1) / 1e3 / reps
+    s = x.sum()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        s = x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    read_s = e0.elapsed_time(e1) / 1e3 / reps
+    del x, y
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "copy_gbs": round(2 * nbytes / copy_s / 1e9, 1),
+            "read_gbs": round(nbytes / read_s / 1e9, 1)}
+
+
+def sustained_scoring(label, B, L, idx_dt, H=64, d=128, window=8192, seed=0, reps=3):
+    """lsa_score_chunks + lsa_select_threshold over many distinct KIComp buffers
+    (together more than twice the 256 MB last-level cache), so every launch
+    streams cold lines: B requests of L tokens each, one launch per trigger."""
+    import math
+    import numpy as np
+    import torch
+    from learned_sparse_kv_amd import lsa, synth
+    g = lsa.Geom(np.full(B, L, np.int32), window)
+    nhist = (max(L - window, 0) // 64)
+    nh = B * nhist
+    row = d * (1 if idx_dt == synth.FP8 else 2)
+    per = nh * (row + (4 if idx_dt == synth.FP8 else 0))  # algorithmic bytes per trigger
+    nbuf = max(6, math.ceil(600e6 / per))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    kic, ksc = [], []
+    for _ in range(nbuf):
+        x = torch.randn(nh, d, generator=gen, device="cuda") * (d ** -0.5)
+        if idx_dt == synth.FP8:
+            kic.append((x * 448.0 / 4.0).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8))
+            ksc.append(torch.full((nh,), 4.0 / 448.0, device="cuda"))
+        else:
+            kic.append(x.to(torch.bfloat16).view(torch.int16))
+            ksc.append(None)
+        del x
+    q = (torch.randn(B, H, d, generator=gen, device="cuda") * (H / 4) ** 0.5).to(torch.bfloat16).view(torch.int16)
+    w = torch.full((B, H), 1.0 / H, device="cuda")
+    bias = torch.full((B,), -1.0, device="cuda")
+    z = torch.empty(nh, device="cuda")
+    sel = torch.empty(nh, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(lsa.lsa_score_ws_bytes(g, d), 256), dtype=torch.uint8, device="cuda")
+
+    def trig(b):
+        lsa.lsa_score_chunks(g, q, synth.BF16, w, bias, H, d, kic[b], idx_dt, ksc[b], z, ws)
+        lsa.lsa_select_threshold(g, z, 0.0, sel, cnt)
+
+    for b in range(nbuf):
+        trig(b)
+    torch.cuda.synchronize()
+    lsa.lsa_timing_reset()
+    lsa.lsa_timing_enable(True)
+    for _ in range(reps):
+        for b in range(nbuf):
+            trig(b)
+    torch.cuda.synchronize()
+    lsa.lsa_timing_enable(False)
+    t = {n: lsa.lsa_timing_read(n) for n in ("k_fuse_query", "k_score", "k_select")}
+    lsa.lsa_timing_reset()
+    us = {n: (ms * 1e3 / c if c else None) for n, (c, ms) in t.items()}
+    gbs = per / (us["k_score"] * 1e-6) / 1e9
+    del kic, ksc
+    torch.cuda.empty_cache()
+    return {"label": label, "batch": B, "context": L,
+            "index_keys": "fp8_e4m3fn" if idx_dt == synth.FP8 else "bf16",
+            "bytes_per_trigger": per, "distinct_buffers": nbuf, "launches": reps * nbuf,
+            "k_score_us": round(us["k_score"], 2), "gbs": round(gbs, 1),
+            "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+            "trigger_us": round(sum(v for v in us.values() if v), 2)}
+
+
+def sustained_attention(label, B, L, nbatch=6, reps=3, k=2048, Hq=64, Dk=576, Dv=512,
+                        window=8192, seed=0):
+    """lsa_sparse_decode_attn rotating over nbatch independent batches (pages,
+    recent rows, top-k lists, queries), so each launch reads lines no recent
+    launch brought into the caches."""
+    import numpy as np
+    import torch
+    from learned_sparse_kv_amd import lsa, synth
+    g = lsa.Geom(np.full(B, L, np.int32), window)
+    nhist = max(L - window, 0) // 64
+    rs = nhist * 64
+    nrec = L - rs
+    row_bytes, ikey_off = Dk * 2, 64 * Dk * 2
+    page_bytes = ikey_off + 64 * 128
+    kv = lsa.kv_layout(synth.BF16, Dk, Dv, 0, row_bytes, page_bytes, ikey_off)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    batches = []
+    for _ in range(nbatch):
+        pages = torch.randn(B * nhist * page_bytes // 2, generator=gen, device="cuda").to(
+            torch.bfloat16).view(torch.uint8)
+        recent = torch.randn(B * nrec * Dk, generator=gen, device="cuda").to(torch.bfloat16).view(torch.uint8)
+        tk = torch.stack([torch.randperm(rs, generator=gen, device="cuda")[:k].sort().values
+                          for _ in range(B)]).to(torch.int32).contiguous()
+        q = torch.randn(B, Hq, Dk, generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+        batches.append((pages, recent, tk, q))
+    tcnt = torch.full((B,), k, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, Hq, Dv, dtype=torch.int16, device="cuda")
+    lse = torch.empty(B, Hq, device="cuda")
+    ws = torch.empty(lsa.lsa_attn_ws_bytes(g, kv, Hq, k, 0), dtype=torch.uint8, device="cuda")
+
+    def run(b):
+        pages, recent, tk, q = batches[b]
+        lsa.lsa_sparse_decode_attn(g, q, Hq, kv, pages, None, recent, tk, tcnt, k, Dk ** -0.5,
+                                   out, lse, 0, ws)
+
+    for b in range(nbatch):
+        run(b)
+    torch.cuda.synchronize()
+    lsa.lsa_timing_reset()
+    lsa.lsa_timing_enable(True)
+    for _ in range(reps):
+        for b in range(nbatch):
+            run(b)
+    torch.cuda.synchronize()
+    lsa.lsa_timing_enable(False)
+    c1, ms1 = lsa.lsa_timing_read("k_attn_mla")
+    c2, ms2 = lsa.lsa_timing_read("k_attn_merge")
+    lsa.lsa_timing_reset()
+    toks = B * (k + nrec)
+    per = toks * row_bytes + B * Hq * Dk * 2  # rows read + queries
+    us = ms1 * 1e3 / c1
+    gbs = per / (us * 1e-6) / 1e9
+    del batches
+    torch.cuda.empty_cache()
+    return {"label": label, "batch": B, "context": L, "attended_tokens_per_request": k + nrec,
+            "bytes_per_launch": per, "rotating_batches": nbatch, "launches": c1,
+            "k_attn_us": round(us, 2), "gbs": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+            "merge_us": round(ms2 * 1e3 / c2, 2) if c2 else None}
 
 
 def main():
@@ -123,6 +289,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2, help="untimed windows before timing")
     ap.add_argument("--workload", default="cfg4", choices=["cfg1", "cfg2", "cfg3", "cfg4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sustained", action="store_true",
+                    help="skip the cold-cache scoring / attention GB/s points at 128K and 500K")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -172,6 +340,35 @@ def main():
         st, cur = run_window(m, cur)
         m += 1
     torch.cuda.synchronize()
+
+    # ---- instrumented window (untimed): every kernel bracketed by HIP events
+    lsa.lsa_timing_reset()
+    lsa.lsa_timing_enable(True)
+    win_cnt = cur.copy()
+    st, cur = run_window(m, cur)
+    m += 1
+    torch.cuda.synchronize()
+    lsa.lsa_timing_enable(False)
+    tsum = int(tcnt.sum().item()) / S  # top-k tokens attended per step (all requests)
+    kern = {}
+    for name in lsa.KERNELS:
+        n, ms = lsa.lsa_timing_read(name)
+        if n:
+            kern[name] = {"launches": n, "avg_us": round(ms * 1e3 / n, 2), "total_ms": round(ms, 3)}
+    lsa.lsa_timing_reset()
+    dom = max(kern, key=lambda k_: kern[k_]["total_ms"])
+    for name, e in kern.items():
+        b, f = kernel_work(name, cfg, inp, win_cnt, cfg.topk, tsum, B)
+        sec = e["avg_us"] * 1e-6
+        e["alg_bytes"] = int(b)
+        e["gbs"] = round(b / sec / 1e9, 1) if b else None
+        e["tflops"] = round(f / sec / 1e12, 2) if f else None
+    log("[bench] kernels (instrumented window): " + json.dumps(kern))
+
+    # ---- timed region: wall clock for the value; the dominant kernel alone is
+    # bracketed by HIP events on its own stream
+    lsa.lsa_timing_only(dom)
+    lsa.lsa_timing_enable(True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
@@ -184,49 +381,32 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    lsa.lsa_timing_enable(False)
+    dn, dms = lsa.lsa_timing_read(dom)
+    lsa.lsa_timing_only(None)
+    lsa.lsa_timing_reset()
     gpu_ms = ev0.elapsed_time(ev1)
     value = S * args.steps / wall
     log(f"[bench] {args.steps} windows in {wall * 1e3:.1f} ms wall ({gpu_ms:.1f} ms main-stream "
         f"events): {value:.1f} decode steps/s")
 
-    # ---- instrumented window: per-kernel HIP-event durations ----
-    lsa.lsa_timing_reset()
-    lsa.lsa_timing_enable(True)
-    win_cnt = cur.copy()
-    st, cur = run_window(m, cur)
-    m += 1
-    torch.cuda.synchronize()
-    lsa.lsa_timing_enable(False)
-    tsum = int(tcnt.sum().item())  # top-k tokens attended over the window's steps
-    kern = {}
-    for name in lsa.KERNELS:
-        n, ms = lsa.lsa_timing_read(name)
-        if n:
-            kern[name] = {"launches": n, "avg_us": round(ms * 1e3 / n, 2), "total_ms": round(ms, 3)}
-    lsa.lsa_timing_reset()
-    dom = max(kern, key=lambda k_: kern[k_]["total_ms"])
-    per_step_topk = tsum / S
-    for name, e in kern.items():
-        b, f = kernel_work(name, cfg, inp, win_cnt, cfg.topk, per_step_topk, B)
-        sec = e["avg_us"] * 1e-6
-        e["alg_bytes"] = int(b)
-        e["gbs"] = round(b / sec / 1e9, 1) if b else None
-        e["tflops"] = round(f / sec / 1e12, 2) if f else None
-    log("[bench] kernels: " + json.dumps(kern))
-
-    d = kern[dom]
+    dom_us = dms * 1e3 / dn
+    works = [kernel_work(dom, cfg, inp, c, cfg.topk, tsum, B) for c in sel_hist]
+    b = sum(x[0] for x in works) / len(works)
+    f = sum(x[1] for x in works) / len(works)
     if dom == "k_refine":
-        b, f = kernel_work(dom, cfg, inp, win_cnt, cfg.topk, per_step_topk, B)
-        ach = f / (d["avg_us"] * 1e-6) / 1e12
+        ach = f / (dom_us * 1e-6) / 1e12
         roof = {"kernel": dom, "bound": "alu", "achieved": round(ach, 2),
                 "peak": round(VALU_F32_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
                 "frac": round(ach / VALU_F32_PEAK_TFLOPS, 4)}
     else:
-        b, f = kernel_work(dom, cfg, inp, win_cnt, cfg.topk, per_step_topk, B)
-        ach = b / (d["avg_us"] * 1e-6) / 1e9
+        ach = b / (dom_us * 1e-6) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = traffic_for(dom, cfg.name, d["launches"])
+    roof["avg_us"] = round(dom_us, 2)
+    roof["launches_timed"] = dn
+    roof["alg_bytes_per_launch"] = int(b)
+    roof["traffic"] = traffic_for(dom, cfg.name, dn)
 
     def hbm(name):
         e = kern.get(name)
@@ -270,10 +450,27 @@ def main():
         for _ in range(3):
             bb.copy_(a)
         torch.cuda.synchronize()
+        del a, bb
+    pipe.close()
+    del pipe, dev
+    torch.cuda.empty_cache()
+    if not args.no_sustained:
+        t0 = time.perf_counter()
+        result["hbm_calibration"] = hbm_calibration()
+        result["scoring_sustained"] = [
+            sustained_scoring("500k", 64, 512000, synth.FP8, seed=101),
+            sustained_scoring("128k", 64, 131072, synth.BF16, seed=102)]
+        result["attention_sustained"] = [
+            sustained_attention("500k", 4, 512000, seed=103),
+            sustained_attention("500k_b8", 8, 512000, seed=104),
+            sustained_attention("128k", 16, 131072, seed=105)]
+        log(f"[bench] sustained points in {time.perf_counter() - t0:.1f}s: "
+            + json.dumps({"scoring": result["scoring_sustained"],
+                          "attention": result["attention_sustained"]}))
     if not args.no_cpu_baseline:
         threads = min(16, len(os.sched_getaffinity(0)))
-        result["cpu_baseline"] = cpu_baseline(inp, cfg, win_cnt, threads)
-    pipe.close()
+        result["cpu_baseline"] = cpu_baseline(inp, cfg, threads)
+        result["cpu_baseline_1core"] = cpu_baseline(inp, cfg, 1, requests=[0])
     print(json.dumps(result), flush=True)
 
 

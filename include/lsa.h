@@ -289,12 +289,16 @@ lsa_status lsa_step64(lsa_ctx* ctx, const lsa_window_in* in, lsa_window_out* out
  * launches is bracketed by two hipEvents recorded on the stream it is
  * launched on (adds a little launch overhead).  lsa_timing_read waits for
  * the recorded events and returns, for one kernel name (k_fuse_query,
- * k_score, k_select, k_refine, k_topk, k_attn_mla, k_attn_f32,
- * k_attn_merge, k_gather), the number of timed launches and their summed
- * duration in milliseconds since the last reset.  Process-wide; the hooks
- * are thread-safe.
+ * k_score, k_select, k_refine, k_topk, k_refine_mfma, k_band_fine,
+ * k_band_list, k_topk_band, k_attn_mla, k_attn_f32, k_attn_merge,
+ * k_gather), the number of timed launches and their summed duration in
+ * milliseconds since the last reset.  lsa_timing_only(name) restricts the
+ * timing to that one kernel (NULL: all; a name of 64 or more characters is
+ * LSA_ERR_INVALID_ARG), so that one kernel can be timed inside a run with
+ * little disturbance.  Process-wide; the hooks are thread-safe.
  * ---------------------------------------------------------------------- */
 lsa_status lsa_timing_enable(int32_t on);
+lsa_status lsa_timing_only(const char* kernel);
 void lsa_timing_reset(void);
 lsa_status lsa_timing_read(const char* kernel, int64_t* launches, double* total_ms);
 

@@ -13,7 +13,7 @@
 // unnormalised output (online softmax, base 2) and writes them to a
 // workspace; k_attn_merge combines the splits of each (request, head).
 //
-// k_attn_mla2 (bf16, Dk 576 / Dv 512): one block per (request, split, group
+// k_attn_mla (bf16, Dk 576 / Dv 512): one block per (request, split, group
 // of 32 heads), 4 waves, 32-token tiles, MFMA 16x16x32 bf16; every KV byte
 // is read from HBM once per head group and feeds both products.
 // Algorithmic bytes per attended token: 1,152 (HBM-bound).
@@ -98,7 +98,7 @@ __device__ __forceinline__ uint2 lds_tr16(const uint8_t* base_lds, int byte_off)
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;
 
-__global__ __launch_bounds__(256, 2) void k_attn_mla2(GeomDev g, PosMap pm,
+__global__ __launch_bounds__(256, 2) void k_attn_mla(GeomDev g, PosMap pm,
                                                      const int32_t* __restrict__ tcnt,
                                                      const uint16_t* __restrict__ q, int Hq,
                                                      int n_splits, int per_split, int hgroups,
@@ -548,7 +548,7 @@ hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, in
         const int units = g.B * plan.n_splits;
         const int grid = (units + 7) / 8 * 8 * plan.head_groups;
         timing_begin("k_attn_mla", s);
-        hipLaunchKernelGGL(k_attn_mla2, dim3(grid), dim3(256), 0, s, g, pm, tcnt,
+        hipLaunchKernelGGL(k_attn_mla, dim3(grid), dim3(256), 0, s, g, pm, tcnt,
                            (const uint16_t*)q, Hq, plan.n_splits, plan.per_split,
                            plan.head_groups, sm_log2e, part_o, part_ml);
         timing_end("k_attn_mla", s);

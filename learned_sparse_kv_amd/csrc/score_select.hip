@@ -13,9 +13,11 @@
 // denormal flush, no other contraction.  One lane owns one chunk so each
 // dot product is a plain sequential chain.
 //
-// k_score streams KIComp from HBM: one wave per tile of 64 chunks, rows
-// loaded with coalesced 16-byte loads into a wave-private LDS tile, then
-// read back one row per lane.  1 (bf16) to 2 (fp8) flop per byte: HBM-bound.
+// k_score streams KIComp from HBM: each wave takes about two tiles of 64
+// chunks of one request; rows come in with coalesced 16-byte loads (the next
+// tile in flight while the current one is scored), go through a wave-private
+// LDS tile, and are read back one row per lane.  1 (bf16) to 2 (fp8) flop
+// per byte: HBM-bound.
 #include "lsa_internal.h"
 
 namespace {
@@ -42,46 +44,50 @@ __global__ void k_fuse_query(GeomDev g, const void* __restrict__ q, const float*
     qbar[(size_t)r * d + i] = acc;
 }
 
-// Dot product of a row held as 16-byte pieces (ROWB bytes) with qbar, as a
-// sequential fma chain in element order.
+// Dot product of a row held as 16-byte pieces (ROWB bytes) with qbar (in
+// LDS, read as float4 broadcasts), as a sequential fma chain in element order.
 template <int KDT, int D>
 __device__ __forceinline__ float row_dot(const uint4* __restrict__ row,
-                                         const float* __restrict__ qb) {
+                                         const float4* __restrict__ qb) {
     float acc = 0.0f;
     if constexpr (KDT == LSA_F32) {
-#pragma unroll
+#pragma unroll 4
         for (int j = 0; j < D / 4; ++j) {
             const uint4 v = row[j];
-            acc = __builtin_fmaf(qb[4 * j + 0], __uint_as_float(v.x), acc);
-            acc = __builtin_fmaf(qb[4 * j + 1], __uint_as_float(v.y), acc);
-            acc = __builtin_fmaf(qb[4 * j + 2], __uint_as_float(v.z), acc);
-            acc = __builtin_fmaf(qb[4 * j + 3], __uint_as_float(v.w), acc);
+            const float4 q = qb[j];
+            acc = __builtin_fmaf(q.x, __uint_as_float(v.x), acc);
+            acc = __builtin_fmaf(q.y, __uint_as_float(v.y), acc);
+            acc = __builtin_fmaf(q.z, __uint_as_float(v.z), acc);
+            acc = __builtin_fmaf(q.w, __uint_as_float(v.w), acc);
         }
     } else if constexpr (KDT == LSA_BF16) {
-#pragma unroll
+#pragma unroll 2
         for (int j = 0; j < D / 8; ++j) {
             const uint4 v = row[j];
-            const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc = __builtin_fmaf(qb[8 * j + 2 * e], __uint_as_float(wds[e] << 16), acc);
-                acc = __builtin_fmaf(qb[8 * j + 2 * e + 1], __uint_as_float(wds[e] & 0xffff0000u),
-                                     acc);
-            }
+            const float4 qa = qb[2 * j], qc = qb[2 * j + 1];
+            acc = __builtin_fmaf(qa.x, __uint_as_float(v.x << 16), acc);
+            acc = __builtin_fmaf(qa.y, __uint_as_float(v.x & 0xffff0000u), acc);
+            acc = __builtin_fmaf(qa.z, __uint_as_float(v.y << 16), acc);
+            acc = __builtin_fmaf(qa.w, __uint_as_float(v.y & 0xffff0000u), acc);
+            acc = __builtin_fmaf(qc.x, __uint_as_float(v.z << 16), acc);
+            acc = __builtin_fmaf(qc.y, __uint_as_float(v.z & 0xffff0000u), acc);
+            acc = __builtin_fmaf(qc.z, __uint_as_float(v.w << 16), acc);
+            acc = __builtin_fmaf(qc.w, __uint_as_float(v.w & 0xffff0000u), acc);
         }
     } else {  // fp8 e4m3fn (OCP), converted exactly to fp32 by the hardware
-#pragma unroll
+#pragma unroll 2
         for (int j = 0; j < D / 16; ++j) {
             const uint4 v = row[j];
             const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+                const float4 q = qb[4 * j + e];
                 const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wds[e], false);
                 const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wds[e], true);
-                acc = __builtin_fmaf(qb[16 * j + 4 * e + 0], lo[0], acc);
-                acc = __builtin_fmaf(qb[16 * j + 4 * e + 1], lo[1], acc);
-                acc = __builtin_fmaf(qb[16 * j + 4 * e + 2], hi[0], acc);
-                acc = __builtin_fmaf(qb[16 * j + 4 * e + 3], hi[1], acc);
+                acc = __builtin_fmaf(q.x, lo[0], acc);
+                acc = __builtin_fmaf(q.y, lo[1], acc);
+                acc = __builtin_fmaf(q.z, hi[0], acc);
+                acc = __builtin_fmaf(q.w, hi[1], acc);
             }
         }
     }
@@ -95,6 +101,9 @@ constexpr int score_waves() {
     return rowb <= 128 ? 4 : (rowb <= 256 ? 2 : 1);
 }
 
+// Grid (X, B): the waves of block column x of request r take the request's
+// tiles x*nw + wave, stepping by X*nw, and load the next tile into registers
+// while the current one is scored from LDS.
 template <int KDT, int D>
 __global__ __launch_bounds__((64 * score_waves<KDT, D>())) void k_score(
     GeomDev g, const uint8_t* __restrict__ kic, const float* __restrict__ kscale,
@@ -102,46 +111,66 @@ __global__ __launch_bounds__((64 * score_waves<KDT, D>())) void k_score(
     constexpr int kScoreWaves = score_waves<KDT, D>();
     constexpr int EB = KDT == LSA_F32 ? 4 : (KDT == LSA_BF16 ? 2 : 1);
     constexpr int ROWB = D * EB;          // bytes per KIComp row
-    constexpr int PIECES = ROWB / 16;     // 16-byte pieces per row
+    constexpr int PIECES = ROWB / 16;     // 16-byte pieces per row = per lane per tile
     constexpr int STRIDE = ROWB + 16;     // padded LDS row (conflict-free reads)
     __shared__ __attribute__((aligned(16))) uint8_t tile[kScoreWaves][64 * STRIDE];
+    __shared__ __attribute__((aligned(16))) float qs[D];
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
-    const int gt = blockIdx.x * kScoreWaves + wv;  // global tile of 64 chunks
-    if (gt >= g.tile_off[g.B]) return;             // whole wave leaves together
-    int r = 0;
-    while (gt >= g.tile_off[r + 1]) ++r;
-    r = __builtin_amdgcn_readfirstlane(r);
-    const int c0 = (gt - g.tile_off[r]) * 64;
-    const int nvalid = min(64, g.nhist[r] - c0);
-    const int64_t row0 = g.chunk_off[r] + c0;
-
-    // coalesced load of the tile (nvalid rows, contiguous) into LDS
-    const uint4* src = (const uint4*)(kic + row0 * ROWB);
-    uint8_t* t = tile[wv];
+    const int r = blockIdx.y;
+    const int nh = g.nhist[r];
+    const int ntile = (nh + 63) >> 6;
+    const int step = gridDim.x * kScoreWaves;
+    if ((int)blockIdx.x * kScoreWaves >= ntile) return;  // uniform across the block
+    for (int i = threadIdx.x; i < D; i += blockDim.x) qs[i] = qbar[(size_t)r * D + i];
+    __syncthreads();
+    int t = blockIdx.x * kScoreWaves + wv;
+    if (t >= ntile) return;  // whole wave leaves together
+    const int64_t off = g.chunk_off[r];
+    const float br = bias[r];
+    uint8_t* lt = tile[wv];
+    uint4 raw[PIECES];
+    float sc = 1.0f;
+    // tile tt: rows off + 64tt .. (nvalid of them), contiguous; lane takes the
+    // 16-byte pieces j*64 + lane, and the scale of row 64tt + lane
+    auto fetch = [&](int tt) {
+        const int nvalid = min(64, nh - tt * 64);
+        const uint4* src = (const uint4*)(kic + (off + (int64_t)tt * 64) * ROWB);
 #pragma unroll
-    for (int j = 0; j < PIECES; ++j) {
-        const int piece = j * 64 + lane;          // 16-byte piece index in the tile
-        const int rr = piece / PIECES, cc = piece % PIECES;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (rr < nvalid) v = src[piece];
-        *(uint4*)(t + rr * STRIDE + cc * 16) = v;
+        for (int j = 0; j < PIECES; ++j) {
+            const int piece = j * 64 + lane;
+            raw[j] = (piece / PIECES < nvalid) ? src[piece] : make_uint4(0, 0, 0, 0);
+        }
+        if constexpr (KDT == LSA_FP8_E4M3FN)
+            sc = lane < nvalid ? kscale[off + (int64_t)tt * 64 + lane] : 1.0f;
+    };
+    fetch(t);
+    for (; t < ntile; t += step) {
+#pragma unroll
+        for (int j = 0; j < PIECES; ++j) {
+            const int piece = j * 64 + lane;
+            *(uint4*)(lt + (piece / PIECES) * STRIDE + (piece % PIECES) * 16) = raw[j];
+        }
+        const float s = sc;
+        if (t + step < ntile) fetch(t + step);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int c = t * 64 + lane;
+        const float acc = row_dot<KDT, D>((const uint4*)(lt + lane * STRIDE), (const float4*)qs);
+        if (c < nh) z[off + c] = __builtin_fmaf(s, acc, br);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();  // the LDS tile is rewritten next round
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    if (lane >= nvalid) return;
-    const float* qb = qbar + (size_t)r * D;
-    const float acc = row_dot<KDT, D>((const uint4*)(t + lane * STRIDE), qb);
-    const int64_t c = row0 + lane;
-    const float s = (KDT == LSA_FP8_E4M3FN) ? kscale[c] : 1.0f;
-    z[c] = __builtin_fmaf(s, acc, bias[r]);
 }
 
 // Ordered stream compaction of {c : z_c > theta} per request: wave ballot,
-// in-wave rank by popcount, wave totals through LDS.  One block per request.
+// in-wave rank by popcount, wave totals through LDS.  One block per request;
+// the first kSelPre rounds of logits are loaded before any is compacted.
+constexpr int kSelPre = 16;
+
 __global__ __launch_bounds__(1024) void k_select(GeomDev g, const float* __restrict__ z,
                                                  float theta, int32_t* __restrict__ sel,
                                                  int32_t* __restrict__ cnt) {
@@ -151,23 +180,35 @@ __global__ __launch_bounds__(1024) void k_select(GeomDev g, const float* __restr
     const int64_t off = g.chunk_off[r];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     int base = 0;
-    for (int c0 = 0; c0 < n; c0 += 1024) {
-        const int c = c0 + (int)threadIdx.x;
-        const bool f = (c < n) && (z[off + c] > theta);
-        const uint64_t m = __ballot(f);
-        const int pre = __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == 0) wsum[wv] = __popcll(m);
-        __syncthreads();
-        int wpre = 0, tot = 0;
+    for (int c00 = 0; c00 < n; c00 += 1024 * kSelPre) {
+        bool fl[kSelPre];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int v = wsum[i];
-            wpre += (i < wv) ? v : 0;
-            tot += v;
+        for (int u = 0; u < kSelPre; ++u) {
+            const int c = c00 + u * 1024 + (int)threadIdx.x;
+            fl[u] = (c < n) && (z[off + c] > theta);
         }
-        if (f) sel[off + base + wpre + pre] = c;
-        base += tot;
-        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kSelPre; ++u) {
+            const int c0 = c00 + u * 1024;
+            if (c0 < n) {  // uniform
+                const int c = c0 + (int)threadIdx.x;
+                const bool f = fl[u];
+                const uint64_t m = __ballot(f);
+                const int pre = __popcll(m & ((1ull << lane) - 1ull));
+                if (lane == 0) wsum[wv] = __popcll(m);
+                __syncthreads();
+                int wpre = 0, tot = 0;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int v = wsum[i];
+                    wpre += (i < wv) ? v : 0;
+                    tot += v;
+                }
+                if (f) sel[off + base + wpre + pre] = c;
+                base += tot;
+                __syncthreads();
+            }
+        }
     }
     if (threadIdx.x == 0) cnt[r] = base;
 }
@@ -189,12 +230,15 @@ hipError_t launch_score(const GeomDev& g, const void* kic, lsa_dtype kdt, const 
                         const float* qbar, const float* bias, int d, float* z, hipStream_t s) {
     const int tiles = g.tile_off[g.B];
     if (tiles == 0) return hipSuccess;
+    int mt = 0;  // tiles of the longest request
+    for (int r = 0; r < g.B; ++r) mt = g.tile_off[r + 1] - g.tile_off[r] > mt ? g.tile_off[r + 1] - g.tile_off[r] : mt;
     const uint8_t* k = (const uint8_t*)kic;
 #define LSA_SCORE_CASE(KDT, D)                                                                  \
     if (kdt == KDT && d == D) {                                                                 \
         constexpr int nw = score_waves<KDT, D>();                                               \
         timing_begin("k_score", s);                                                             \
-        hipLaunchKernelGGL((k_score<KDT, D>), dim3((tiles + nw - 1) / nw), dim3(64 * nw), 0, s, \
+        hipLaunchKernelGGL((k_score<KDT, D>), dim3((mt + 2 * nw - 1) / (2 * nw), g.B),           \
+                           dim3(64 * nw), 0, s,                                                 \
                            g, k, kscale, qbar, bias, z);                                        \
         timing_end("k_score", s);                                                               \
         return hipGetLastError();                                                               \

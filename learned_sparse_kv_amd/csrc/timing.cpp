@@ -22,27 +22,43 @@ struct Pair {
 };
 
 std::atomic<int> g_on{0};
+std::atomic<int> g_filtered{0};  // time only the kernel named in g_only
+char g_only[64] = {0};
 std::mutex g_mu;
 std::map<std::string, std::vector<Pair>> g_pending;
 std::map<std::string, std::pair<int64_t, double>> g_done;
+std::vector<hipEvent_t> g_free;  // recycled events (created once, reused)
 thread_local hipEvent_t t_start = nullptr;
+
+hipEvent_t take_event() {
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if (!g_free.empty()) {
+            hipEvent_t e = g_free.back();
+            g_free.pop_back();
+            return e;
+        }
+    }
+    hipEvent_t e = nullptr;
+    return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+}
 
 }  // namespace
 
+static bool wanted(const char* name) {
+    return !g_filtered.load(std::memory_order_acquire) || std::strcmp(name, g_only) == 0;
+}
+
 void timing_begin(const char* name, hipStream_t s) {
-    (void)name;
-    if (!g_on.load(std::memory_order_relaxed)) return;
-    if (hipEventCreate(&t_start) != hipSuccess) {
-        t_start = nullptr;
-        return;
-    }
-    (void)hipEventRecord(t_start, s);
+    if (!g_on.load(std::memory_order_relaxed) || !wanted(name)) return;
+    t_start = take_event();
+    if (t_start) (void)hipEventRecord(t_start, s);
 }
 
 void timing_end(const char* name, hipStream_t s) {
     if (!g_on.load(std::memory_order_relaxed) || !t_start) return;
-    hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return;
+    hipEvent_t e = take_event();
+    if (!e) return;
     (void)hipEventRecord(e, s);
     std::lock_guard<std::mutex> lk(g_mu);
     g_pending[name].push_back({t_start, e});
@@ -58,8 +74,8 @@ static void drain() {
                 acc.first += 1;
                 acc.second += ms;
             }
-            (void)hipEventDestroy(p.a);
-            (void)hipEventDestroy(p.b);
+            g_free.push_back(p.a);
+            g_free.push_back(p.b);
         }
     }
     g_pending.clear();
@@ -69,6 +85,17 @@ extern "C" {
 
 lsa_status lsa_timing_enable(int32_t on) {
     g_on.store(on ? 1 : 0);
+    return LSA_OK;
+}
+
+lsa_status lsa_timing_only(const char* kernel) {
+    if (kernel && std::strlen(kernel) >= sizeof(g_only)) return LSA_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_filtered.store(0, std::memory_order_release);
+    if (kernel) {
+        std::strcpy(g_only, kernel);
+        g_filtered.store(1, std::memory_order_release);
+    }
     return LSA_OK;
 }
 

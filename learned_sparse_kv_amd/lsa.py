@@ -99,6 +99,7 @@ def _load():
         "lsa_ctx_prime": ([P, C.POINTER(lsa_trigger_in), P, P, C.POINTER(lsa_window_out)], I),
         "lsa_step64": ([P, C.POINTER(lsa_window_in), C.POINTER(lsa_window_out), P, P], I),
         "lsa_timing_enable": ([I32], I),
+        "lsa_timing_only": ([C.c_char_p], I),
         "lsa_timing_reset": ([], None),
         "lsa_timing_read": ([C.c_char_p, C.POINTER(I64), C.POINTER(C.c_double)], I),
     }
@@ -286,6 +287,10 @@ KERNELS = ("k_fuse_query", "k_score", "k_select", "k_refine", "k_topk", "k_refin
 
 def lsa_timing_enable(on: bool):
     _check("lsa_timing_enable", _lib.lsa_timing_enable(1 if on else 0))
+
+
+def lsa_timing_only(kernel=None):
+    _check("lsa_timing_only", _lib.lsa_timing_only(kernel.encode() if kernel else None))
 
 
 def lsa_timing_reset():
