@@ -11,7 +11,7 @@
 //     U = I' + E as order-preserving 32-bit keys and adds to the request's
 //     coarse histograms of L and U (top 10 key bits).
 //  K2 k_band_fine    every block finds the coarse bins holding the k-th
-//     largest L and the k-th largest U, then adds fine histograms (1024-key
+//     largest L and the k-th largest U, then adds fine histograms (2048-key
 //     bins) of the keys inside those two coarse bins.
 //  K3 k_band_list    every block finds tau = lowest key of the fine bin
 //     holding the k-th largest L and edge = first key above the fine bin
@@ -54,12 +54,15 @@ __host__ __device__ constexpr float gam(int n) { return n * kU2 / (1.0f - n * kU
 
 constexpr int kWaves = 4;         // waves per block of K1 and K3
 constexpr int kCoarse = 1024;     // coarse bins: key >> 22
-constexpr int kFine = 4096;       // fine bins inside one coarse bin: (key >> 10) & 4095
+constexpr int kFine = 2048;       // fine bins inside one coarse bin: (key >> 11) & 2047
 constexpr int kHist = 2 * kCoarse + 2 * kFine;  // per request: coarse L, U, then fine L, U
 constexpr int kRedStride = 33;    // per-token row: 16 + 16 partial sums, |key|^2
 constexpr int kT = 1024, kTW = kT / 64;
 constexpr int kMaxSeg = 1024;     // band list segments (K3 blocks) per request, at most
 constexpr int kListCap = 8192;    // band entries K4 keeps in LDS
+constexpr int kUncCap = 1024;     // uncertain entries K4 ranks directly
+constexpr int kPgCap = 256;       // chunks per K3 block whose pages K3 keeps in LDS
+constexpr int kUclCap = 512;      // uncertain entries per K3 block kept in LDS
 
 // 8 fp8 e4m3fn bytes -> 8 bf16 (exact: every e4m3 value is a bf16 value)
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 v) {
@@ -369,8 +372,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
 #pragma unroll
         for (int u = 0; u < U4; ++u) {
             if (cb + kWaves * u >= c1) break;
-            if ((f[u].x >> 22) == cL) atomicAdd(&hf[(f[u].x >> 10) & (kFine - 1)], 1u);
-            if ((f[u].y >> 22) == cU) atomicAdd(&hf[kFine + ((f[u].y >> 10) & (kFine - 1))], 1u);
+            if ((f[u].x >> 22) == cL) atomicAdd(&hf[(f[u].x >> 11) & (kFine - 1)], 1u);
+            if ((f[u].y >> 22) == cU) atomicAdd(&hf[kFine + ((f[u].y >> 11) & (kFine - 1))], 1u);
         }
     }
     __syncthreads();
@@ -407,20 +410,47 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     __shared__ int s_nb[kWaves], s_nu[kWaves];
     __shared__ uint32_t hf[2 * kFine];
     __shared__ int wsum[kWaves], s_out[4];
+    __shared__ int64_t pgb[kPgCap];  // page (slot) of chunk c0 + t
+    __shared__ float psc[kPgCap];    // its index-key scale
+    __shared__ int ucp[kUclCap], ucj[kUclCap];  // uncertain entries: position, list index
     const int r = blockIdx.y, X = gridDim.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nc = cnt[r];
     if (nc * 64 <= k) return;
     const int64_t off = g.chunk_off[r];
+    int c0, c1;
+    block_chunks(nc, X, blockIdx.x, c0, c1);
+    const int nch = c1 - c0;
+    const bool pg_lds = nch <= kPgCap;
+    // independent loads first: page and scale of this block's chunks, the
+    // weights and the query rows (for the re-score)
+    if (pg_lds && tid < nch) {
+        const int c = sel[off + c0 + tid];
+        pgb[tid] = page_table ? (int64_t)page_table[off + c] : off + c;
+        psc[tid] = KDT == LSA_FP8_E4M3FN ? ikey_scale[off + c] : 1.0f;
+    }
+    for (int e = tid; e < H; e += blockDim.x) wf[e] = w[(int64_t)r * H + e];
+    const int lt2 = lane % TPT, ts = lane / TPT;
+    uint32_t qp[HPT][D / 2];
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) {
+        const uint4* src = (const uint4*)(q + ((int64_t)r * H + lt2 + TPT * j) * D);
+#pragma unroll
+        for (int x = 0; x < D / 8; ++x) {
+            const uint4 v = src[x];
+            qp[j][4 * x] = v.x;
+            qp[j][4 * x + 1] = v.y;
+            qp[j][4 * x + 2] = v.z;
+            qp[j][4 * x + 3] = v.w;
+        }
+    }
     // tau: lowest key of the fine bin holding the k-th largest L; edge: first
     // key above the fine bin holding the k-th largest U
     const int4 ci = cinfo[r];
     load_hist(hist + (int64_t)r * kHist + 2 * kCoarse, hf, 2 * kFine);
     kth_bin<kFine, kWaves>(hf, k - ci.y, wsum, &s_out[0]);
     kth_bin<kFine, kWaves>(hf + kFine, k - ci.w, wsum, &s_out[2]);
-    const uint32_t tau = ((uint32_t)ci.x << 22) | ((uint32_t)s_out[0] << 10);
-    const uint64_t edge = ((uint64_t)(uint32_t)ci.z << 22) + ((uint64_t)(s_out[2] + 1) << 10);
-    int c0, c1;
-    block_chunks(nc, X, blockIdx.x, c0, c1);
+    const uint32_t tau = ((uint32_t)ci.x << 22) | ((uint32_t)s_out[0] << 11);
+    const uint64_t edge = ((uint64_t)(uint32_t)ci.z << 22) + ((uint64_t)(s_out[2] + 1) << 11);
     const int64_t seg = (off + c0) * 64;
     const uint64_t lt = (1ull << lane) - 1;
     // ordered lists: round j takes chunk c0 + 4j + wave
@@ -453,29 +483,21 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
             const int j = pb + __popcll(mb & lt);
             bl[seg + j] = c * 64 + lane;
             bk[seg + j] = sure ? 0xffffffffu : 0u;
-            if (unc) ul[seg + pu + __popcll(mu & lt)] = j;
+            if (unc) {
+                const int u = pu + __popcll(mu & lt);
+                ul[seg + u] = j;
+                if (u < kUclCap) {
+                    ucp[u] = c * 64 + lane;
+                    ucj[u] = j;
+                }
+            }
         }
     }
     if (tid == 0) scnt[(int64_t)r * X + blockIdx.x] = nb;
     if (nu == 0) return;  // uniform
     // canonical scores of this block's uncertain entries
     __threadfence_block();
-    for (int e = tid; e < H; e += blockDim.x) wf[e] = w[(int64_t)r * H + e];
     __syncthreads();
-    const int lt2 = lane % TPT, ts = lane / TPT;
-    uint32_t qp[HPT][D / 2];
-#pragma unroll
-    for (int j = 0; j < HPT; ++j) {
-        const uint4* src = (const uint4*)(q + ((int64_t)r * H + lt2 + TPT * j) * D);
-#pragma unroll
-        for (int x = 0; x < D / 8; ++x) {
-            const uint4 v = src[x];
-            qp[j][4 * x] = v.x;
-            qp[j][4 * x + 1] = v.y;
-            qp[j][4 * x + 2] = v.z;
-            qp[j][4 * x + 3] = v.w;
-        }
-    }
     float* kr = kf[wv][ts];
     float* rr = rel[wv][ts];
     for (int u0 = wv * TPW; u0 < nu; u0 += kWaves * TPW) {
@@ -484,12 +506,25 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
         int64_t e = 0;
         float scale = 1.0f;
         if (valid) {
-            e = seg + ul[seg + u];
-            const int p = bl[e];
-            const int c = sel[off + (p >> 6)];
-            const int64_t pg = page_table ? (int64_t)page_table[off + c] : off + c;
+            int p, j;
+            if (u < kUclCap) {
+                p = ucp[u];
+                j = ucj[u];
+            } else {
+                j = ul[seg + u];
+                p = bl[seg + j];
+            }
+            e = seg + j;
+            int64_t pg;
+            if (pg_lds) {
+                pg = pgb[(p >> 6) - c0];
+                scale = psc[(p >> 6) - c0];
+            } else {
+                const int c = sel[off + (p >> 6)];
+                pg = page_table ? (int64_t)page_table[off + c] : off + c;
+                if constexpr (KDT == LSA_FP8_E4M3FN) scale = ikey_scale[off + c];
+            }
             const uint8_t* row = pages + pg * page_bytes + ikey_off + (int64_t)(p & 63) * ROWB;
-            if constexpr (KDT == LSA_FP8_E4M3FN) scale = ikey_scale[off + c];
             for (int e4 = lt2; e4 < D / 4; e4 += TPT) {
                 float4 x;
                 if constexpr (KDT == LSA_BF16) {
@@ -541,11 +576,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
 }
 
 // K4.  Exact top-k over the band of one request (one block); also clears
-// the request's histograms.  The block
-// lists of K3 are gathered in order into LDS (up to kListCap entries), the
-// k-th largest key is found by 12/12/8-bit radix select, then the emit keeps
-// keys above it and the lowest-index ties.  Larger bands (only with massive
-// ties) take the same steps reading global memory.
+// the request's histograms.  The block lists of K3 are gathered in order
+// into LDS (up to kListCap entries).  Usually few entries are uncertain:
+// each is ranked against the others by (score desc, token asc) and the best
+// k - #certain join the certain ones, emitted in token order.  Otherwise (only
+// with massive ties) the k-th largest key is found by 12/12/8-bit radix
+// select and the emit keeps keys above it and the lowest-index ties, reading
+// global memory when the band does not fit in LDS.
 __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __restrict__ sel,
                                                   const int32_t* __restrict__ cnt,
                                                   const int32_t* __restrict__ scnt, int X,
@@ -557,10 +594,12 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
     __shared__ uint32_t hist[4096];
     __shared__ uint32_t lkey[kListCap];
     __shared__ int32_t lpos[kListCap];
+    __shared__ __attribute__((aligned(16))) uint64_t uval[kUncCap];  // (key, ~position): larger ranks first
+    __shared__ int32_t uj[kUncCap];
     __shared__ int boff[kMaxSeg + 1];
     __shared__ int wsum[kTW];
     __shared__ uint32_t s_prefix;
-    __shared__ int s_remaining, s_eq;
+    __shared__ int s_remaining, s_eq, s_u;
     const int r = blockIdx.x, tid = threadIdx.x;
     const int nc = cnt[r];
     // the request's histograms were last read by the previous kernel: clear
@@ -598,13 +637,66 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
         key = bk[e];
         pos = bl[e];
     };
+    const int32_t* sl = sel + off;
+    int32_t* out = topk + (int64_t)r * k;
     if (in_lds) {
+        if (tid == 0) s_u = 0;
         for (int j = tid; j < m; j += kT) {
             const int64_t e = gidx(j);
             lkey[j] = bk[e];
             lpos[j] = bl[e];
         }
         __syncthreads();
+        // The certain entries (key 0xffffffff) are all in; the uncertain ones
+        // (few) are ranked against each other by (score desc, token asc) and
+        // the best k - #certain are taken.
+        const int lane = tid & 63;
+        const uint64_t lt = (1ull << lane) - 1;
+        for (int j0 = 0; j0 < m; j0 += kT) {  // uniform trip count
+            const int j = j0 + tid;
+            const bool unc = j < m && lkey[j] != 0xffffffffu;
+            const uint64_t mk = __ballot(unc);
+            int base = 0;
+            if (lane == 0 && mk) base = atomicAdd(&s_u, __popcll(mk));
+            base = __shfl(base, 0);
+            const int t = base + __popcll(mk & lt);
+            if (unc && t < kUncCap) {
+                uval[t] = ((uint64_t)lkey[j] << 32) | (uint32_t)~(uint32_t)lpos[j];
+                uj[t] = j;
+            }
+        }
+        __syncthreads();
+        const int u = s_u;
+        if (u <= kUncCap) {
+            const int need = k - (m - u);
+            if (u & 1) {  // pad to an even count with an entry below every other
+                if (tid == 0) uval[u] = 0ull;
+                __syncthreads();
+            }
+            const int u2 = (u + 1) & ~1;
+            for (int t = tid; t < u; t += kT) {
+                const uint64_t vt = uval[t];
+                int rank = 0;
+#pragma unroll 8
+                for (int s2 = 0; s2 < u2; s2 += 2) {
+                    const ulonglong2 v2 = *(const ulonglong2*)&uval[s2];
+                    rank += (v2.x > vt) + (v2.y > vt);
+                }
+                lkey[uj[t]] = rank < need ? 0xffffffffu : 0u;
+            }
+            __syncthreads();
+            // emit the taken entries in list (token) order: thread t takes a
+            // contiguous run of the list
+            const int per = (m + kT - 1) / kT;
+            const int j0 = min(m, tid * per), j1 = min(m, j0 + per);
+            int tc = 0;
+            for (int j = j0; j < j1; ++j) tc += lkey[j] == 0xffffffffu;
+            int o = block_scan<kTW>(tc, wsum, tot);
+            for (int j = j0; j < j1; ++j)
+                if (lkey[j] == 0xffffffffu) out[o++] = sl[lpos[j] >> 6] * 64 + (lpos[j] & 63);
+            if (tid == 0) tcnt[r] = tot;
+            return;
+        }
     }
     uint32_t prefix = 0, mask = 0;
     int remaining = k;
@@ -646,8 +738,6 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
     const uint32_t K = prefix;
     const int need = remaining;
     const bool all_ties = (s_eq == need);
-    const int32_t* sl = sel + off;
-    int32_t* out = topk + (int64_t)r * k;
     int base = 0, eqbase = 0;
     for (int p0 = 0; p0 < m; p0 += 4 * kT) {
         const int pb = p0 + 4 * tid;
