@@ -64,18 +64,24 @@ constexpr int kUncCap = 1024;     // uncertain entries K4 ranks directly
 constexpr int kPgCap = 256;       // chunks per K3 block whose pages K3 keeps in LDS
 constexpr int kUclCap = 512;      // uncertain entries per K3 block kept in LDS
 
-// 8 fp8 e4m3fn bytes -> 8 bf16 (exact: every e4m3 value is a bf16 value)
-__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 v) {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, false);
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, true);
-    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false);
-    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true);
+// 8 fp8 e4m3fn bytes -> 8 bf16 (exact: every e4m3 value is a bf16 value;
+// the conversion scale is 1)
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
     uint4 r;
-    r.x = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-    r.y = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
-    r.z = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
-    r.w = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
     return r;
+}
+
+// Element offset of the 8 dims lane group lq holds in MFMA k-step ks.  Any
+// order of the dims gives the same dot products as long as both operands
+// use it; fp8 rows are read 16 bytes (two k-steps) per lane.
+template <int KDT>
+__device__ __forceinline__ int kdim(int ks, int lq) {
+    if constexpr (KDT == LSA_FP8_E4M3FN) return (ks >> 1) * 64 + lq * 16 + (ks & 1) * 8;
+    else return ks * 32 + lq * 8;
 }
 
 __device__ __forceinline__ float sumsq_bf16x8(uint4 v) {
@@ -166,7 +172,7 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
     constexpr int ROWB = D * EB;
     constexpr int KS = D / 32;   // MFMA k-steps
     constexpr int HB = H / 16;   // head blocks
-    using Raw = std::conditional_t<KDT == LSA_BF16, uint4, uint2>;
+    constexpr int NR = KDT == LSA_BF16 ? KS : KS / 2;  // 16-byte key loads per token row and lane
     __shared__ uint32_t hl[2 * kCoarse];  // coarse L bins, then coarse U bins
     __shared__ float red[kWaves][64 * kRedStride];
 
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
         for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                qb[hb][ks] = *(const uint4*)(qr + (hb * 16 + l16) * D + ks * 32 + lq * 8);
+                qb[hb][ks] = *(const uint4*)(qr + (hb * 16 + l16) * D + kdim<KDT>(ks, lq));
             wl[hb] = w[(int64_t)r * H + hb * 16 + l16];
             wa[hb] = fabsf(wl[hb]);
         }
@@ -217,8 +223,8 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
                 if constexpr (KDT == LSA_FP8_E4M3FN) sc_l = ikey_scale[off + c];
             }
         };
-        Raw raw[4][KS];
-        // key rows of chunk j: A operands of tokens tb*16 + l16, dims ks*32 + lq*8 .. +8
+        uint4 raw[4][NR];
+        // key rows of chunk j: A operands of tokens tb*16 + l16 (16 bytes per load)
         auto fetch = [&](int j) {
             const int src = j & 63;
             const int64_t pgo = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pg_l, src) |
@@ -227,8 +233,8 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    raw[tb][ks] = *(const Raw*)(base + (tb * 16 + l16) * ROWB + (ks * 32 + lq * 8) * EB);
+                for (int n = 0; n < NR; ++n)
+                    raw[tb][n] = *(const uint4*)(base + (tb * 16 + l16) * ROWB + n * 64 + lq * 16);
         };
         if (nj > 0) {
             load_idx(0);
@@ -243,7 +249,8 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     if constexpr (KDT == LSA_BF16) ka[tb][ks] = raw[tb][ks];
-                    else ka[tb][ks] = fp8x8_to_bf16x8(raw[tb][ks]);
+                    else ka[tb][ks] = (ks & 1) ? fp8x8_to_bf16x8(raw[tb][ks >> 1].z, raw[tb][ks >> 1].w)
+                                               : fp8x8_to_bf16x8(raw[tb][ks >> 1].x, raw[tb][ks >> 1].y);
                 }
             const float scale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), j & 63));
             if (j + 1 < nj) {
