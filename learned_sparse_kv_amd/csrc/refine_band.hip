@@ -341,14 +341,20 @@ __device__ __forceinline__ void block_chunks(int nc, int X, int x, int& c0, int&
 // K2.  Grid (X, B).  Requests with no more than k candidates keep them all
 // here.  Otherwise every block finds the coarse bins cL, cU holding the k-th
 // largest L and U (block 0 keeps them, with the counts above them, in
-// cinfo), then adds the fine histograms of its chunks' keys that fall in
-// those bins.
+// cinfo), then, in one pass over its chunks' keys: adds the fine histograms
+// of the keys that fall in those bins, and lists in token order (at
+// (off + c0) * 64, count in pcnt[r][x]) the candidates whose U reaches the
+// lower edge of bin cL.  No other candidate can be in the band (its
+// U < (cL << 22) <= tau).
+constexpr int kPre = 8;  // rounds of keys a K2 wave has in flight
+
 __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
     GeomDev g, const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
     const uint2* __restrict__ lu, int k, uint32_t* __restrict__ hist, int4* __restrict__ cinfo,
-    int32_t* __restrict__ topk, int32_t* __restrict__ tcnt) {
+    int32_t* __restrict__ plist, int32_t* __restrict__ pcnt, int32_t* __restrict__ topk,
+    int32_t* __restrict__ tcnt) {
     __shared__ uint32_t hf[2 * kFine];
-    __shared__ int wsum[kWaves], s_out[4];
+    __shared__ int wsum[kWaves], s_out[4], s_np[kWaves];
     const int r = blockIdx.y, X = gridDim.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nc = cnt[r], n = nc * 64;
     const int64_t off = g.chunk_off[r];
@@ -358,41 +364,69 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
         if (blockIdx.x == 0 && tid == 0) tcnt[r] = n;
         return;
     }
+    int c0, c1;
+    block_chunks(nc, X, blockIdx.x, c0, c1);
+    // this wave's keys for the first kPre rounds (round j: chunk c0 + 4j + wave)
+    uint2 f[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const int c = c0 + kWaves * u + wv;
+        f[u] = c < c1 ? lu[(off + c) * 64 + lane] : make_uint2(0u, 0u);
+    }
     uint32_t* gh = hist + (int64_t)r * kHist;
     load_hist(gh, hf, 2 * kCoarse);
     kth_bin<kCoarse, kWaves>(hf, k, wsum, &s_out[0]);
     kth_bin<kCoarse, kWaves>(hf + kCoarse, k, wsum, &s_out[2]);
     const uint32_t cL = (uint32_t)s_out[0], cU = (uint32_t)s_out[2];
+    const uint32_t tau_c = cL << 22;
     if (blockIdx.x == 0 && tid == 0) cinfo[r] = make_int4(s_out[0], s_out[1], s_out[2], s_out[3]);
     for (int i = tid; i < 2 * kFine; i += blockDim.x) hf[i] = 0;
     __syncthreads();
-    int c0, c1;
-    block_chunks(nc, X, blockIdx.x, c0, c1);
-    constexpr int U4 = 4;
-    for (int cb = c0 + wv; cb < c1; cb += kWaves * U4) {
-        uint2 f[U4];
+    const int64_t seg = (off + c0) * 64;
+    const uint64_t lt = (1ull << lane) - 1;
+    int np = 0;
+    for (int cb0 = c0; cb0 < c1; cb0 += kWaves * kPre) {  // uniform
 #pragma unroll
-        for (int u = 0; u < U4; ++u) {
-            const int c = cb + kWaves * u;
+        for (int u = 0; u < kPre; ++u) {
+            const int cb = cb0 + kWaves * u;
+            if (cb >= c1) break;  // uniform
+            const int c = cb + wv;
+            const bool have = c < c1;
+            const uint2 cur = f[u];
+            if (have) {
+                if ((cur.x >> 22) == cL) atomicAdd(&hf[(cur.x >> 11) & (kFine - 1)], 1u);
+                if ((cur.y >> 22) == cU) atomicAdd(&hf[kFine + ((cur.y >> 11) & (kFine - 1))], 1u);
+            }
+            const bool pre = have && cur.y >= tau_c;
+            const uint64_t m = __ballot(pre);
+            if (lane == 0) s_np[wv] = __popcll(m);
+            __syncthreads();
+            int pb = np;
+            for (int w2 = 0; w2 < kWaves; ++w2) {
+                pb += w2 < wv ? s_np[w2] : 0;
+                np += s_np[w2];
+            }
+            __syncthreads();
+            if (pre) plist[seg + pb + __popcll(m & lt)] = c * 64 + lane;
+        }
+        // next kPre rounds
+#pragma unroll
+        for (int u = 0; u < kPre; ++u) {
+            const int c = cb0 + kWaves * (kPre + u) + wv;
             f[u] = c < c1 ? lu[(off + c) * 64 + lane] : make_uint2(0u, 0u);
         }
-#pragma unroll
-        for (int u = 0; u < U4; ++u) {
-            if (cb + kWaves * u >= c1) break;
-            if ((f[u].x >> 22) == cL) atomicAdd(&hf[(f[u].x >> 11) & (kFine - 1)], 1u);
-            if ((f[u].y >> 22) == cU) atomicAdd(&hf[kFine + ((f[u].y >> 11) & (kFine - 1))], 1u);
-        }
     }
+    if (tid == 0) pcnt[(int64_t)r * X + blockIdx.x] = np;
     __syncthreads();
     uint32_t* gf = gh + 2 * kCoarse;
     for (int i = tid; i < 2 * kFine; i += blockDim.x)
         if (hf[i]) atomicAdd(&gf[i], hf[i]);
 }
 
-// K3.  Grid (X, B).  Block x lists, in token order, the band candidates of
-// its chunks at (off + c0) * 64 (positions p into the request's candidates;
-// key 0xffffffff for certain ones) and its count at scnt[r][x]; its
-// uncertain ones get the canonical score as their key.  For the score each
+// K3.  Grid (X, B).  Block x lists, in token order, the band candidates
+// among its pre-band list at (off + c0) * 64 (positions p into the request's
+// candidates; key 0xffffffff for certain ones) and its count at scnt[r][x];
+// its uncertain ones get the canonical score as their key.  For the score each
 // token is taken by TPT = min(H, 64) lanes, one or two heads per lane, with
 // the lane's query rows held in registers (bf16 pairs); the key row goes
 // through LDS as fp32, each head runs its fma chain in element order, then
@@ -401,7 +435,8 @@ template <int KDT, int D, int H>
 __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     GeomDev g, const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
     const uint2* __restrict__ lu, const uint32_t* __restrict__ hist,
-    const int4* __restrict__ cinfo, int k,
+    const int4* __restrict__ cinfo, const int32_t* __restrict__ plist,
+    const int32_t* __restrict__ pcnt, int k,
     const uint8_t* __restrict__ pages, int64_t page_bytes, int64_t ikey_off,
     const int32_t* __restrict__ page_table, const float* __restrict__ ikey_scale,
     const uint16_t* __restrict__ q, const float* __restrict__ w, int32_t* __restrict__ bl,
@@ -414,7 +449,6 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     __shared__ __attribute__((aligned(16))) float kf[kWaves][TPW][D];
     __shared__ float rel[kWaves][TPW][H];
     __shared__ float wf[H];
-    __shared__ int s_nb[kWaves], s_nu[kWaves];
     __shared__ uint32_t hf[2 * kFine];
     __shared__ int wsum[kWaves], s_out[4];
     __shared__ int64_t pgb[kPgCap];  // page (slot) of chunk c0 + t
@@ -459,46 +493,34 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     const uint32_t tau = ((uint32_t)ci.x << 22) | ((uint32_t)s_out[0] << 11);
     const uint64_t edge = ((uint64_t)(uint32_t)ci.z << 22) + ((uint64_t)(s_out[2] + 1) << 11);
     const int64_t seg = (off + c0) * 64;
-    const uint64_t lt = (1ull << lane) - 1;
-    // ordered lists: round j takes chunk c0 + 4j + wave
+    const int npre = pcnt[(int64_t)r * X + blockIdx.x];
+    const uint2* lur = lu + off * 64;
+    // ordered lists over the pre-band entries, one per thread per round
     int nb = 0, nu = 0;
-    uint2 f = make_uint2(0u, 0u);
-    if (c0 + wv < c1) f = lu[(off + c0 + wv) * 64 + lane];
-    for (int cb = c0; cb < c1; cb += kWaves) {
-        const int c = cb + wv;
-        const bool have = c < c1;
-        const uint2 cur = f;
-        if (c + kWaves < c1) f = lu[(off + c + kWaves) * 64 + lane];
+    for (int b0 = 0; b0 < npre; b0 += 64 * kWaves) {  // uniform
+        const int idx = b0 + tid;
+        const bool have = idx < npre;
+        const int p = have ? plist[seg + idx] : 0;
+        const uint2 cur = have ? lur[p] : make_uint2(0u, 0u);
         const bool band = have && cur.y >= tau;
         const bool sure = band && (uint64_t)cur.x >= edge;
         const bool unc = band && !sure;
-        const uint64_t mb = __ballot(band), mu = __ballot(unc);
-        if (lane == 0) {
-            s_nb[wv] = __popcll(mb);
-            s_nu[wv] = __popcll(mu);
-        }
-        __syncthreads();
-        int pb = nb, pu = nu;
-        for (int i = 0; i < kWaves; ++i) {
-            pb += i < wv ? s_nb[i] : 0;
-            pu += i < wv ? s_nu[i] : 0;
-            nb += s_nb[i];
-            nu += s_nu[i];
-        }
-        __syncthreads();
+        int tb_, tu_;
+        const int j = nb + block_scan<kWaves>(band ? 1 : 0, wsum, tb_);
+        const int u = nu + block_scan<kWaves>(unc ? 1 : 0, wsum, tu_);
         if (band) {
-            const int j = pb + __popcll(mb & lt);
-            bl[seg + j] = c * 64 + lane;
+            bl[seg + j] = p;
             bk[seg + j] = sure ? 0xffffffffu : 0u;
             if (unc) {
-                const int u = pu + __popcll(mu & lt);
                 ul[seg + u] = j;
                 if (u < kUclCap) {
-                    ucp[u] = c * 64 + lane;
+                    ucp[u] = p;
                     ucj[u] = j;
                 }
             }
         }
+        nb += tb_;
+        nu += tu_;
     }
     if (tid == 0) scnt[(int64_t)r * X + blockIdx.x] = nb;
     if (nu == 0) return;  // uniform
@@ -831,8 +853,8 @@ static size_t clean_words(const GeomDev& g) { return (size_t)g.B * kHist; }
 size_t band_ws_bytes(const GeomDev& g) {
     const size_t nc = (size_t)g.chunk_off[g.B] * 64 + 64;
     return align_up(clean_words(g) * 4, 256) + align_up((size_t)g.B * sizeof(int4), 256) +
-           align_up(nc * sizeof(uint2), 256) + 3 * align_up(nc * 4, 256) +
-           align_up((size_t)g.B * k23_blocks(g) * 4, 256);
+           align_up(nc * sizeof(uint2), 256) + 4 * align_up(nc * 4, 256) +
+           2 * align_up((size_t)g.B * k23_blocks(g) * 4, 256);
 }
 
 hipError_t launch_band_clear(const GeomDev& g, void* ws, hipStream_t s) {
@@ -864,7 +886,11 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
     b += align_up(nc * 4, 256);
     int32_t* ul = (int32_t*)b;
     b += align_up(nc * 4, 256);
+    int32_t* plist = (int32_t*)b;
+    b += align_up(nc * 4, 256);
     int32_t* scnt = (int32_t*)b;
+    b += align_up((size_t)g.B * X2 * 4, 256);
+    int32_t* pcnt = (int32_t*)b;
     const uint8_t* pg = (const uint8_t*)pages;
     const uint16_t* qq = (const uint16_t*)q;
     const int Hh = H;
@@ -888,7 +914,7 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
     if (e != hipSuccess) return e;
     timing_begin("k_band_fine", s);
     hipLaunchKernelGGL(k_band_fine, dim3(X2, g.B), dim3(64 * kWaves), 0, s, g, sel, cnt, lu, k,
-                       hist, cinfo, topk, tcnt);
+                       hist, cinfo, plist, pcnt, topk, tcnt);
     timing_end("k_band_fine", s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = hipErrorInvalidValue;
@@ -896,8 +922,8 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
 #define LSA_K3(KDT, D, HH)                                                                        \
     if (idx_dt == KDT && d == D && Hh == HH) {                                                    \
         hipLaunchKernelGGL((k_band_list<KDT, D, HH>), dim3(X2, g.B), dim3(64 * kWaves), 0, s, g,   \
-                           sel, cnt, lu, hist, cinfo, k, pg, page_bytes, ikey_off, page_table,   \
-                           ikey_scale, qq, w, bl, bk, ul, scnt);                                  \
+                           sel, cnt, lu, hist, cinfo, plist, pcnt, k, pg, page_bytes, ikey_off,   \
+                           page_table, ikey_scale, qq, w, bl, bk, ul, scnt);                      \
         e = hipGetLastError();                                                                    \
     }
     LSA_K3(LSA_BF16, 128, 16) LSA_K3(LSA_BF16, 128, 32) LSA_K3(LSA_BF16, 128, 64)
