@@ -25,6 +25,8 @@
  *    failure returns LSA_ERR_HIP; a kernel fault surfaces at the next
  *    synchronisation.
  *  - Calls are reentrant when given distinct outputs and workspaces.
+ *  - Workspaces (ws) must be 16-byte aligned (hipMalloc and torch device
+ *    allocations are); an unaligned one is LSA_ERR_INVALID_ARG.
  *
  * Geometry (per request r, context L_r, chunk C, recent window W).  The most
  * recent W tokens are always attended (cjcn.com.cn explainer, section 二, last

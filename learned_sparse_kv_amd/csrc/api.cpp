@@ -74,7 +74,7 @@ lsa_status lsa_score_chunks(const lsa_geom* g, const void* q, lsa_dtype q_dt, co
     GeomDev gd;
     lsa_status st = geom_derive(g, &gd);
     if (st != LSA_OK) return st;
-    if (!q || !w || !bias || !ws) return LSA_ERR_INVALID_ARG;
+    if (!q || !w || !bias || !ws || !aligned16(ws)) return LSA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return LSA_ERR_UNSUPPORTED;
     if (H < 1 || H > 256) return LSA_ERR_INVALID_ARG;
     if (q_dt != LSA_F32 && q_dt != LSA_BF16) return LSA_ERR_UNSUPPORTED;
@@ -121,7 +121,7 @@ lsa_status lsa_topk_refine(const lsa_geom* g, const int32_t* sel_ids, const int3
     GeomDev gd;
     lsa_status st = geom_derive(g, &gd);
     if (st != LSA_OK) return st;
-    if (!sel_cnt || !q || !w || !topk_idx || !topk_cnt || !ws) return LSA_ERR_INVALID_ARG;
+    if (!sel_cnt || !q || !w || !topk_idx || !topk_cnt || !ws || !aligned16(ws)) return LSA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return LSA_ERR_UNSUPPORTED;
     if (H < 1 || H > 128 || k < 1) return LSA_ERR_INVALID_ARG;
     // the VALU refine (every case the matrix-core path does not take) keeps the queries in LDS
@@ -185,7 +185,7 @@ lsa_status lsa_sparse_decode_attn(const lsa_geom* g, const void* q, int32_t Hq,
     if (!q || !recent || !topk_idx || !topk_cnt || !out || !ws || Hq < 1 || k < 1)
         return LSA_ERR_INVALID_ARG;
     if (gd.chunk_off[gd.B] > 0 && !pages) return LSA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(recent) || (pages && !aligned16(pages)))
+    if (!aligned16(q) || !aligned16(recent) || !aligned16(ws) || (pages && !aligned16(pages)))
         return LSA_ERR_INVALID_ARG;
     if (!(sm_scale == sm_scale) || n_splits < 0) return LSA_ERR_INVALID_ARG;
     AttnPlan plan;

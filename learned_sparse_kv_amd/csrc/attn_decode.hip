@@ -7,15 +7,15 @@
 // heads share one KV row per token (MQA); the latent row holds 576 values and
 // the value is its first 512.
 //
-// Positions of request r: p in [0, k) is top-k slot p (valid below the
-// top-k count), p in [k, k + R_r) is recent token rs + (p - k).  Positions
-// are cut into splits; each split keeps a running max m, sum l and
+// Positions of request r (bf16 latent kernel): the R_r recent tokens first,
+// then the filled top-k slots, so empty slots are never visited.  Positions
+// are cut into splits; each split keeps a reference max m, sum l and
 // unnormalised output (online softmax, base 2) and writes them to a
 // workspace; k_attn_merge combines the splits of each (request, head).
 //
 // k_attn_mla (bf16, Dk 576 / Dv 512): one block per (request, split, group
-// of 32 heads), 4 waves, 32-token tiles, MFMA 16x16x32 bf16; every KV byte
-// is read from HBM once per head group and feeds both products.
+// of 64 or 32 heads), 32-token tiles, MFMA 16x16x32 bf16; every KV byte is
+// read from HBM once per head group and feeds both products.
 // Algorithmic bytes per attended token: 1,152 (HBM-bound).
 //
 // k_attn_f32: fp32 rows, VALU, for small head counts (fp32 path).
@@ -60,33 +60,49 @@ __device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even
 }
 
 // ----------------------------------------------------------------------------
-// bf16 latent MQA (Dk 576, Dv 512), MFMA
+// bf16 latent MQA (Dk 576, Dv 512), MFMA 16x16x32 bf16.
+//
+// A block takes one (request, split, head group) with NW waves; the wave
+// pair (2 hq, 2 hq + 1) owns 32 heads.  In the pair, wave vh = 0 takes the
+// first half of the 576 key dimensions and value dimensions 0..255, wave
+// vh = 1 the second half and values 256..511.  Per 32-token tile:
+//   S^T = K Q^T  partial over the wave's 9 k-steps (A = key rows from LDS,
+//                B = the wave's query slice, held in registers all along);
+//   the two partials are swapped through LDS and added in a fixed order, so
+//   both waves hold the same S^T and run the same softmax;
+//   O^T += V^T P^T for the wave's 256 value dims (A = V^T from LDS transpose
+//                reads, B = P^T straight from the softmax registers).
+// The output and the softmax state stay in registers; only the partial S
+// goes through LDS.  The running reference m of a head is raised only when
+// a tile's max exceeds it by more than 8 (log2 units): the probabilities
+// exp2(s - m) then stay below 256 and the rescale of O^T is rare.  Since O
+// and l share the reference, the result is the same softmax.
+//
+// KV tiles: 32 rows land in LDS by direct global->LDS loads (16 bytes per
+// lane), three tiles deep.  The tile is kept in the operand layout of the
+// matrix core: block (token half tb, k-step ks) holds 64 slots of 16 bytes,
+// slot lq*16 + t = key row 16 tb + t, dims 32 ks + 8 lq .. +8, so the S
+// operand read of a wave is one contiguous 1 KB.  ds_read_b64_tr_b16 turns
+// 4 rows x 4 dims per lane group into the V^T operand.
+//
+// Positions of request r are [recent window (nrec) | top-k (kcnt)]: the
+// recent tokens first, then the filled top-k slots; splits cut this list.
+// The tail of the last tile repeats its last row and is masked to -inf.
 // ----------------------------------------------------------------------------
-constexpr int MT = 32;           // tokens per tile
-constexpr int MH = 32;           // heads per block
+constexpr int MT = 32;                        // tokens per tile
 constexpr int MDK = 576, MDV = 512;
-constexpr int PLS = 40;          // pl row stride (bf16)
+constexpr int kKSteps = MDK / 32;             // 18
+constexpr int kBlk = 1024;                    // bytes per (tb, ks) operand block
+constexpr int kTileB = 2 * kKSteps * kBlk;    // 36,864
+constexpr int kNBuf = 3;                      // tiles in LDS
 constexpr int kMaxSplitPos = 1024;
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-
-// ----------------------------------------------------------------------------
-// bf16 latent MQA, second form: the 32-token KV tile sits row-major in LDS
-// (rows padded to 1168 bytes), filled from registers that prefetch the next
-// tile.  S = Q K^T splits the 576-wide contraction over the 4 waves as
-// above; O += P V takes its V operands with LDS transpose reads
-// (ds_read_b64_tr_b16: lane n of each 16-lane group, pointing at
-// V[t0 + n/4][v0 + 4(n%4)], receives V[t0..t0+3][v0 + n]), so no transposed
-// copy of V is written.  Softmax is spread over all waves, one head per 8
-// lanes.  About 66 KB of LDS: two blocks per CU.
-// ----------------------------------------------------------------------------
-constexpr int RB = 1152, RBP = 1168;    // KV row bytes, padded LDS row bytes
-constexpr int SPT = 36;                 // sp row stride (floats), head-major [h][t]
-constexpr int kPieces = MT * RB / 16;   // 16-byte pieces per tile (2304)
-constexpr int kPPT = kPieces / 256;     // pieces per thread (9)
+constexpr float kRescaleSlack = 8.0f;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 __device__ __forceinline__ uint2 lds_tr16(const uint8_t* base_lds, int byte_off) {
     const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -95,205 +111,290 @@ __device__ __forceinline__ uint2 lds_tr16(const uint8_t* base_lds, int byte_off)
     return __builtin_bit_cast(uint2, r);
 }
 
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
-__global__ __launch_bounds__(256, 2) void k_attn_mla(GeomDev g, PosMap pm,
-                                                     const int32_t* __restrict__ tcnt,
-                                                     const uint16_t* __restrict__ q, int Hq,
-                                                     int n_splits, int per_split, int hgroups,
-                                                     float sm_log2e, float* __restrict__ part_o,
-                                                     float* __restrict__ part_ml) {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[MT * RBP];
-    __shared__ __attribute__((aligned(16))) float sp[4][MH * SPT];
-    __shared__ __attribute__((aligned(16))) uint16_t pl[MH][PLS];
-    __shared__ __attribute__((aligned(16))) float alpha_s[MH];
-    // row address per position; bit 0 set: empty position (the address is then
-    // a valid row of finite values, whose probability is forced to 0)
+// 16 bytes per lane from gptr to LDS (M0 + 16 * lane).  Written as asm so
+// that the compiler does not wait for these loads before every LDS read;
+// the kernel waits for them itself (vmcnt) before the tile barrier.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_off) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_off))
+                 : "memory");
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }  // lgkmcnt(0)
+
+// reductions over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane rows)
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    const __bf16 x = (__bf16)a, y = (__bf16)b;  // round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// NW waves per block, HPW blocks of 16 heads per wave; the block covers
+// 16 * HPW * NW / 2 heads.
+template <int NW, int HPW>
+__global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
+                                                        const int32_t* __restrict__ tcnt,
+                                                        const uint16_t* __restrict__ q, int Hq,
+                                                        int n_splits, int per_split, int hgroups,
+                                                        float sm_log2e, float* __restrict__ part_o,
+                                                        float* __restrict__ part_ml) {
+    constexpr int NB = 2 * kKSteps;                   // operand blocks per tile (36)
+    constexpr int NLmax = (NB + NW - 1) / NW;         // tile loads per wave (the first NB % NW waves)
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[kNBuf][kTileB];
+    __shared__ __attribute__((aligned(16))) float sx[NW][64 * 8 * HPW];
     __shared__ uint64_t rowp[kMaxSplitPos];
 
     const int bi = blockIdx.x;
-    const int xcd = bi & 7, j = bi >> 3;
-    const int hg = j % hgroups;
-    const int unit = (j / hgroups) * 8 + xcd;
+    const int xcd = bi & 7, jb = bi >> 3;
+    const int hg = jb % hgroups;
+    const int unit = (jb / hgroups) * 8 + xcd;
     if (unit >= g.B * n_splits) return;
     const int r = unit / n_splits, split = unit % n_splits;
+    const int tid = threadIdx.x, w = tid >> 6, L = tid & 63, l16 = L & 15, lq = L >> 4;
+    const int vh = w & 1;
+    const int h0 = hg * (8 * HPW * NW) + 16 * HPW * (w >> 1);  // first head of the pair
+    const int nl = (NB % NW == 0 || w < NB % NW) ? NLmax : NLmax - 1;  // this wave's tile loads
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, lq = l >> 4;
-    const int kcnt = tcnt[r];
+    const int kcnt = min(max(tcnt[r], 0), pm.k);
+    const int nrec = g.nrec[r];
+    const int P = nrec + kcnt;
     const int p_begin = split * per_split;
-    const int P = pm.k + g.nrec[r];
     const int npos = max(0, min(per_split, P - p_begin));
     const int ntiles = (npos + MT - 1) / MT;
-    const uint64_t dummy = (uint64_t)(pm.recent + g.rec_off[r] * pm.row_bytes) | 1ull;
 
-    for (int i = tid; i < ntiles * MT; i += 256) {
-        const uint8_t* row = (i < npos) ? pos_row(g, pm, r, kcnt, p_begin + i) : nullptr;
-        rowp[i] = row ? (uint64_t)row : dummy;
+    // query slices (B operands): head h0 + 16 hb + l16, k-steps 9 vh .. 9 vh + 8
+    u32x4_t Qb[HPW][9];
+    {
+        const uint16_t* qr = q + ((int64_t)r * Hq + h0) * MDK + (9 * vh) * 32 + lq * 8;
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb)
+#pragma unroll
+            for (int j = 0; j < 9; ++j) Qb[hb][j] = *(const u32x4_t*)(qr + (hb * 16 + l16) * MDK + j * 32);
     }
-
-    // Q slices as MFMA A operands: k-steps 4w..4w+3 and the rope k-step 16+w
-    // (waves 2 and 3 have no rope k-step: a zero slice)
-    uint4 Qa[2][5];
-    const uint16_t* qr = q + ((int64_t)r * Hq + hg * MH) * MDK;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            Qa[hb][jj] = *(const uint4*)(qr + (hb * 16 + l16) * MDK + (4 * w + jj) * 32 + lq * 8);
-        Qa[hb][4] = (w < 2) ? *(const uint4*)(qr + (hb * 16 + l16) * MDK + (16 + w) * 32 + lq * 8)
-                            : make_uint4(0, 0, 0, 0);
-    }
-    const int ks4 = 16 + (w & 1);  // rope k-step read by this wave (harmless for w >= 2)
-    __syncthreads();  // rowp ready
-
-    // tile loader: 8 threads per row; thread t copies the 16-byte columns
-    // (t%8) + 8k, k = 0..8, of row t/8 (coalesced 128-byte runs per row)
-    const int ld_row = tid >> 3, ld_col = (tid & 7) * 16;
-    uint8_t* const ld_dst = tile + ld_row * RBP + ld_col;
-
-    f32x4_t acc[2][8];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int vb = 0; vb < 8; ++vb) acc[hb][vb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;  // head 8w + l/8
-
-    u32x4_t R0[kPPT];  // the next tile, in flight while this one is computed
-    if (ntiles > 0) {
-        const int T0_ = 0;
-        {
-            gu32x4_t* src_ = (gu32x4_t*)((rowp[T0_ + ld_row] & ~15ull) + ld_col);
-            R0[0] = src_[0]; R0[1] = src_[8]; R0[2] = src_[16]; R0[3] = src_[24];
-            R0[4] = src_[32]; R0[5] = src_[40]; R0[6] = src_[48]; R0[7] = src_[56];
-            R0[8] = src_[64];
-        }
-        {
-            u32x4_t* d_ = (u32x4_t*)ld_dst;
-            d_[0] = R0[0]; d_[8] = R0[1]; d_[16] = R0[2]; d_[24] = R0[3]; d_[32] = R0[4];
-            d_[40] = R0[5]; d_[48] = R0[6]; d_[56] = R0[7]; d_[64] = R0[8];
+    // row address of every position of the split (the tail repeats the last)
+    {
+        const uint8_t* rec0 = pm.recent + g.rec_off[r] * pm.row_bytes;
+        const int64_t coff = g.chunk_off[r];
+        const int32_t* tk = pm.topk + (int64_t)r * pm.k;
+        for (int i = tid; i < ntiles * MT; i += 64 * NW) {
+            const int p = p_begin + min(i, npos - 1);
+            const uint8_t* row;
+            if (p < nrec) {
+                row = rec0 + (int64_t)p * pm.row_bytes;
+            } else {
+                const int sl = tk[p - nrec];
+                const int64_t c = coff + (sl >> 6);
+                const int64_t slot = pm.pt ? (int64_t)pm.pt[c] : c;
+                row = pm.pages + slot * pm.page_bytes + (int64_t)(sl & 63) * pm.row_bytes;
+            }
+            rowp[i] = (uint64_t)row;
         }
     }
-    if (ntiles > 1) {
-        const int T0_ = MT;
-        {
-            gu32x4_t* src_ = (gu32x4_t*)((rowp[T0_ + ld_row] & ~15ull) + ld_col);
-            R0[0] = src_[0]; R0[1] = src_[8]; R0[2] = src_[16]; R0[3] = src_[24];
-            R0[4] = src_[32]; R0[5] = src_[40]; R0[6] = src_[48]; R0[7] = src_[56];
-            R0[8] = src_[64];
+    // every load of the compiler's own is done before the tile loads start,
+    // so that the vmcnt waits in the loop count tile loads only
+    wait_vm<0>();
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+
+    // wave w loads blocks w, w + NW, ... of a tile: slot L of block (tb, ks) is
+    // key row 16 tb + l16, bytes 64 ks + 16 lq .. +16
+    auto load_tile = [&](int t, int buf) __attribute__((always_inline)) {
+        const uint8_t* ra0 = (const uint8_t*)rowp[t * MT + l16];
+        const uint8_t* ra1 = (const uint8_t*)rowp[t * MT + 16 + l16];
+        const uint32_t dst = lds_u32(tiles[buf]);
+#pragma unroll
+        for (int m = 0; m < NLmax; ++m) {
+            const int b = w + NW * m;
+            if (b < NB) {
+                const int tb = b >= kKSteps ? 1 : 0, ks = b - kKSteps * tb;
+                lds_dma16((tb ? ra1 : ra0) + ks * 64 + lq * 16, dst + b * kBlk);
+            }
         }
+    };
+    if (ntiles > 0) load_tile(0, 0);
+    if (ntiles > 1) load_tile(1, 1);
+
+    f32x4_t acc[HPW][16];
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb)
+#pragma unroll
+        for (int vb = 0; vb < 16; ++vb) acc[hb][vb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_ref[HPW], l_lane[HPW];
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb) {
+        m_ref[hb] = -INFINITY;
+        l_lane[hb] = 0.0f;
     }
 
-    for (int it = 0; it < ntiles; ++it) {
+    // V^T operand read offsets inside a tile (token half 0; half 1 is + 18 KB)
+    // lane (n = l16, lq) points at row 4 lq + n / 4, dims 16 vbg + 4 (n % 4)
+    const int tr_slot_row = 4 * lq + (l16 >> 2);
+    const int tr_lqp_lo = (l16 & 3) >> 1, tr_sub = 8 * (l16 & 1);
+
+    float s[HPW][8], mx[HPW];  // s[hb][tb * 4 + i]: token 16 tb + 4 lq + i of head h0 + 16 hb + l16
+    // scores of tile `it` (pair sum, scaled, masked) and their per-head max
+    auto score_tile = [&](int it) __attribute__((always_inline)) {
+        if (it + 1 < ntiles) {  // the loads of tile it + 1 may still be in flight
+            if (nl == NLmax)
+                wait_vm<NLmax>();
+            else
+                wait_vm<NLmax - 1>();
+        } else {
+            wait_vm<0>();
+        }
+        __builtin_amdgcn_s_barrier();  // tile `it` in LDS; tile it - 1 released
+        if (it + 2 < ntiles) load_tile(it + 2, (it + 2) % kNBuf);
+        const uint8_t* tile = tiles[it % kNBuf];
+        f32x4_t c[2][HPW];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int hb = 0; hb < HPW; ++hb) c[tb][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 9; ++j)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                const uint4 a = *(const uint4*)(tile + (tb * kKSteps + 9 * vh + j) * kBlk + L * 16);
+#pragma unroll
+                for (int hb = 0; hb < HPW; ++hb)
+                    c[tb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(Qb[hb][j]),
+                                                                        c[tb][hb], 0, 0, 0);
+            }
+        // swap the partials with the other wave of the pair; both waves add
+        // first-half + second-half, so they hold the same S^T
+        {
+            float4* mine = (float4*)(sx[w] + L * 8 * HPW);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int hb = 0; hb < HPW; ++hb)
+                    mine[tb * HPW + hb] = make_float4(c[tb][hb][0], c[tb][hb][1], c[tb][hb][2], c[tb][hb][3]);
+        }
+        wait_lds();
+        __builtin_amdgcn_s_barrier();
+        const float4* other = (const float4*)(sx[w ^ 1] + L * 8 * HPW);
         const int t0 = it * MT;
-        __syncthreads();  // tile `it` is in LDS
-        // ---- partial S over this wave's dims: sp[w][h][t] ----
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const uint8_t* krow = tile + (tb * 16 + l16) * RBP + lq * 16;
-            uint4 kb[5];
+        for (int hb = 0; hb < HPW; ++hb) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) kb[jj] = *(const uint4*)(krow + (4 * w + jj) * 64);
-            kb[4] = *(const uint4*)(krow + ks4 * 64);
+            for (int tb = 0; tb < 2; ++tb) {
+                const float4 o = other[tb * HPW + hb];
+                const float ov[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-                f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int jj = 0; jj < 5; ++jj)
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Qa[hb][jj]),
-                                                                as_bf16x8(kb[jj]), c, 0, 0, 0);
-                float* dst = &sp[w][(hb * 16 + lq * 4) * SPT + tb * 16 + l16];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dst[i * SPT] = c[i];
+                for (int i = 0; i < 4; ++i) {
+                    const float lo = vh ? ov[i] : c[tb][hb][i];
+                    const float hi = vh ? c[tb][hb][i] : ov[i];
+                    const int tok = t0 + 16 * tb + 4 * lq + i;
+                    s[hb][tb * 4 + i] = tok < npos ? (lo + hi) * sm_log2e : -INFINITY;
+                }
             }
-        }
-        __syncthreads();
-        // ---- online softmax: head h = 8w + l/8, tokens 4*(l%8) .. +4 ----
-        {
-            const int h = 8 * w + (l >> 3), tq = 4 * (l & 7);
-            const float4 a = *(const float4*)&sp[0][h * SPT + tq];
-            const float4 b = *(const float4*)&sp[1][h * SPT + tq];
-            const float4 c = *(const float4*)&sp[2][h * SPT + tq];
-            const float4 d = *(const float4*)&sp[3][h * SPT + tq];
-            float x[4] = {((a.x + b.x) + c.x) + d.x, ((a.y + b.y) + c.y) + d.y,
-                          ((a.z + b.z) + c.z) + d.z, ((a.w + b.w) + c.w) + d.w};
-            float mloc = -INFINITY;
+            float m = s[hb][0];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[e] = (rowp[t0 + tq + e] & 1ull) ? -INFINITY : x[e] * sm_log2e;
-                mloc = fmaxf(mloc, x[e]);
-            }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 1));
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 2));
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 4));
-            const float m_new = fmaxf(m_run, mloc);
-            const bool none = (m_new == -INFINITY);
-            const float alpha = none ? 1.0f : exp2f(m_run - m_new);
-            float p[4], lsum = 0.0f;
+            for (int e = 1; e < 8; ++e) m = fmaxf(m, s[hb][e]);
+            mx[hb] = max_xor32(max_xor16(m));
+        }
+    };
+    // probabilities against the reference, row sums, O^T += V^T P^T over this
+    // wave's 256 value dims
+    auto accumulate = [&](int it) __attribute__((always_inline)) {
+        const uint8_t* tile = tiles[it % kNBuf];
+        uint4 pb[HPW];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                p[e] = none ? 0.0f : exp2f(x[e] - m_new);
-                lsum += p[e];
-            }
-            lsum += __shfl_xor(lsum, 1);
-            lsum += __shfl_xor(lsum, 2);
-            lsum += __shfl_xor(lsum, 4);
-            l_run = l_run * alpha + lsum;
-            m_run = m_new;
-            *(uint2*)&pl[h][tq] = make_uint2((uint32_t)f2bf(p[0]) | ((uint32_t)f2bf(p[1]) << 16),
-                                             (uint32_t)f2bf(p[2]) | ((uint32_t)f2bf(p[3]) << 16));
-            if ((l & 7) == 0) alpha_s[h] = alpha;
-        }
-        __syncthreads();
-        // ---- O[:, 128w .. 128w+128) = O * alpha + P V ----
+        for (int hb = 0; hb < HPW; ++hb) {
+            float p[8];
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            const float4 a4 = *(const float4*)&alpha_s[hb * 16 + lq * 4];
-            const bf16x8_t pa = as_bf16x8(*(const uint4*)&pl[hb * 16 + l16][lq * 8]);
+            for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(s[hb][e] - m_ref[hb]);
+            pb[hb] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                                pack_bf16(p[6], p[7]));
+            // the sum uses the rounded weights the products use
+            float ls = 0.0f;
+            ls += bf16_lo(pb[hb].x) + bf16_hi(pb[hb].x);
+            ls += bf16_lo(pb[hb].y) + bf16_hi(pb[hb].y);
+            ls += bf16_lo(pb[hb].z) + bf16_hi(pb[hb].z);
+            ls += bf16_lo(pb[hb].w) + bf16_hi(pb[hb].w);
+            l_lane[hb] += ls;
+        }
 #pragma unroll
-            for (int vb = 0; vb < 8; ++vb) {
-                acc[hb][vb][0] *= a4.x;
-                acc[hb][vb][1] *= a4.y;
-                acc[hb][vb][2] *= a4.z;
-                acc[hb][vb][3] *= a4.w;
-                const int off0 = (lq * 8 + (l16 >> 2)) * RBP + (128 * w + vb * 16 + 4 * (l16 & 3)) * 2;
-                const uint2 lo = lds_tr16(tile, off0);
-                const uint2 hi = lds_tr16(tile, off0 + 4 * RBP);
-                const bf16x8_t vb8 = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-                acc[hb][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb8, acc[hb][vb], 0, 0, 0);
-            }
+        for (int vb = 0; vb < 16; ++vb) {
+            const int vbg = 16 * vh + vb;
+            const int off = (vbg >> 1) * kBlk + ((2 * (vbg & 1) + tr_lqp_lo) * 16 + tr_slot_row) * 16 + tr_sub;
+            const uint2 lo = lds_tr16(tile, off);
+            const uint2 hi = lds_tr16(tile, off + kKSteps * kBlk);
+            const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+            for (int hb = 0; hb < HPW; ++hb)
+                acc[hb][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(pb[hb]), acc[hb][vb], 0, 0, 0);
         }
-        __syncthreads();  // every wave is done with tile `it`
-        if (it + 1 < ntiles) {
-            {
-            u32x4_t* d_ = (u32x4_t*)ld_dst;
-            d_[0] = R0[0]; d_[8] = R0[1]; d_[16] = R0[2]; d_[24] = R0[3]; d_[32] = R0[4];
-            d_[40] = R0[5]; d_[48] = R0[6]; d_[56] = R0[7]; d_[64] = R0[8];
+    };
+
+    // The inner loop runs while no head's tile max exceeds its reference by
+    // more than the slack; such a tile (always the first) leaves it, the
+    // reference is raised and O^T, l rescaled outside, and the tile finished.
+    int it = 0;
+    while (it < ntiles) {
+        for (; it < ntiles; ++it) {
+            score_tile(it);
+            bool need = false;
+#pragma unroll
+            for (int hb = 0; hb < HPW; ++hb) need |= mx[hb] > m_ref[hb] + kRescaleSlack;
+            if (__builtin_amdgcn_ballot_w64(need) != 0) break;  // same in both waves of the pair
+            accumulate(it);
         }
-            if (it + 2 < ntiles) {
-                const int T0_ = t0 + 2 * MT;
-                {
-            gu32x4_t* src_ = (gu32x4_t*)((rowp[T0_ + ld_row] & ~15ull) + ld_col);
-            R0[0] = src_[0]; R0[1] = src_[8]; R0[2] = src_[16]; R0[3] = src_[24];
-            R0[4] = src_[32]; R0[5] = src_[40]; R0[6] = src_[48]; R0[7] = src_[56];
-            R0[8] = src_[64];
+        if (it == ntiles) break;
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) {
+            const float m_new = fmaxf(m_ref[hb], mx[hb]);
+            const float alpha = m_new == -INFINITY ? 1.0f : exp2f(m_ref[hb] - m_new);
+            m_ref[hb] = m_new;
+            l_lane[hb] *= alpha;
+#pragma unroll
+            for (int vb = 0; vb < 16; ++vb) acc[hb][vb] *= alpha;
         }
-            }
-        }
+        accumulate(it);
+        ++it;
     }
 
-    const int64_t hbase = ((int64_t)r * n_splits + split) * Hq + hg * MH;
+    // ---- partial outputs: O^T lane (head l16, lq) holds dims 16 vbg + 4 lq .. +4 ----
+    const int64_t hbase = ((int64_t)r * n_splits + split) * Hq + h0;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int hb = 0; hb < HPW; ++hb) {
+        float* dst = part_o + (hbase + hb * 16 + l16) * MDV + 256 * vh + 4 * lq;
 #pragma unroll
-        for (int vb = 0; vb < 8; ++vb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                part_o[(hbase + hb * 16 + lq * 4 + i) * MDV + 128 * w + vb * 16 + l16] = acc[hb][vb][i];
-    if ((l & 7) == 0) {
-        const int h = 8 * w + (l >> 3);
-        part_ml[(hbase + h) * 2 + 0] = m_run;
-        part_ml[(hbase + h) * 2 + 1] = l_run;
+        for (int vb = 0; vb < 16; ++vb)
+            *(float4*)(dst + 16 * vb) = make_float4(acc[hb][vb][0], acc[hb][vb][1], acc[hb][vb][2], acc[hb][vb][3]);
+        const float l = add_xor32(add_xor16(l_lane[hb]));
+        if (vh == 0 && lq == 0) {
+            part_ml[(hbase + hb * 16 + l16) * 2 + 0] = m_ref[hb];
+            part_ml[(hbase + hb * 16 + l16) * 2 + 1] = l;
+        }
     }
 }
 
@@ -403,76 +504,79 @@ __global__ __launch_bounds__(256) void k_attn_f32(GeomDev g, PosMap pm, const in
 }
 
 // ----------------------------------------------------------------------------
-// merge of the splits: one block per (request, head).  The split weights
-// 2^(m_s - m) and the total sum are formed once per block in a fixed order;
-// then each thread combines four columns at a time.
+// merge of the splits: one wave per (request, head, 128 value columns).  The
+// split weights 2^(m_s - m) and the total sum are formed by the wave in a
+// fixed order; then each lane combines two columns over all splits, in
+// split order, with up to 32 splits' loads in flight at once.
 // ----------------------------------------------------------------------------
 constexpr int kMergeMaxSplits = 1024;
+constexpr int kMergeCols = 128;
+constexpr int kMergeBatch = 32;
 
 template <int ODT>
-__global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_ml, int Hq,
-                                                    int Dv, int n_splits, void* __restrict__ out,
-                                                    float* __restrict__ lse) {
+__global__ __launch_bounds__(64) void k_attn_merge(const float* __restrict__ part_o,
+                                                   const float* __restrict__ part_ml, int Hq, int Dv,
+                                                   int n_splits, void* __restrict__ out,
+                                                   float* __restrict__ lse) {
     __shared__ float fac[kMergeMaxSplits];
-    __shared__ float s_m, s_inv, s_L;
-    const int rh = blockIdx.x;  // r * Hq + h
+    const int nchunk = (Dv + kMergeCols - 1) / kMergeCols;
+    const int rh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;  // rh = r * Hq + h
     const int r = rh / Hq, h = rh % Hq;
+    const int L = threadIdx.x;
     const int64_t b0 = (int64_t)r * n_splits * Hq + h;  // split s: (b0 + s*Hq)
-    // split weights in parallel; max and sum by a fixed-order tree
-    __shared__ float red[128];
+    const int v = chunk * kMergeCols + 2 * L;
+    const bool col = v < Dv;
+    const float* src = part_o + b0 * Dv + v;
+    const int64_t stride = (int64_t)Hq * Dv;
+    // the first batch of partial rows is requested before the split weights
+    // are formed, so both latencies overlap
+    float2 x[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+        if (col && u < n_splits) x[u] = *(const float2*)(src + (int64_t)u * stride);
     float m = -INFINITY;
-    for (int s = threadIdx.x; s < n_splits; s += blockDim.x)
-        m = fmaxf(m, part_ml[(b0 + (int64_t)s * Hq) * 2]);
-    red[threadIdx.x] = m;
-    __syncthreads();
-    for (int w = 64; w > 0; w >>= 1) {
-        if (threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
-        __syncthreads();
-    }
-    m = red[0];
-    __syncthreads();
+    for (int s = L; s < n_splits; s += 64) m = fmaxf(m, part_ml[(b0 + (int64_t)s * Hq) * 2]);
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     float part = 0.0f;
-    for (int s = threadIdx.x; s < n_splits; s += blockDim.x) {
+    for (int s = L; s < n_splits; s += 64) {
         const float ms = part_ml[(b0 + (int64_t)s * Hq) * 2];
         const float f = (ms == -INFINITY) ? 0.0f : exp2f(ms - m);
         fac[s] = f;
         part += part_ml[(b0 + (int64_t)s * Hq) * 2 + 1] * f;
     }
-    red[threadIdx.x] = part;
+    // fixed-order tree over the lanes
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+    const float Lsum = part, inv = 1.0f / part;
     __syncthreads();
-    for (int w = 64; w > 0; w >>= 1) {
-        if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-        s_m = m;
-        s_L = red[0];
-        s_inv = 1.0f / red[0];
-    }
-    __syncthreads();
-    const float inv = s_inv;
-    for (int v = 4 * threadIdx.x; v < Dv; v += 4 * blockDim.x) {
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-        for (int s = 0; s < n_splits; ++s) {
-            const float f = fac[s];
-            const float4 x = *(const float4*)&part_o[(b0 + (int64_t)s * Hq) * Dv + v];
-            o.x += f == 0.0f ? 0.0f : x.x * f;
-            o.y += f == 0.0f ? 0.0f : x.y * f;
-            o.z += f == 0.0f ? 0.0f : x.z * f;
-            o.w += f == 0.0f ? 0.0f : x.w * f;
-        }
-        const float ov[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+    if (col) {
+        float ox = 0.0f, oy = 0.0f;
+        for (int s0 = 0; s0 < n_splits; s0 += kMergeBatch) {
+            if (s0 > 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if constexpr (ODT == LSA_F32)
-                ((float*)out)[(int64_t)rh * Dv + v + e] = ov[e];
-            else
-                ((uint16_t*)out)[(int64_t)rh * Dv + v + e] = f2bf(ov[e]);
+                for (int u = 0; u < kMergeBatch; ++u)
+                    if (s0 + u < n_splits) x[u] = *(const float2*)(src + (int64_t)(s0 + u) * stride);
+            }
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                if (s0 + u < n_splits) {
+                    const float f = fac[s0 + u];
+                    if (f != 0.0f) {
+                        ox += x[u].x * f;
+                        oy += x[u].y * f;
+                    }
+                }
+            }
+        }
+        // element stores: the output pointer carries no alignment promise
+        if constexpr (ODT == LSA_F32) {
+            ((float*)out)[(int64_t)rh * Dv + v] = ox * inv;
+            ((float*)out)[(int64_t)rh * Dv + v + 1] = oy * inv;
+        } else {
+            ((uint16_t*)out)[(int64_t)rh * Dv + v] = f2bf(ox * inv);
+            ((uint16_t*)out)[(int64_t)rh * Dv + v + 1] = f2bf(oy * inv);
         }
     }
-    if (lse && threadIdx.x == 0) lse[rh] = (s_m + __log2f(s_L)) * kLn2;
+    if (lse && chunk == 0 && L == 0) lse[rh] = (m + __log2f(Lsum)) * kLn2;
 }
 
 }  // namespace
@@ -485,28 +589,25 @@ lsa_status attn_plan(const GeomDev& g, const lsa_kv_layout* kv, int Hq, int k, i
     AttnPlan p{};
     p.P_max = P;
     if (kv->kv_dtype == LSA_BF16) {
-        if (kv->Dk != MDK || kv->Dv != MDV || kv->v_off != 0 || Hq % MH != 0 ||
+        if (kv->Dk != MDK || kv->Dv != MDV || kv->v_off != 0 || Hq % 32 != 0 ||
             kv->row_bytes % 16 != 0 || kv->page_bytes % 16 != 0)
             return LSA_ERR_UNSUPPORTED;
         p.mode = 1;
-        p.head_groups = Hq / MH;
+        p.waves = Hq % 64 == 0 ? 8 : 4;  // 16 heads per wave: 64 or 32 heads per block
+        p.head_groups = Hq / (8 * p.waves);
         const int tile = MT;
         int S = n_splits;
         if (S <= 0) {
-            // about two blocks per CU over 256 CUs, at least 2 tiles per split
-            const int want = (512 + g.B * p.head_groups - 1) / (g.B * p.head_groups);
+            // one block per CU over 256 CUs, at least 2 tiles per split
+            const int want = (256 + g.B * p.head_groups - 1) / (g.B * p.head_groups);
             const int max_by_len = (P + 2 * tile - 1) / (2 * tile);
             S = want < max_by_len ? want : max_by_len;
             if (S < 1) S = 1;
         }
         int per = (P + S - 1) / S;
         per = (per + tile - 1) / tile * tile;
-        if (per > kMaxSplitPos) {
-            per = kMaxSplitPos;
-            S = (P + per - 1) / per;
-        }
-        S = (P + per - 1) / per;
-        p.n_splits = S;
+        if (per > kMaxSplitPos) per = kMaxSplitPos;
+        p.n_splits = (P + per - 1) / per;
         p.per_split = per;
     } else if (kv->kv_dtype == LSA_F32) {
         if (Hq > FMAXH || kv->Dk > FMAXD || kv->Dv > FMAXD || kv->Dk % 4 || kv->Dv % 4 ||
@@ -548,9 +649,14 @@ hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, in
         const int units = g.B * plan.n_splits;
         const int grid = (units + 7) / 8 * 8 * plan.head_groups;
         timing_begin("k_attn_mla", s);
-        hipLaunchKernelGGL(k_attn_mla, dim3(grid), dim3(256), 0, s, g, pm, tcnt,
-                           (const uint16_t*)q, Hq, plan.n_splits, plan.per_split,
-                           plan.head_groups, sm_log2e, part_o, part_ml);
+        if (plan.waves == 8)
+            hipLaunchKernelGGL((k_attn_mla<8, 1>), dim3(grid), dim3(512), 0, s, g, pm, tcnt,
+                               (const uint16_t*)q, Hq, plan.n_splits, plan.per_split,
+                               plan.head_groups, sm_log2e, part_o, part_ml);
+        else
+            hipLaunchKernelGGL((k_attn_mla<4, 1>), dim3(grid), dim3(256), 0, s, g, pm, tcnt,
+                               (const uint16_t*)q, Hq, plan.n_splits, plan.per_split,
+                               plan.head_groups, sm_log2e, part_o, part_ml);
         timing_end("k_attn_mla", s);
     } else {
         timing_begin("k_attn_f32", s);
@@ -561,12 +667,13 @@ hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, in
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const int nchunk = (kv.Dv + kMergeCols - 1) / kMergeCols;
     timing_begin("k_attn_merge", s);
     if (kv.kv_dtype == LSA_F32)
-        hipLaunchKernelGGL(k_attn_merge<LSA_F32>, dim3(g.B * Hq), dim3(128), 0, s, part_o,
+        hipLaunchKernelGGL(k_attn_merge<LSA_F32>, dim3(g.B * Hq * nchunk), dim3(64), 0, s, part_o,
                            part_ml, Hq, kv.Dv, plan.n_splits, out, lse);
     else
-        hipLaunchKernelGGL(k_attn_merge<LSA_BF16>, dim3(g.B * Hq), dim3(128), 0, s, part_o,
+        hipLaunchKernelGGL(k_attn_merge<LSA_BF16>, dim3(g.B * Hq * nchunk), dim3(64), 0, s, part_o,
                            part_ml, Hq, kv.Dv, plan.n_splits, out, lse);
     timing_end("k_attn_merge", s);
     return hipGetLastError();

@@ -46,6 +46,7 @@ struct AttnPlan {
     int n_splits;    // splits per request
     int per_split;   // positions per split (multiple of the tile)
     int head_groups; // WGs per (request, split) along heads
+    int waves;       // waves per WG (mode 1)
     int P_max;       // k + max recent
     size_t part_o_bytes, part_ml_bytes;
 };

@@ -121,7 +121,8 @@ lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc) {
     if (desc->d != 64 && desc->d != 128) return LSA_ERR_UNSUPPORTED;
     if (desc->H < 1 || desc->H > 128 || desc->k < 1 || desc->Hq < 1) return LSA_ERR_INVALID_ARG;
     if (desc->q_dt != LSA_F32 && desc->q_dt != LSA_BF16) return LSA_ERR_UNSUPPORTED;
-    if (!desc->pool || !desc->recent || !desc->ws) return LSA_ERR_INVALID_ARG;
+    if (!desc->pool || !desc->recent || !desc->ws || ((uintptr_t)desc->ws & 15u))
+        return LSA_ERR_INVALID_ARG;
     if (desc->idx_dt == LSA_FP8_E4M3FN && !desc->ikey_scale && g.chunk_off[g.B] > 0)
         return LSA_ERR_INVALID_ARG;
     if (desc->kv.ikey_off % 16 || desc->kv.page_bytes % 16) return LSA_ERR_INVALID_ARG;
