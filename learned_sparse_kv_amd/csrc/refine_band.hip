@@ -182,6 +182,24 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
     for (int i = tid; i < 2 * kCoarse; i += 64 * kWaves) hl[i] = 0;
     __syncthreads();
     if ((int)blockIdx.x * kWaves < nc) {  // uniform across the block
+        const int64_t off = g.chunk_off[r];
+        const int stride = X * kWaves;
+        const int i0 = blockIdx.x * kWaves + wv;  // this wave's chunks: i0 + j * stride
+        const int nj = i0 < nc ? (nc - i0 + stride - 1) / stride : 0;
+        // chunk j0 + lane: page (slot) index and scale, 64 chunks at a time
+        int64_t pg_l = 0;
+        float sc_l = 1.0f;
+        auto load_idx = [&](int j0) __attribute__((always_inline)) {
+            if (j0 + lane < nj) {
+                const int c = sel[off + i0 + (j0 + lane) * stride];
+                pg_l = page_table ? (int64_t)page_table[off + c] : off + c;
+                if constexpr (KDT == LSA_FP8_E4M3FN) sc_l = ikey_scale[off + c];
+            }
+        };
+        // the dependent index loads go first, the query operands load behind
+        // them, the first key rows as soon as their pages are known, and the
+        // query norms are formed while the key rows are in flight
+        if (nj > 0) load_idx(0);
         uint4 qb[HB][KS];
         float wl[HB], wa[HB];
         const uint16_t* qr = q + (int64_t)r * H * D;
@@ -191,13 +209,33 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
             for (int ks = 0; ks < KS; ++ks)
                 qb[hb][ks] = *(const uint4*)(qr + (hb * 16 + l16) * D + kdim<KDT>(ks, lq));
             wl[hb] = w[(int64_t)r * H + hb * 16 + l16];
-            wa[hb] = fabsf(wl[hb]);
+        }
+        // key rows of chunk j: A operands of tokens tb*16 + l16 (16 bytes per
+        // load); DEPTH chunks are in flight ahead of the one computed (two
+        // where the registers allow it)
+        constexpr int DEPTH = NR * 4 * 4 <= 32 ? 2 : 1;
+        uint4 raw[4][NR], raw2[4][NR];
+        auto fetch = [&](int j, uint4 (&dst)[4][NR]) __attribute__((always_inline)) {
+            const int src = j & 63;
+            const int64_t pgo = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pg_l, src) |
+                                ((int64_t)__builtin_amdgcn_readlane((int)(pg_l >> 32), src) << 32);
+            const uint8_t* base = pages + pgo * page_bytes + ikey_off;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int n = 0; n < NR; ++n)
+                    dst[tb][n] = *(const uint4*)(base + (tb * 16 + l16) * ROWB + n * 64 + lq * 16);
+        };
+        if (nj > 0) {
+            fetch(0, raw);
+            if (DEPTH == 2 && nj > 1) fetch(1, raw2);
         }
         // Wq = sum_h |w_h| * |q_h|_2 (rounded up), from the operands held:
         // lane (l16, lq) has dims lq*8.. of every k-step of head hb*16 + l16
         float part = 0.0f;
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
+            wa[hb] = fabsf(wl[hb]);
             float ss = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) ss += sumsq_bf16x8(qb[hb][ks]);
@@ -209,37 +247,6 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
         for (int o = 1; o < 16; o <<= 1) part += __shfl_xor(part, o);
         const float wq = part * (1.0f + gam(H + 8));
 
-        const int64_t off = g.chunk_off[r];
-        const int stride = X * kWaves;
-        const int i0 = blockIdx.x * kWaves + wv;  // this wave's chunks: i0 + j * stride
-        const int nj = i0 < nc ? (nc - i0 + stride - 1) / stride : 0;
-        // chunk j0 + lane: page (slot) index and scale, 64 chunks at a time
-        int64_t pg_l = 0;
-        float sc_l = 1.0f;
-        auto load_idx = [&](int j0) {
-            if (j0 + lane < nj) {
-                const int c = sel[off + i0 + (j0 + lane) * stride];
-                pg_l = page_table ? (int64_t)page_table[off + c] : off + c;
-                if constexpr (KDT == LSA_FP8_E4M3FN) sc_l = ikey_scale[off + c];
-            }
-        };
-        uint4 raw[4][NR];
-        // key rows of chunk j: A operands of tokens tb*16 + l16 (16 bytes per load)
-        auto fetch = [&](int j) {
-            const int src = j & 63;
-            const int64_t pgo = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pg_l, src) |
-                                ((int64_t)__builtin_amdgcn_readlane((int)(pg_l >> 32), src) << 32);
-            const uint8_t* base = pages + pgo * page_bytes + ikey_off;
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                for (int n = 0; n < NR; ++n)
-                    raw[tb][n] = *(const uint4*)(base + (tb * 16 + l16) * ROWB + n * 64 + lq * 16);
-        };
-        if (nj > 0) {
-            load_idx(0);
-            fetch(0);
-        }
         float* pr = red[wv];
         for (int j = 0; j < nj; ++j) {
             const int i = i0 + j * stride;
@@ -253,9 +260,22 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
                                                : fp8x8_to_bf16x8(raw[tb][ks >> 1].x, raw[tb][ks >> 1].y);
                 }
             const float scale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), j & 63));
-            if (j + 1 < nj) {
+            if constexpr (DEPTH == 2) {
+                if (j + 1 < nj) {
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                        for (int n = 0; n < NR; ++n) raw[tb][n] = raw2[tb][n];
+                    if (j + 2 < nj) {
+                        // the index window moves 64 chunks at a time; its scales
+                        // are read for chunk j above, so it may move now
+                        if (((j + 2) & 63) == 0) load_idx(j + 2);
+                        fetch(j + 2, raw2);
+                    }
+                }
+            } else if (j + 1 < nj) {
                 if (((j + 1) & 63) == 0) load_idx(j + 1);
-                fetch(j + 1);
+                fetch(j + 1, raw);
             }
             // |key|^2 on the matrix cores: the diagonal of the 16x16 Gram block
             // of tokens tb*16..; lane (l16, lq) holds rows 4lq..4lq+3 of column l16
