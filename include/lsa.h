@@ -293,7 +293,7 @@ lsa_status lsa_step64(lsa_ctx* ctx, const lsa_window_in* in, lsa_window_out* out
  * the recorded events and returns, for one kernel name (k_fuse_query,
  * k_score, k_select, k_refine, k_topk, k_refine_mfma, k_band_fine,
  * k_band_list, k_topk_band, k_attn_mla, k_attn_f32, k_attn_merge,
- * k_gather), the number of timed launches and their summed duration in
+ * k_gather, k_stream_read), the number of timed launches and their summed duration in
  * milliseconds since the last reset.  lsa_timing_only(name) restricts the
  * timing to that one kernel (NULL: all; a name of 64 or more characters is
  * LSA_ERR_INVALID_ARG), so that one kernel can be timed inside a run with
@@ -303,6 +303,16 @@ lsa_status lsa_timing_enable(int32_t on);
 lsa_status lsa_timing_only(const char* kernel);
 void lsa_timing_reset(void);
 lsa_status lsa_timing_read(const char* kernel, int64_t* launches, double* total_ms);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics: achievable read bandwidth.  Reads `bytes` of device memory at
+ * src (16-byte aligned, a multiple of 16) with a plain streaming kernel
+ * (k_stream_read) and writes nothing but, practically never, one word to
+ * sink (device, 4 bytes).  Time it with lsa_timing_* or events: bytes over
+ * its duration is the read bandwidth a simple kernel reaches on this GPU,
+ * the reference line for the HBM figures of the kernels above.
+ * ---------------------------------------------------------------------- */
+lsa_status lsa_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

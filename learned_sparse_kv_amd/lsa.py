@@ -102,6 +102,7 @@ def _load():
         "lsa_timing_only": ([C.c_char_p], I),
         "lsa_timing_reset": ([], None),
         "lsa_timing_read": ([C.c_char_p, C.POINTER(I64), C.POINTER(C.c_double)], I),
+        "lsa_stream_read": ([P, SZ, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -282,7 +283,7 @@ def lsa_step64(ctx: Ctx, win, out, main=None, copy=None):
 # ---------------------------------------------------------------- diagnostics
 KERNELS = ("k_fuse_query", "k_score", "k_select", "k_refine", "k_topk", "k_refine_mfma",
            "k_band_fine", "k_band_list", "k_topk_band", "k_attn_mla", "k_attn_f32", "k_attn_merge",
-           "k_gather")
+           "k_gather", "k_stream_read")
 
 
 def lsa_timing_enable(on: bool):
@@ -301,3 +302,7 @@ def lsa_timing_read(kernel: str):
     n, ms = C.c_int64(), C.c_double()
     _check("lsa_timing_read", _lib.lsa_timing_read(kernel.encode(), C.byref(n), C.byref(ms)))
     return int(n.value), float(ms.value)
+
+
+def lsa_stream_read(src, nbytes: int, sink, stream=None):
+    _check("lsa_stream_read", _lib.lsa_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
