@@ -184,6 +184,7 @@ def seq_lens_of(cfg: LsaConfig):
 # generation
 # ----------------------------------------------------------------------------
 _T_KIC, _T_PLANT, _T_QC, _T_IKEY, _T_KVH, _T_KVR, _T_QR, _T_QA, _T_DRIFT = range(9)
+_T_LAYER = 100  # tensor ids of indexer layer l >= 1: _T_LAYER + 10 l + {0: KIComp, 1: planted, 2: query}
 
 
 def _rng(root: np.random.SeedSequence, tensor: int, req: int = 0):
@@ -318,3 +319,41 @@ def small_config(name="small_bf16", seed=11, seq_lens=(5000, 3000), window=1024,
                      q_dtype=(F32 if kv == F32 else BF16) if q_dtype is None else q_dtype,
                      idx_dtype=idx, planted=planted, topk=topk, Hq=Hq, Dk=Dk, Dv=Dv,
                      kv_dtype=kv, separate_v=separate_v, steps=steps)
+
+
+def indexer_layers(inp: Inputs, n_layers: int = 3, window: int = 0):
+    """Coarse-indexer inputs of n_layers independent memory indexers (the
+    pages place three, at layers 10, 12 and 20).  Layer 0 is the inputs' own
+    indexer; layer l >= 1 draws its own coarse query (same law), its own
+    KIComp noise, and its own planted chunks (same rate, drawn independently,
+    so the layers' selections overlap only partly).  Returns a list of dicts
+    with q_coarse, w_coarse, bias, kic, kic_scale for the given window."""
+    cfg = inp.cfg
+    B, H, d = cfg.batch, cfg.H, cfg.d
+    chunk_off, n_hist = inp["chunk_off"], inp["n_hist"]
+    NH = int(chunk_off[-1])
+    root = np.random.SeedSequence(cfg.seed)
+    layers = [dict(q_coarse=inp["q_coarse"], w_coarse=inp["w_coarse"], bias=inp["bias"],
+                   kic=inp["kic_windows"][window], kic_scale=inp["kic_scale_windows"][window])]
+    for l in range(1, n_layers):
+        t = _T_LAYER + 10 * l
+        q_raw = np.stack([_normal(_rng(root, t + 2, r), (H, d), std=np.sqrt(H / 4.0)) for r in range(B)])
+        q_enc = encode(q_raw, cfg.q_dtype)
+        w = np.full((B, H), 1.0 / H, dtype=np.float32)
+        qv = decode_query_f64(q_enc, cfg.q_dtype)
+        u = np.einsum("bh,bhd->bd", w.astype(np.float64), qv)
+        u /= np.linalg.norm(u, axis=1, keepdims=True)
+        rows = np.zeros((NH, d), dtype=np.float32)
+        for r in range(B):
+            n = int(n_hist[r])
+            rows[chunk_off[r]:chunk_off[r + 1]] = _normal(_rng(root, t, r), (n, d), std=1.0 / np.sqrt(d))
+            if n:
+                pl = np.sort(_rng(root, t + 1, r).choice(n, size=int(round(cfg.planted * n)), replace=False))
+                rows[chunk_off[r] + pl] += (2.0 * u[r]).astype(np.float32)
+        if cfg.idx_dtype == FP8:
+            enc, sc = to_fp8_blocks(rows)
+        else:
+            enc, sc = encode(rows, cfg.idx_dtype), np.ones(NH, np.float32)
+        layers.append(dict(q_coarse=q_enc, w_coarse=w, bias=np.full((B,), -1.0, dtype=np.float32),
+                           kic=enc, kic_scale=sc))
+    return layers

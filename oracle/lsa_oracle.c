@@ -181,6 +181,60 @@ int lsao_score_select(const lsao_batch* b, const void* q, const float* w, const 
     return 0;
 }
 
+/* OR-mode union over indexer layers.  Independent memory indexers sit at
+ * several layers (three: 10, 12 and 20); at inference a chunk is recalled
+ * when any of them scores it above 0.5 (cjcn.com.cn explainer, section 四;
+ * gist.science summary, section 2.4 "Optimale Konfiguration").  Each layer
+ * l has its own query state, head weights, bias and KIComp rows; its logits
+ * follow the single-layer definition above in the same fp32 order.  The
+ * per-chunk masks (z_l > theta) are OR-ed before one ordered compaction.
+ * zmax[c] = max_l z_l[c] (so zmax > theta exactly when the OR mask is set).
+ * kic[l], kic_scale[l] replace b->kic, b->kic_scale. */
+int lsao_score_select_union(const lsao_batch* b, int32_t n_layers, const void* const* q,
+                            const float* const* w, const float* const* bias,
+                            const void* const* kic, const float* const* kic_scale, float theta,
+                            float* zmax, int32_t* sel, int32_t* cnt) {
+    if (n_layers < 1) return -1;
+    int64_t chunk0 = 0;
+    float* qbar = (float*)malloc(sizeof(float) * (size_t)b->d * (size_t)n_layers);
+    if (!qbar) return -1;
+    for (int32_t r = 0; r < b->B; r++) {
+        int64_t g[3];
+        lsao_geometry(b->seq_len[r], b->C, b->W, g);
+        const int64_t N = g[1];
+        for (int32_t l = 0; l < n_layers; l++)
+            for (int32_t i = 0; i < b->d; i++) {
+                float acc = 0.0f;
+                for (int32_t h = 0; h < b->H; h++)
+                    acc = fmaf(w[l][(int64_t)r * b->H + h],
+                               o_elem(b->q_dt, q[l], ((int64_t)r * b->H + h) * b->d + i), acc);
+                qbar[(int64_t)l * b->d + i] = acc;
+            }
+        int32_t n_sel = 0;
+        for (int64_t c = 0; c < N; c++) {
+            const int64_t row = chunk0 + c;
+            int any = 0;
+            float zm = 0.0f;
+            for (int32_t l = 0; l < n_layers; l++) {
+                float acc = 0.0f;
+                for (int32_t i = 0; i < b->d; i++)
+                    acc = fmaf(qbar[(int64_t)l * b->d + i], o_elem(b->idx_dt, kic[l], row * b->d + i),
+                               acc);
+                const float s = (b->idx_dt == O_FP8) ? kic_scale[l][row] : 1.0f;
+                const float z = fmaf(s, acc, bias[l][r]);
+                any |= (z > theta);
+                zm = (l == 0 || z > zm) ? z : zm;
+            }
+            zmax[row] = zm;
+            if (any) sel[chunk0 + n_sel++] = (int32_t)c;
+        }
+        cnt[r] = n_sel;
+        chunk0 += N;
+    }
+    free(qbar);
+    return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* O6-O8: candidate tokens, lightning refine score, top-k              */
 /* ------------------------------------------------------------------ */

@@ -55,6 +55,8 @@ def load(path: str):
     _lib.lsao_geometry.argtypes = [I32, I32, I32, P]
     _lib.lsao_score_select.argtypes = [C.POINTER(Batch), P, P, P, F, P, P, P]
     _lib.lsao_score_select.restype = C.c_int
+    _lib.lsao_score_select_union.argtypes = [C.POINTER(Batch), I32, P, P, P, P, P, F, P, P, P]
+    _lib.lsao_score_select_union.restype = C.c_int
     _lib.lsao_refine_topk.argtypes = [C.POINTER(Batch), I32, P, I32, P, P, I32, P, P]
     _lib.lsao_refine_topk.restype = I32
     _lib.lsao_attend.argtypes = [C.POINTER(Batch), I32, P, I32, P, D, P, P]
@@ -125,6 +127,26 @@ class Oracle:
                                      np.float32(theta), _p(z), _p(sel), _p(cnt))
         assert rc == 0
         return z[:self.n_total], sel[:self.n_total], cnt
+
+    def score_select_union(self, layers, theta: float = 0.0):
+        """OR-mode union over indexer layers.  layers: list of dicts with
+        q_coarse, w_coarse, bias, kic, kic_scale.  Returns (zmax, sel, cnt)."""
+        n = max(self.n_total, 1)
+        keep = [{k: np.ascontiguousarray(v) for k, v in lay.items()} for lay in layers]
+        for lay in keep:
+            lay["w_coarse"] = np.ascontiguousarray(lay["w_coarse"], dtype=np.float32)
+            lay["bias"] = np.ascontiguousarray(lay["bias"], dtype=np.float32)
+            lay["kic_scale"] = np.ascontiguousarray(lay["kic_scale"], dtype=np.float32)
+        nl = len(keep)
+        arr = lambda key: (C.c_void_p * nl)(*[_p(lay[key]) for lay in keep])
+        zmax = np.zeros(n, np.float32)
+        sel = np.full(n, -1, np.int32)
+        cnt = np.zeros(self.cfg.batch, np.int32)
+        rc = lib().lsao_score_select_union(C.byref(self.batch), nl, arr("q_coarse"), arr("w_coarse"),
+                                           arr("bias"), arr("kic"), arr("kic_scale"), np.float32(theta),
+                                           _p(zmax), _p(sel), _p(cnt))
+        assert rc == 0
+        return zmax[:self.n_total], sel[:self.n_total], cnt
 
     def refine_topk(self, r: int, sel_r, q_r, w_r, k: int, want_scores=False):
         sel_r = np.ascontiguousarray(sel_r, dtype=np.int32)

@@ -39,6 +39,11 @@ MUTATIONS = {
                            "int64_t rs = (int64_t)C * ((h + C - 1) / C);"),
     "fp8_bias_8": ("ldexpf(1.0f + (float)m / 8.0f, e - 7)", "ldexpf(1.0f + (float)m / 8.0f, e - 8)"),
     "fp8_subnormal": ("ldexpf((float)m / 8.0f, -6)", "ldexpf((float)m / 8.0f, -7)"),
+    "union_and_mode": ("any |= (z > theta);", "any = (l == 0) ? (z > theta) : (any & (z > theta));"),
+    "union_last_layer_skipped": ("for (int32_t l = 0; l < n_layers; l++) {\n                float acc",
+                                 "for (int32_t l = 0; l < n_layers - 1; l++) {\n                float acc"),
+    "union_keys_of_layer0": ("o_elem(b->idx_dt, kic[l], row * b->d + i)", "o_elem(b->idx_dt, kic[0], row * b->d + i)"),
+    "union_query_of_layer0": ("acc = fmaf(qbar[(int64_t)l * b->d + i],", "acc = fmaf(qbar[i],"),
 }
 
 PIN_CALLS = [
@@ -54,6 +59,8 @@ PIN_CALLS = [
     "p.test_full_selection_equals_dense_attention('f32_sep')",
     "p.test_no_selection_equals_sliding_window_attention()",
     "p.test_attention_closed_forms()",
+    "p.test_union_is_union_of_single_layers(1)",
+    "p.test_union_special_cases()",
 ]
 
 RUNNER = """

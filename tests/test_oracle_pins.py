@@ -348,3 +348,50 @@ def test_generator_selection_rate_cfg0():
     leak = len(chosen - planted) / (n - len(planted))
     assert 0.0 <= leak < 0.08
     assert 0.10 <= cnt[0] / n <= 0.20
+
+
+# ------------------------------------------------ NEXT-1 OR-union over layers
+def _single_layer(inp, lay, theta=0.0):
+    o = oracle.Oracle(inp, kic=lay["kic"], kic_scale=lay["kic_scale"])
+    return o.score_select(theta=theta, q=lay["q_coarse"], w=lay["w_coarse"], bias=lay["bias"])
+
+
+@pytest.mark.parametrize("idx", [synth.F32, synth.BF16, synth.FP8])
+def test_union_is_union_of_single_layers(idx):
+    """The OR-mode union equals the set union of the three single-layer
+    selections, and its logit is the per-chunk max of theirs, bitwise."""
+    inp = synth.generate(synth.small_config(seq_lens=(9000, 4000), idx=idx, H=4, d=64))
+    lays = synth.indexer_layers(inp, 3)
+    zm, sel, cnt = oracle.Oracle(inp).score_select_union(lays)
+    singles = [_single_layer(inp, lay) for lay in lays]
+    assert np.array_equal(zm.view(np.uint32),
+                          np.maximum.reduce([s[0] for s in singles]).view(np.uint32))
+    for r in range(inp.cfg.batch):
+        c0 = inp["chunk_off"][r]
+        want = sorted(set().union(*[set(s[1][c0:c0 + s[2][r]].tolist()) for s in singles]))
+        assert sel[c0:c0 + cnt[r]].tolist() == want
+        # the union is strictly larger than every single layer here
+        assert all(cnt[r] > s[2][r] for s in singles)
+
+
+def test_union_special_cases():
+    inp = synth.generate(synth.small_config(seq_lens=(9000, 4000), H=4, d=64))
+    lays = synth.indexer_layers(inp, 3)
+    o = oracle.Oracle(inp)
+    z0, sel0, cnt0 = _single_layer(inp, lays[0])
+    # one layer, and three copies of it: the single-layer selection, bitwise
+    for group in ([lays[0]], [lays[0]] * 3):
+        zm, sel, cnt = o.score_select_union(group)
+        assert np.array_equal(zm.view(np.uint32), z0.view(np.uint32))
+        assert np.array_equal(cnt, cnt0)
+        assert all(np.array_equal(sel[c:c + n], sel0[c:c + n]) for c, n in zip(inp["chunk_off"], cnt0))
+    # a layer that never fires changes nothing
+    dead = dict(lays[2], bias=np.full_like(lays[2]["bias"], -1e30))
+    _, sel_a, cnt_a = o.score_select_union(lays[:2])
+    _, sel_b, cnt_b = o.score_select_union(lays[:2] + [dead])
+    assert np.array_equal(cnt_a, cnt_b)
+    assert all(np.array_equal(sel_a[c:c + n], sel_b[c:c + n]) for c, n in zip(inp["chunk_off"], cnt_a))
+    # thresholds at the ends
+    _, _, cnt_none = o.score_select_union(lays, theta=float("inf"))
+    _, _, cnt_all = o.score_select_union(lays, theta=float("-inf"))
+    assert (cnt_none == 0).all() and list(cnt_all) == list(inp["n_hist"])
