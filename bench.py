@@ -171,10 +171,12 @@ def hbm_calibration(nbytes=1 << 30, reps=5):
             "stream_read_gbs": round(nbytes / stream_s / 1e9, 1)}
 
 
-def sustained_scoring(label, B, L, idx_dt, H=64, d=128, window=8192, seed=0, reps=3):
+def sustained_scoring(label, B, L, idx_dt, H=64, d=128, window=8192, seed=0, reps=3, layers=1):
     """lsa_score_chunks + lsa_select_threshold over many distinct KIComp buffers
     (together more than twice the 256 MB last-level cache), so every launch
-    streams cold lines: B requests of L tokens each, one launch per trigger."""
+    streams cold lines: B requests of L tokens each, one launch per trigger.
+    layers > 1: the OR-mode union over that many indexer layers
+    (lsa_score_chunks_union), each layer reading its own buffer."""
     import math
     import numpy as np
     import torch
@@ -197,7 +199,9 @@ def sustained_scoring(label, B, L, idx_dt, H=64, d=128, window=8192, seed=0, rep
             kic.append(x.to(torch.bfloat16).view(torch.int16))
             ksc.append(None)
         del x
-    q = (torch.randn(B, H, d, generator=gen, device="cuda") * (H / 4) ** 0.5).to(torch.bfloat16).view(torch.int16)
+    qs = [(torch.randn(B, H, d, generator=gen, device="cuda") * (H / 4) ** 0.5).to(torch.bfloat16).view(torch.int16)
+          for _ in range(layers)]
+    q = qs[0]
     w = torch.full((B, H), 1.0 / H, device="cuda")
     bias = torch.full((B,), -1.0, device="cuda")
     z = torch.empty(nh, device="cuda")
@@ -206,7 +210,12 @@ def sustained_scoring(label, B, L, idx_dt, H=64, d=128, window=8192, seed=0, rep
     ws = torch.empty(max(lsa.lsa_score_ws_bytes(g, d), 256), dtype=torch.uint8, device="cuda")
 
     def trig(b):
-        lsa.lsa_score_chunks(g, q, synth.BF16, w, bias, H, d, kic[b], idx_dt, ksc[b], z, ws)
+        if layers == 1:
+            lsa.lsa_score_chunks(g, q, synth.BF16, w, bias, H, d, kic[b], idx_dt, ksc[b], z, ws)
+        else:
+            bs = [(b + l) % nbuf for l in range(layers)]
+            lsa.lsa_score_chunks_union(g, qs, synth.BF16, [w] * layers, [bias] * layers, H, d,
+                                       [kic[x] for x in bs], idx_dt, [ksc[x] for x in bs], z, ws)
         lsa.lsa_select_threshold(g, z, 0.0, sel, cnt)
 
     for b in range(nbuf):
@@ -222,15 +231,16 @@ def sustained_scoring(label, B, L, idx_dt, H=64, d=128, window=8192, seed=0, rep
     t = {n: lsa.lsa_timing_read(n) for n in ("k_fuse_query", "k_score", "k_select")}
     lsa.lsa_timing_reset()
     us = {n: (ms * 1e3 / c if c else None) for n, (c, ms) in t.items()}
-    gbs = per / (us["k_score"] * 1e-6) / 1e9
+    gbs = per / (us["k_score"] * 1e-6) / 1e9  # per layer launch
+    trig_us = sum(ms for (c, ms) in t.values()) * 1e3 / (reps * nbuf)
     del kic, ksc
     torch.cuda.empty_cache()
     return {"label": label, "batch": B, "context": L,
-            "index_keys": "fp8_e4m3fn" if idx_dt == synth.FP8 else "bf16",
-            "bytes_per_trigger": per, "distinct_buffers": nbuf, "launches": reps * nbuf,
+            "index_keys": "fp8_e4m3fn" if idx_dt == synth.FP8 else "bf16", "indexer_layers": layers,
+            "bytes_per_trigger": per * layers, "distinct_buffers": nbuf, "launches": reps * nbuf * layers,
             "k_score_us": round(us["k_score"], 2), "gbs": round(gbs, 1),
             "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
-            "trigger_us": round(sum(v for v in us.values() if v), 2)}
+            "trigger_us": round(trig_us, 2)}
 
 
 def sustained_attention(label, B, L, nbatch=6, reps=3, k=2048, Hq=64, Dk=576, Dv=512,
@@ -471,7 +481,8 @@ def main():
         result["hbm_calibration"] = hbm_calibration()
         result["scoring_sustained"] = [
             sustained_scoring("500k", 64, 512000, synth.FP8, seed=101),
-            sustained_scoring("128k", 64, 131072, synth.BF16, seed=102)]
+            sustained_scoring("128k", 64, 131072, synth.BF16, seed=102),
+            sustained_scoring("500k_union3", 64, 512000, synth.FP8, seed=106, layers=3)]
         result["attention_sustained"] = [
             sustained_attention("500k", 4, 512000, seed=103),
             sustained_attention("500k_b8", 8, 512000, seed=104),

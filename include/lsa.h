@@ -58,6 +58,7 @@ extern "C" {
 #endif
 
 #define LSA_MAX_BATCH 64
+#define LSA_MAX_LAYERS 8   /* indexer layers of lsa_score_chunks_union */
 #define LSA_CHUNK 64
 
 typedef enum {
@@ -116,6 +117,27 @@ lsa_status lsa_score_chunks(const lsa_geom* g, const void* q, lsa_dtype q_dt, co
                             const float* bias, int32_t H, int32_t d, const void* kic,
                             lsa_dtype kic_dt, const float* kic_scale, float* z, void* ws,
                             size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * a2, OR mode.  Independent memory indexers sit at several layers (the
+ * pages place three, at layers 10, 12 and 20); at inference a chunk is
+ * fetched when any layer scores it above 0.5 (cjcn.com.cn explainer,
+ * section 四; gist.science summary, section 2.4).  Layer l has its own
+ * q[l], w[l], bias[l], kic[l] (and kic_scale[l] for fp8 keys), with the
+ * shapes, dtypes and meaning of lsa_score_chunks; each layer's logits are
+ * computed exactly as there, and z receives their per-chunk maximum
+ * (the earliest of equals), so lsa_select_threshold on z selects the OR of
+ * the layers' selections.
+ *   n_layers  1..LSA_MAX_LAYERS
+ *   q, w, bias, kic, kic_scale  (host) arrays of n_layers device pointers
+ *             (kic_scale may be NULL unless kic_dt is fp8)
+ *   z (device) [sum N] f32 output;  ws as lsa_score_ws_bytes(g, d)
+ * ---------------------------------------------------------------------- */
+lsa_status lsa_score_chunks_union(const lsa_geom* g, int32_t n_layers, const void* const* q,
+                                  lsa_dtype q_dt, const float* const* w, const float* const* bias,
+                                  int32_t H, int32_t d, const void* const* kic, lsa_dtype kic_dt,
+                                  const float* const* kic_scale, float* z, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /* ------------------------------------------------------------------------
  * a3. Threshold selection.  A fixed threshold replaces a fixed top-k, so

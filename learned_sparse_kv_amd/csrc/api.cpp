@@ -91,6 +91,41 @@ lsa_status lsa_score_chunks(const lsa_geom* g, const void* q, lsa_dtype q_dt, co
     return LSA_OK;
 }
 
+lsa_status lsa_score_chunks_union(const lsa_geom* g, int32_t n_layers, const void* const* q,
+                                  lsa_dtype q_dt, const float* const* w, const float* const* bias,
+                                  int32_t H, int32_t d, const void* const* kic, lsa_dtype kic_dt,
+                                  const float* const* kic_scale, float* z, void* ws, size_t ws_bytes,
+                                  void* stream) {
+    GeomDev gd;
+    lsa_status st = geom_derive(g, &gd);
+    if (st != LSA_OK) return st;
+    if (n_layers < 1 || n_layers > LSA_MAX_LAYERS || !q || !w || !bias || !kic || !ws ||
+        !aligned16(ws))
+        return LSA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LSA_ERR_UNSUPPORTED;
+    if (H < 1 || H > 256) return LSA_ERR_INVALID_ARG;
+    if (q_dt != LSA_F32 && q_dt != LSA_BF16) return LSA_ERR_UNSUPPORTED;
+    if (kic_dt != LSA_F32 && kic_dt != LSA_BF16 && kic_dt != LSA_FP8_E4M3FN)
+        return LSA_ERR_UNSUPPORTED;
+    const int64_t n = gd.chunk_off[gd.B];
+    if (n > 0 && !z) return LSA_ERR_INVALID_ARG;
+    if (n > 0 && kic_dt == LSA_FP8_E4M3FN && !kic_scale) return LSA_ERR_INVALID_ARG;
+    for (int l = 0; l < n_layers; ++l) {
+        if (!q[l] || !w[l] || !bias[l]) return LSA_ERR_INVALID_ARG;
+        if (n > 0 && (!kic[l] || !aligned16(kic[l]))) return LSA_ERR_INVALID_ARG;
+        if (n > 0 && kic_dt == LSA_FP8_E4M3FN && !kic_scale[l]) return LSA_ERR_INVALID_ARG;
+    }
+    if (ws_bytes < lsa_score_ws_bytes(g, d)) return LSA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    float* qbar = (float*)ws;  // reused by each layer in stream order
+    for (int l = 0; l < n_layers; ++l) {
+        LSA_HIP(launch_fuse_query(gd, q[l], q_dt, w[l], H, d, qbar, s));
+        LSA_HIP(launch_score(gd, kic[l], kic_dt, kic_dt == LSA_FP8_E4M3FN ? kic_scale[l] : nullptr, qbar,
+                             bias[l], d, z, s, l > 0));
+    }
+    return LSA_OK;
+}
+
 lsa_status lsa_select_threshold(const lsa_geom* g, const float* z, float theta, int32_t* sel_ids,
                                 int32_t* sel_cnt, void* stream) {
     GeomDev gd;

@@ -13,6 +13,12 @@
 // denormal flush, no other contraction.  One lane owns one chunk so each
 // dot product is a plain sequential chain.
 //
+// The union over several indexer layers (OR mode: a chunk is fetched when
+// any layer's score exceeds 0.5; cjcn.com.cn explainer, section 四;
+// gist.science summary, section 2.4) scores the layers one after another
+// into the same z, each later layer keeping the per-chunk maximum, so that
+// z > theta exactly when some layer's logit is.
+//
 // k_score streams KIComp from HBM: each wave takes about two tiles of 64
 // chunks of one request; rows come in with coalesced 16-byte loads (the next
 // tile in flight while the current one is scored), go through a wave-private
@@ -107,7 +113,8 @@ constexpr int score_waves() {
 template <int KDT, int D>
 __global__ __launch_bounds__((64 * score_waves<KDT, D>())) void k_score(
     GeomDev g, const uint8_t* __restrict__ kic, const float* __restrict__ kscale,
-    const float* __restrict__ qbar, const float* __restrict__ bias, float* __restrict__ z) {
+    const float* __restrict__ qbar, const float* __restrict__ bias, float* __restrict__ z,
+    int combine) {
     constexpr int kScoreWaves = score_waves<KDT, D>();
     constexpr int EB = KDT == LSA_F32 ? 4 : (KDT == LSA_BF16 ? 2 : 1);
     constexpr int ROWB = D * EB;          // bytes per KIComp row
@@ -159,7 +166,17 @@ __global__ __launch_bounds__((64 * score_waves<KDT, D>())) void k_score(
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int c = t * 64 + lane;
         const float acc = row_dot<KDT, D>((const uint4*)(lt + lane * STRIDE), (const float4*)qs);
-        if (c < nh) z[off + c] = __builtin_fmaf(s, acc, br);
+        if (c < nh) {
+            const float zl = __builtin_fmaf(s, acc, br);
+            // union over indexer layers: keep the earlier logit unless this one
+            // is strictly larger (the per-chunk max, first of equals)
+            if (combine) {
+                const float zo = z[off + c];
+                z[off + c] = zl > zo ? zl : zo;
+            } else {
+                z[off + c] = zl;
+            }
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();  // the LDS tile is rewritten next round
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -227,7 +244,8 @@ hipError_t launch_fuse_query(const GeomDev& g, const void* q, lsa_dtype q_dt, co
 }
 
 hipError_t launch_score(const GeomDev& g, const void* kic, lsa_dtype kdt, const float* kscale,
-                        const float* qbar, const float* bias, int d, float* z, hipStream_t s) {
+                        const float* qbar, const float* bias, int d, float* z, hipStream_t s,
+                        bool combine) {
     const int tiles = g.tile_off[g.B];
     if (tiles == 0) return hipSuccess;
     int mt = 0;  // tiles of the longest request
@@ -239,7 +257,7 @@ hipError_t launch_score(const GeomDev& g, const void* kic, lsa_dtype kdt, const 
         timing_begin("k_score", s);                                                             \
         hipLaunchKernelGGL((k_score<KDT, D>), dim3((mt + 2 * nw - 1) / (2 * nw), g.B),           \
                            dim3(64 * nw), 0, s,                                                 \
-                           g, k, kscale, qbar, bias, z);                                        \
+                           g, k, kscale, qbar, bias, z, combine ? 1 : 0);                       \
         timing_end("k_score", s);                                                               \
         return hipGetLastError();                                                               \
     }

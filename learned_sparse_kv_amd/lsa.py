@@ -84,6 +84,7 @@ def _load():
         "lsa_score_ws_bytes": ([G, I32], SZ),
         "lsa_score_chunks": ([G, P, I, P, P, I32, I32, P, I, P, P, P, SZ, P], I),
         "lsa_select_threshold": ([G, P, F, P, P, P], I),
+        "lsa_score_chunks_union": ([G, I32, P, I, P, P, I32, I32, P, I, P, P, P, SZ, P], I),
         "lsa_refine_ws_bytes": ([G, I32], SZ),
         "lsa_topk_refine": ([G, P, P, P, I64, I64, P, I, P, P, I, P, I32, I32, I32, P, P, P, SZ,
                              P], I),
@@ -168,6 +169,18 @@ def lsa_score_chunks(g: Geom, q, q_dt, w, bias, H, d, kic, kic_dt, kic_scale, z,
            _lib.lsa_score_chunks(g.ref, _ptr(q), q_dt, _ptr(w), _ptr(bias), H, d, _ptr(kic), kic_dt,
                                  _ptr(kic_scale), _ptr(z), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(stream)))
+
+
+def lsa_score_chunks_union(g: Geom, q, q_dt, w, bias, H, d, kic, kic_dt, kic_scale, z, ws,
+                           stream=None):
+    """q, w, bias, kic, kic_scale: equal-length lists of per-layer tensors
+    (kic_scale entries may be None unless kic_dt is fp8)."""
+    n = len(q)
+    arr = lambda xs: (C.c_void_p * n)(*[_ptr(x) for x in xs])
+    _check("lsa_score_chunks_union",
+           _lib.lsa_score_chunks_union(g.ref, n, arr(q), q_dt, arr(w), arr(bias), H, d, arr(kic), kic_dt,
+                                       arr(kic_scale), _ptr(z), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream)))
 
 
 def lsa_select_threshold(g: Geom, z, theta, sel_ids, sel_cnt, stream=None):

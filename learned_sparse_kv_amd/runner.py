@@ -71,6 +71,22 @@ class DeviceInputs:
         lsa.lsa_select_threshold(self.geom, z, theta, sel, cnt, stream)
         return z[:self.nh], sel, cnt
 
+    def score_select_union(self, layers, theta=0.0, stream=None):
+        """OR-mode union over indexer layers (list of dicts with q_coarse,
+        w_coarse, bias, kic, kic_scale as host arrays)."""
+        cfg, d = self.cfg, self.device
+        dev = [{k: torch.from_numpy(np.ascontiguousarray(v)).to(d) for k, v in lay.items()} for lay in layers]
+        z = torch.empty(max(self.nh, 1), dtype=torch.float32, device=d)
+        sel = torch.full((max(self.nh, 1),), -1, dtype=torch.int32, device=d)
+        cnt = torch.zeros(self.B, dtype=torch.int32, device=d)
+        ws = _ws(lsa.lsa_score_ws_bytes(self.geom, cfg.d), d)
+        lsa.lsa_score_chunks_union(self.geom, [x["q_coarse"] for x in dev], cfg.q_dtype,
+                                   [x["w_coarse"] for x in dev], [x["bias"] for x in dev], cfg.H, cfg.d,
+                                   [x["kic"] for x in dev], cfg.idx_dtype, [x["kic_scale"] for x in dev],
+                                   z, ws, stream)
+        lsa.lsa_select_threshold(self.geom, z, theta, sel, cnt, stream)
+        return z[:self.nh], sel, cnt
+
     def refine_topk(self, sel, cnt, step, k, pages=None, page_table=None, stream=None):
         cfg, d = self.cfg, self.device
         pages = self.pages if pages is None else pages

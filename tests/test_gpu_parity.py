@@ -263,3 +263,27 @@ def test_topk_all_ties_zero_query():
         want = toks[:cfg.topk]
         got = topk.cpu().numpy()[r, :tcnt.cpu().numpy()[r]]
         assert list(got) == want
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16", "fp8", "cfg3"])
+def test_score_union_bitexact(kind):
+    """OR-mode union over three indexer layers: the combined logits bitwise,
+    the selected ids and counts exactly."""
+    inp, dev, o = setup(kind)
+    layers = synth.indexer_layers(inp, 3)
+    z, sel, cnt = dev.score_select_union(layers)
+    torch.cuda.synchronize()
+    z_o, sel_o, cnt_o = o.score_select_union(layers)
+    assert np.array_equal(z.cpu().numpy().view(np.uint32), z_o.view(np.uint32))
+    c = cnt.cpu().numpy()
+    assert np.array_equal(c, cnt_o)
+    s = sel.cpu().numpy()
+    for r in range(inp.cfg.batch):
+        a = int(inp["chunk_off"][r])
+        assert np.array_equal(s[a:a + c[r]], sel_o[a:a + c[r]])
+    # one layer through the union entry point is the single-layer scoring
+    z1, _, c1 = dev.score_select_union(layers[:1])
+    z0, _, c0 = dev.score_select()
+    torch.cuda.synchronize()
+    assert np.array_equal(z1.cpu().numpy().view(np.uint32), z0.cpu().numpy().view(np.uint32))
+    assert np.array_equal(c1.cpu().numpy(), c0.cpu().numpy())
