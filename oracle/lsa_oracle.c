@@ -235,6 +235,69 @@ int lsao_score_select_union(const lsao_batch* b, int32_t n_layers, const void* c
     return 0;
 }
 
+/* Per-head sigmoid score.  The memory indexer is the lightning indexer with
+ * its ReLU replaced by a sigmoid, so that its score is a probability in
+ * (0, 1) and a fixed threshold of 0.5 decides the fetch (cjcn.com.cn
+ * explainer, section 二).  Read literally, per chunk c of request r:
+ *     S_c = sum_h w_h sigmoid(s_c (q_h . k_c) + b_r),  fetched iff S_c > 0.5.
+ * fp32 order: per head the dot product is an fmaf chain over i from +0,
+ * x_h = fmaf(s_c, a_h, b_r), and S_c an fmaf chain over h from +0 of
+ * w_h * sigmoid(x_h).  The pages fix no precision for the sigmoid, so one
+ * fp32 definition is written out (o_sigmoid) and the library follows it:
+ *     sigmoid(x) = 1 / (1 + e^(-x)),  e^y = 2^t with t = y * log2(e):
+ *     n = rint(t), f = t - n (|f| <= 1/2), 2^f by the degree-7 Taylor
+ *     polynomial (ln 2)^k / k! in Horner form with fmaf, times 2^n (ldexp).
+ * t is clamped to [-200, 200] first (2^t is 0 or inf beyond, in fp32).
+ * The constants are the fp32 values nearest to log2(e) and (ln 2)^k / k!. */
+static const float O_LOG2E = 1.44269502162933349609375f;  /* 0x3fb8aa3b */
+static const float O_EXP2C[8] = {1.0f, 0.693147182464599609375f, 0.2402265071868896484375f,
+                                 0.0555041097104549407958984375f, 0.00961812864989042282104492188f,
+                                 0.00133335578721016645431518555f, 0.000154035296873189508914947510f,
+                                 1.52527336467755958437919616699e-05f};
+
+float lsao_sigmoid(float x) {
+    float t = -x * O_LOG2E;
+    t = fminf(fmaxf(t, -200.0f), 200.0f);
+    const float n = rintf(t);
+    const float f = t - n;
+    float p = O_EXP2C[7];
+    for (int k = 6; k >= 0; k--) p = fmaf(p, f, O_EXP2C[k]);
+    const float e = ldexpf(p, (int)n);
+    return 1.0f / (1.0f + e);
+}
+
+int lsao_score_select_sigmoid(const lsao_batch* b, const void* q, const float* w, const float* bias,
+                              float theta, float* S, int32_t* sel, int32_t* cnt) {
+    int64_t chunk0 = 0;
+    float* kf = (float*)malloc(sizeof(float) * (size_t)b->d);
+    if (!kf) return -1;
+    for (int32_t r = 0; r < b->B; r++) {
+        int64_t g[3];
+        lsao_geometry(b->seq_len[r], b->C, b->W, g);
+        const int64_t N = g[1];
+        int32_t n_sel = 0;
+        for (int64_t c = 0; c < N; c++) {
+            const int64_t row = chunk0 + c;
+            for (int32_t i = 0; i < b->d; i++) kf[i] = o_elem(b->idx_dt, b->kic, row * b->d + i);
+            const float s = (b->idx_dt == O_FP8) ? b->kic_scale[row] : 1.0f;
+            float acc_s = 0.0f;
+            for (int32_t h = 0; h < b->H; h++) {
+                float a = 0.0f;
+                for (int32_t i = 0; i < b->d; i++)
+                    a = fmaf(o_elem(b->q_dt, q, ((int64_t)r * b->H + h) * b->d + i), kf[i], a);
+                const float x = fmaf(s, a, bias[r]);
+                acc_s = fmaf(w[(int64_t)r * b->H + h], lsao_sigmoid(x), acc_s);
+            }
+            S[row] = acc_s;
+            if (acc_s > theta) sel[chunk0 + n_sel++] = (int32_t)c;
+        }
+        cnt[r] = n_sel;
+        chunk0 += N;
+    }
+    free(kf);
+    return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* O6-O8: candidate tokens, lightning refine score, top-k              */
 /* ------------------------------------------------------------------ */

@@ -57,6 +57,10 @@ def load(path: str):
     _lib.lsao_score_select.restype = C.c_int
     _lib.lsao_score_select_union.argtypes = [C.POINTER(Batch), I32, P, P, P, P, P, F, P, P, P]
     _lib.lsao_score_select_union.restype = C.c_int
+    _lib.lsao_score_select_sigmoid.argtypes = [C.POINTER(Batch), P, P, P, F, P, P, P]
+    _lib.lsao_score_select_sigmoid.restype = C.c_int
+    _lib.lsao_sigmoid.argtypes = [F]
+    _lib.lsao_sigmoid.restype = F
     _lib.lsao_refine_topk.argtypes = [C.POINTER(Batch), I32, P, I32, P, P, I32, P, P]
     _lib.lsao_refine_topk.restype = I32
     _lib.lsao_attend.argtypes = [C.POINTER(Batch), I32, P, I32, P, D, P, P]
@@ -128,6 +132,22 @@ class Oracle:
         assert rc == 0
         return z[:self.n_total], sel[:self.n_total], cnt
 
+    def score_select_sigmoid(self, theta: float = 0.5, q=None, w=None, bias=None):
+        """Per-head sigmoid score S_c (probabilities) and the chunks with
+        S_c > theta.  Returns (S, sel, cnt)."""
+        inp = self.inp
+        q = np.ascontiguousarray(inp["q_coarse"] if q is None else q)
+        w = np.ascontiguousarray(inp["w_coarse"] if w is None else w, dtype=np.float32)
+        bias = np.ascontiguousarray(inp["bias"] if bias is None else bias, dtype=np.float32)
+        n = max(self.n_total, 1)
+        S = np.zeros(n, np.float32)
+        sel = np.full(n, -1, np.int32)
+        cnt = np.zeros(self.cfg.batch, np.int32)
+        rc = lib().lsao_score_select_sigmoid(C.byref(self.batch), _p(q), _p(w), _p(bias),
+                                             np.float32(theta), _p(S), _p(sel), _p(cnt))
+        assert rc == 0
+        return S[:self.n_total], sel[:self.n_total], cnt
+
     def score_select_union(self, layers, theta: float = 0.0):
         """OR-mode union over indexer layers.  layers: list of dicts with
         q_coarse, w_coarse, bias, kic, kic_scale.  Returns (zmax, sel, cnt)."""
@@ -195,6 +215,11 @@ class Oracle:
                                      _p(out), _p(lse), threads)
         assert rc == 0
         return [tk[i, :tc[i]].copy() for i in range(n)], out, lse
+
+
+def sigmoid(x: float) -> float:
+    """The oracle's fp32 sigmoid of the per-head score (exposed for its pins)."""
+    return float(lib().lsao_sigmoid(np.float32(x)))
 
 
 def pool_sim(selections, capacity: int):

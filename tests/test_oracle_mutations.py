@@ -44,6 +44,13 @@ MUTATIONS = {
                                  "for (int32_t l = 0; l < n_layers - 1; l++) {\n                float acc"),
     "union_keys_of_layer0": ("o_elem(b->idx_dt, kic[l], row * b->d + i)", "o_elem(b->idx_dt, kic[0], row * b->d + i)"),
     "union_query_of_layer0": ("acc = fmaf(qbar[(int64_t)l * b->d + i],", "acc = fmaf(qbar[i],"),
+    "sigmoid_sign": ("float t = -x * O_LOG2E;", "float t = x * O_LOG2E;"),
+    "sigmoid_poly_short": ("for (int k = 6; k >= 0; k--) p = fmaf(p, f, O_EXP2C[k]);",
+                           "for (int k = 6; k >= 1; k--) p = fmaf(p, f, O_EXP2C[k]);"),
+    "sigscore_no_bias": ("const float x = fmaf(s, a, bias[r]);", "const float x = s * a;"),
+    "sigscore_weight_of_request0": ("acc_s = fmaf(w[(int64_t)r * b->H + h],", "acc_s = fmaf(w[h],"),
+    "sigscore_relu": ("acc_s = fmaf(w[(int64_t)r * b->H + h], lsao_sigmoid(x), acc_s);",
+                      "acc_s = fmaf(w[(int64_t)r * b->H + h], x > 0.0f ? x : 0.0f, acc_s);"),
 }
 
 PIN_CALLS = [
@@ -61,6 +68,9 @@ PIN_CALLS = [
     "p.test_attention_closed_forms()",
     "p.test_union_is_union_of_single_layers(1)",
     "p.test_union_special_cases()",
+    "p.test_sigmoid_against_double_and_closed_forms()",
+    "p.test_sigmoid_score_brute_force(0)",
+    "p.test_sigmoid_score_special_cases()",
 ]
 
 RUNNER = """

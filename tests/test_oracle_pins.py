@@ -395,3 +395,90 @@ def test_union_special_cases():
     _, _, cnt_none = o.score_select_union(lays, theta=float("inf"))
     _, _, cnt_all = o.score_select_union(lays, theta=float("-inf"))
     assert (cnt_none == 0).all() and list(cnt_all) == list(inp["n_hist"])
+
+
+# ------------------------------------------------- NEXT-2 per-head sigmoid score
+def test_sigmoid_against_double_and_closed_forms():
+    """The oracle's written-out fp32 sigmoid against the double-precision
+    1/(1+exp(-x)): within a few ulp plus the conditioning of forming
+    t = x log2(e) in fp32 (its rounding, |t| 2^-24, becomes a relative error
+    of ln 2 |t| 2^-24 in e^-x), up to |x| = 88; exact at 0; 1 beyond 17 and 0
+    below -89."""
+    rng = np.random.default_rng(5)
+    xs = np.concatenate([rng.uniform(-20, 20, 20000), rng.uniform(-88, 88, 5000),
+                         [0.25, 0.5, 1.0, -1.0, 3.0, -7.5]]).astype(np.float32)
+    for x in xs:
+        s = oracle.sigmoid(float(x))
+        ref = 1.0 / (1.0 + math.exp(-float(x)))
+        tol = 3e-7 + abs(float(x)) * 1.4427 * 2 ** -23
+        assert abs(s - ref) <= tol * ref, (float(x), s, ref)
+    assert oracle.sigmoid(0.0) == 0.5 and oracle.sigmoid(-0.0) == 0.5
+    assert oracle.sigmoid(17.0) == 1.0 and oracle.sigmoid(1e30) == 1.0
+    assert oracle.sigmoid(-89.0) == 0.0 and oracle.sigmoid(-1e30) == 0.0
+    # symmetry sigma(x) + sigma(-x) = 1 to a few ulp
+    for x in rng.uniform(-15, 15, 2000).astype(np.float32):
+        assert abs(oracle.sigmoid(float(x)) + oracle.sigmoid(-float(x)) - 1.0) <= 3e-7
+
+
+def _exact_sigmoid_scores(inp):
+    """S_c with exact rational dot products and a double sigmoid, and a bound
+    on the fp32 result's distance from it."""
+    cfg = inp.cfg
+    q = oracle.decode(cfg.q_dtype, inp["q_coarse"]).reshape(cfg.batch, cfg.H, cfg.d)
+    kic = oracle.decode(cfg.idx_dtype, inp["kic"]).reshape(-1, cfg.d)
+    out, bound = [], []
+    for r in range(cfg.batch):
+        b = float(inp["bias"][r])
+        for c in range(inp["chunk_off"][r], inp["chunk_off"][r + 1]):
+            s = float(inp["kic_scale"][c]) if cfg.idx_dtype == synth.FP8 else 1.0
+            tot, err = 0.0, 0.0
+            for h in range(cfg.H):
+                a = sum(Fraction(float(q[r, h, i])) * Fraction(float(kic[c, i])) for i in range(cfg.d))
+                mag = sum(abs(float(q[r, h, i]) * float(kic[c, i])) for i in range(cfg.d))
+                x = float(s * a + Fraction(b))
+                sig = 1.0 / (1.0 + math.exp(-x))
+                w = float(inp["w_coarse"][r, h])
+                tot += w * sig
+                dx = gamma(cfg.d + 2) * (abs(s) * mag + abs(b))
+                err += abs(w) * (dx / 4 + 4e-7 * sig + 1e-38)
+            out.append(tot)
+            bound.append(err + gamma(cfg.H + 1) * tot + 1e-38)
+    return out, bound
+
+
+@pytest.mark.parametrize("idx", [synth.F32, synth.FP8])
+def test_sigmoid_score_brute_force(idx):
+    inp = helpers.tiny_inputs(idx_dtype=idx, d=7, H=4)
+    rng = np.random.default_rng(9)
+    inp["w_coarse"] = rng.uniform(0.05, 0.5, size=inp["w_coarse"].shape).astype(np.float32)
+    inp["bias"] = np.array([0.3, -0.7], np.float32)
+    S, sel, cnt = oracle.Oracle(inp).score_select_sigmoid()
+    exact, bound = _exact_sigmoid_scores(inp)
+    assert len(S) == len(exact) > 0
+    for si, ei, bi in zip(S, exact, bound):
+        assert abs(float(si) - ei) <= bi, (si, ei, bi)
+    for r in range(inp.cfg.batch):
+        c0 = inp["chunk_off"][r]
+        n = inp["chunk_off"][r + 1] - c0
+        assert sel[c0:c0 + cnt[r]].tolist() == [c for c in range(n) if S[c0 + c] > 0.5]
+
+
+def test_sigmoid_score_special_cases():
+    inp = helpers.tiny_inputs(H=4, d=5)
+    inp["w_coarse"][:] = 0.25
+    inp["kic"][:] = 0.0
+    for b, want_sel in [(0.0, False), (1e-3, True), (-1e-3, False)]:
+        inp["bias"][:] = b
+        S, sel, cnt = oracle.Oracle(inp).score_select_sigmoid()
+        # every head sees x = b: S = 4 * 0.25 * sigmoid(b) = sigmoid(b), exactly
+        assert (S == np.float32(oracle.sigmoid(b))).all()
+        assert list(cnt) == (list(inp["n_hist"]) if want_sel else [0] * inp.cfg.batch)
+    # a chunk aligned with every head's query is selected, its negation is not
+    inp = helpers.tiny_inputs(H=2, d=4)
+    inp["w_coarse"][:] = 0.5
+    inp["bias"][:] = 0.0
+    inp["q_coarse"][:] = 1.0
+    inp["kic"][:] = 0.5
+    inp["kic"][1::2] = -0.5
+    S, sel, cnt = oracle.Oracle(inp).score_select_sigmoid()
+    assert (S[0::2] > 0.5).all() and (S[1::2] < 0.5).all()
