@@ -171,12 +171,15 @@ def hbm_calibration(nbytes=1 << 30, reps=5):
             "stream_read_gbs": round(nbytes / stream_s / 1e9, 1)}
 
 
-def sustained_scoring(label, B, L, idx_dt, H=64, d=128, window=8192, seed=0, reps=3, layers=1):
+def sustained_scoring(label, B, L, idx_dt, H=64, d=128, window=8192, seed=0, reps=3, layers=1,
+                      sigmoid=False, theta=0.5):
     """lsa_score_chunks + lsa_select_threshold over many distinct KIComp buffers
     (together more than twice the 256 MB last-level cache), so every launch
     streams cold lines: B requests of L tokens each, one launch per trigger.
     layers > 1: the OR-mode union over that many indexer layers
-    (lsa_score_chunks_union), each layer reading its own buffer."""
+    (lsa_score_chunks_union), each layer reading its own buffer.
+    sigmoid: the per-head sigmoid score (lsa_score_chunks_sigmoid) with the
+    0.5 threshold; its bound is fp32 vector arithmetic (H*d fma per chunk)."""
     import math
     import numpy as np
     import torch
@@ -210,6 +213,10 @@ def sustained_scoring(label, B, L, idx_dt, H=64, d=128, window=8192, seed=0, rep
     ws = torch.empty(max(lsa.lsa_score_ws_bytes(g, d), 256), dtype=torch.uint8, device="cuda")
 
     def trig(b):
+        if sigmoid:
+            lsa.lsa_score_chunks_sigmoid(g, q, synth.BF16, w, bias, theta, H, d, kic[b], idx_dt, ksc[b], z)
+            lsa.lsa_select_threshold(g, z, theta, sel, cnt)
+            return
         if layers == 1:
             lsa.lsa_score_chunks(g, q, synth.BF16, w, bias, H, d, kic[b], idx_dt, ksc[b], z, ws)
         else:
@@ -228,19 +235,25 @@ def sustained_scoring(label, B, L, idx_dt, H=64, d=128, window=8192, seed=0, rep
             trig(b)
     torch.cuda.synchronize()
     lsa.lsa_timing_enable(False)
-    t = {n: lsa.lsa_timing_read(n) for n in ("k_fuse_query", "k_score", "k_select")}
+    kname = "k_score_sig" if sigmoid else "k_score"
+    t = {n: lsa.lsa_timing_read(n) for n in ("k_fuse_query", kname, "k_select")}
     lsa.lsa_timing_reset()
     us = {n: (ms * 1e3 / c if c else None) for n, (c, ms) in t.items()}
-    gbs = per / (us["k_score"] * 1e-6) / 1e9  # per layer launch
+    gbs = per / (us[kname] * 1e-6) / 1e9  # per layer launch
     trig_us = sum(ms for (c, ms) in t.values()) * 1e3 / (reps * nbuf)
     del kic, ksc
     torch.cuda.empty_cache()
-    return {"label": label, "batch": B, "context": L,
-            "index_keys": "fp8_e4m3fn" if idx_dt == synth.FP8 else "bf16", "indexer_layers": layers,
-            "bytes_per_trigger": per * layers, "distinct_buffers": nbuf, "launches": reps * nbuf * layers,
-            "k_score_us": round(us["k_score"], 2), "gbs": round(gbs, 1),
-            "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
-            "trigger_us": round(trig_us, 2)}
+    out = {"label": label, "batch": B, "context": L,
+           "index_keys": "fp8_e4m3fn" if idx_dt == synth.FP8 else "bf16", "indexer_layers": layers,
+           "score": "sigmoid" if sigmoid else "relu_fused",
+           "bytes_per_trigger": per * layers, "distinct_buffers": nbuf, "launches": reps * nbuf * layers,
+           "k_score_us": round(us[kname], 2), "gbs": round(gbs, 1),
+           "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+           "trigger_us": round(trig_us, 2)}
+    if sigmoid:
+        flops = 2.0 * nh * H * d
+        out["tflops"] = round(flops / (us[kname] * 1e-6) / 1e12, 1)
+    return out
 
 
 def sustained_attention(label, B, L, nbatch=6, reps=3, k=2048, Hq=64, Dk=576, Dv=512,

@@ -140,6 +140,36 @@ lsa_status lsa_score_chunks_union(const lsa_geom* g, int32_t n_layers, const voi
                                   void* stream);
 
 /* ------------------------------------------------------------------------
+ * a2, per-head sigmoid variant.  The memory indexer is the lightning indexer
+ * with its ReLU replaced by a sigmoid, so that its score is a probability
+ * and a fixed 0.5 decides the fetch (cjcn.com.cn explainer, section 二).
+ * Read per head, for every history chunk c of request r:
+ *     x_h = fma(s_c, a_h, b[r]),  a_h = sum_i q[r,h,i] * k_c[i] (fp32 fma chain
+ *           over i from +0),  s_c = kic_scale[c] for fp8 keys, else 1
+ *     S[c] = sum_h w[r,h] * sigmoid(x_h)  (fp32 fma chain over h from +0)
+ * with one written fp32 sigmoid: 1 / (1 + 2^t), t = clamp(-x log2 e, -200,
+ * 200), 2^t = ldexp(P(f), n), n = rint(t), f = t - n, P the degree-7 Taylor
+ * polynomial of 2^f with coefficients nearest to (ln 2)^k / k! in Horner
+ * fma form; IEEE division.
+ * With bf16 queries and bf16 or fp8 keys (H <= 64 for d = 128, H <= 128 for
+ * d = 64) the dot products run on the matrix cores and S[c] is within a
+ * rigorous per-chunk bound E_c (about 1e-4 at unit weights) of the value
+ * above; where |S[c] - theta| <= E_c, S[c] is that value bit for bit.  So
+ * S[c] > theta holds exactly when it holds in the order above, and
+ * lsa_select_threshold(S, theta) with the same theta selects exactly the
+ * fetched chunks.  Otherwise (fp32 queries or keys, H * d <= 8192) every
+ * S[c] is the value above bit for bit.
+ *   q, w, bias, kic, kic_scale as lsa_score_chunks (q 16-byte aligned);
+ *   theta   the fetch threshold (0.5 for probabilities)
+ *   S (device) [sum N] f32
+ * d must be 64 or 128.  No workspace.
+ * ---------------------------------------------------------------------- */
+lsa_status lsa_score_chunks_sigmoid(const lsa_geom* g, const void* q, lsa_dtype q_dt, const float* w,
+                                    const float* bias, float theta, int32_t H, int32_t d,
+                                    const void* kic, lsa_dtype kic_dt, const float* kic_scale, float* S,
+                                    void* stream);
+
+/* ------------------------------------------------------------------------
  * a3. Threshold selection.  A fixed threshold replaces a fixed top-k, so
  * the number of fetched chunks varies (cjcn.com.cn, section 二; gist.science
  * 2.1 "Dynamisches Fetching").  Chunk c of request r is selected iff
@@ -315,7 +345,7 @@ lsa_status lsa_step64(lsa_ctx* ctx, const lsa_window_in* in, lsa_window_out* out
  * the recorded events and returns, for one kernel name (k_fuse_query,
  * k_score, k_select, k_refine, k_topk, k_refine_mfma, k_band_fine,
  * k_band_list, k_topk_band, k_attn_mla, k_attn_f32, k_attn_merge,
- * k_gather, k_stream_read), the number of timed launches and their summed duration in
+ * k_gather, k_stream_read, k_score_sig), the number of timed launches and their summed duration in
  * milliseconds since the last reset.  lsa_timing_only(name) restricts the
  * timing to that one kernel (NULL: all; a name of 64 or more characters is
  * LSA_ERR_INVALID_ARG), so that one kernel can be timed inside a run with

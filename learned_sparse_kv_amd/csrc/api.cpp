@@ -126,6 +126,28 @@ lsa_status lsa_score_chunks_union(const lsa_geom* g, int32_t n_layers, const voi
     return LSA_OK;
 }
 
+lsa_status lsa_score_chunks_sigmoid(const lsa_geom* g, const void* q, lsa_dtype q_dt, const float* w,
+                                    const float* bias, float theta, int32_t H, int32_t d,
+                                    const void* kic, lsa_dtype kic_dt, const float* kic_scale, float* S,
+                                    void* stream) {
+    GeomDev gd;
+    lsa_status st = geom_derive(g, &gd);
+    if (st != LSA_OK) return st;
+    if (!q || !w || !bias) return LSA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LSA_ERR_UNSUPPORTED;
+    if (H < 1 || H * d > 8192) return LSA_ERR_INVALID_ARG;
+    if (q_dt != LSA_F32 && q_dt != LSA_BF16) return LSA_ERR_UNSUPPORTED;
+    if (kic_dt != LSA_F32 && kic_dt != LSA_BF16 && kic_dt != LSA_FP8_E4M3FN)
+        return LSA_ERR_UNSUPPORTED;
+    const int64_t n = gd.chunk_off[gd.B];
+    if (n > 0 && (!kic || !S || !aligned16(kic) || !aligned16(q))) return LSA_ERR_INVALID_ARG;
+    if (n > 0 && kic_dt == LSA_FP8_E4M3FN && !kic_scale) return LSA_ERR_INVALID_ARG;
+    if (!(theta == theta)) return LSA_ERR_INVALID_ARG;
+    LSA_HIP(launch_score_sig(gd, kic, kic_dt, kic_scale, q, q_dt, w, H, bias, theta, d, S,
+                             (hipStream_t)stream));
+    return LSA_OK;
+}
+
 lsa_status lsa_select_threshold(const lsa_geom* g, const float* z, float theta, int32_t* sel_ids,
                                 int32_t* sel_cnt, void* stream) {
     GeomDev gd;

@@ -31,6 +31,9 @@ hipError_t launch_fuse_query(const GeomDev& g, const void* q, lsa_dtype q_dt, co
 hipError_t launch_score(const GeomDev& g, const void* kic, lsa_dtype kdt, const float* kscale,
                         const float* qbar, const float* bias, int d, float* z, hipStream_t s,
                         bool combine = false);
+hipError_t launch_score_sig(const GeomDev& g, const void* kic, lsa_dtype kdt, const float* kscale,
+                            const void* q, lsa_dtype q_dt, const float* w, int H, const float* bias,
+                            float theta, int d, float* S, hipStream_t s);
 hipError_t launch_select(const GeomDev& g, const float* z, float theta, int32_t* sel,
                          int32_t* cnt, hipStream_t s);
 

@@ -36,21 +36,18 @@
 // sum_i |q_i k_i| <= |q_h| |key| (Cauchy-Schwarz).  ReLU is 1-Lipschitz and
 // the head sums add gamma(H) * sum_h |w_h| (ReLU(a'_h) + eps_h).
 #include "lsa_internal.h"
+#include "mfma_util.h"
 
 #include <type_traits>
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+using namespace lsa_dev;
 
 __device__ __forceinline__ uint32_t fkey(float f) {
     const uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-
-constexpr float kU2 = 2.384185791015625e-07f;  // 2^-22: two ulps of fp32 per operation
-__host__ __device__ constexpr float gam(int n) { return n * kU2 / (1.0f - n * kU2); }
 
 constexpr int kWaves = 4;         // waves per block of K1 and K3
 constexpr int kCoarse = 1024;     // coarse bins: key >> 22
@@ -63,38 +60,6 @@ constexpr int kListCap = 8192;    // band entries K4 keeps in LDS
 constexpr int kUncCap = 1024;     // uncertain entries K4 ranks directly
 constexpr int kPgCap = 256;       // chunks per K3 block whose pages K3 keeps in LDS
 constexpr int kUclCap = 512;      // uncertain entries per K3 block kept in LDS
-
-// 8 fp8 e4m3fn bytes -> 8 bf16 (exact: every e4m3 value is a bf16 value;
-// the conversion scale is 1)
-__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-    uint4 r;
-    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
-    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
-    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
-    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
-    return r;
-}
-
-// Element offset of the 8 dims lane group lq holds in MFMA k-step ks.  Any
-// order of the dims gives the same dot products as long as both operands
-// use it; fp8 rows are read 16 bytes (two k-steps) per lane.
-template <int KDT>
-__device__ __forceinline__ int kdim(int ks, int lq) {
-    if constexpr (KDT == LSA_FP8_E4M3FN) return (ks >> 1) * 64 + lq * 16 + (ks & 1) * 8;
-    else return ks * 32 + lq * 8;
-}
-
-__device__ __forceinline__ float sumsq_bf16x8(uint4 v) {
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-    float s = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float lo = __uint_as_float(w4[e] << 16), hi = __uint_as_float(w4[e] & 0xffff0000u);
-        s = __builtin_fmaf(lo, lo, s);
-        s = __builtin_fmaf(hi, hi, s);
-    }
-    return s;
-}
 
 // ---------------------------------------------------------------------------
 template <int NW>

@@ -85,6 +85,7 @@ def _load():
         "lsa_score_chunks": ([G, P, I, P, P, I32, I32, P, I, P, P, P, SZ, P], I),
         "lsa_select_threshold": ([G, P, F, P, P, P], I),
         "lsa_score_chunks_union": ([G, I32, P, I, P, P, I32, I32, P, I, P, P, P, SZ, P], I),
+        "lsa_score_chunks_sigmoid": ([G, P, I, P, P, F, I32, I32, P, I, P, P, P], I),
         "lsa_refine_ws_bytes": ([G, I32], SZ),
         "lsa_topk_refine": ([G, P, P, P, I64, I64, P, I, P, P, I, P, I32, I32, I32, P, P, P, SZ,
                              P], I),
@@ -181,6 +182,12 @@ def lsa_score_chunks_union(g: Geom, q, q_dt, w, bias, H, d, kic, kic_dt, kic_sca
            _lib.lsa_score_chunks_union(g.ref, n, arr(q), q_dt, arr(w), arr(bias), H, d, arr(kic), kic_dt,
                                        arr(kic_scale), _ptr(z), _ptr(ws), ws.numel() * ws.element_size(),
                                        _stream(stream)))
+
+
+def lsa_score_chunks_sigmoid(g: Geom, q, q_dt, w, bias, theta, H, d, kic, kic_dt, kic_scale, S, stream=None):
+    _check("lsa_score_chunks_sigmoid",
+           _lib.lsa_score_chunks_sigmoid(g.ref, _ptr(q), q_dt, _ptr(w), _ptr(bias), float(theta), H, d,
+                                         _ptr(kic), kic_dt, _ptr(kic_scale), _ptr(S), _stream(stream)))
 
 
 def lsa_select_threshold(g: Geom, z, theta, sel_ids, sel_cnt, stream=None):
@@ -296,7 +303,7 @@ def lsa_step64(ctx: Ctx, win, out, main=None, copy=None):
 # ---------------------------------------------------------------- diagnostics
 KERNELS = ("k_fuse_query", "k_score", "k_select", "k_refine", "k_topk", "k_refine_mfma",
            "k_band_fine", "k_band_list", "k_topk_band", "k_attn_mla", "k_attn_f32", "k_attn_merge",
-           "k_gather", "k_stream_read")
+           "k_gather", "k_stream_read", "k_score_sig")
 
 
 def lsa_timing_enable(on: bool):

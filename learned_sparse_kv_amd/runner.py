@@ -71,6 +71,21 @@ class DeviceInputs:
         lsa.lsa_select_threshold(self.geom, z, theta, sel, cnt, stream)
         return z[:self.nh], sel, cnt
 
+    def score_select_sigmoid(self, theta=0.5, window=0, q=None, w=None, bias=None, stream=None):
+        """Per-head sigmoid score S and the chunks with S > theta; q, w, bias
+        (host arrays) replace the request's own when given."""
+        cfg, d = self.cfg, self.device
+        q = self.q_coarse if q is None else _dev(q, d)
+        w = self.w_coarse if w is None else _dev(np.ascontiguousarray(w, dtype=np.float32), d)
+        bias = self.bias if bias is None else _dev(np.ascontiguousarray(bias, dtype=np.float32), d)
+        S = torch.empty(max(self.nh, 1), dtype=torch.float32, device=d)
+        sel = torch.full((max(self.nh, 1),), -1, dtype=torch.int32, device=d)
+        cnt = torch.zeros(self.B, dtype=torch.int32, device=d)
+        lsa.lsa_score_chunks_sigmoid(self.geom, q, cfg.q_dtype, w, bias, theta, cfg.H, cfg.d,
+                                     self.kic[window], cfg.idx_dtype, self.kic_scale[window], S, stream)
+        lsa.lsa_select_threshold(self.geom, S, theta, sel, cnt, stream)
+        return S[:self.nh], sel, cnt
+
     def score_select_union(self, layers, theta=0.0, stream=None):
         """OR-mode union over indexer layers (list of dicts with q_coarse,
         w_coarse, bias, kic, kic_scale as host arrays)."""

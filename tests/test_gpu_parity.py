@@ -39,6 +39,12 @@ def small(kind):
     if kind == "bf16_h8":  # head count off the matrix-core path: the VALU refine
         return synth.small_config("bf16_h8", 25, (7000, 2500), window=1024, idx=BF16, H=8,
                                   topk=256, steps=2)
+    if kind == "bf16_qf32":  # fp32 queries: the one-lane-per-chunk sigmoid score
+        return synth.small_config("bf16_qf32", 26, (6000, 2500), window=1024, idx=BF16, H=16,
+                                  topk=256, steps=1, q_dtype=F32)
+    if kind == "fp8_qf32":
+        return synth.small_config("fp8_qf32", 27, (6000, 4000), window=1024, idx=FP8, H=16,
+                                  topk=256, steps=1, q_dtype=F32)
     if kind == "bf16_h128":
         return synth.small_config("bf16_h128", 24, (4000,), window=512, idx=BF16, H=16, Hq=128,
                                   topk=128, steps=1)
@@ -287,3 +293,89 @@ def test_score_union_bitexact(kind):
     torch.cuda.synchronize()
     assert np.array_equal(z1.cpu().numpy().view(np.uint32), z0.cpu().numpy().view(np.uint32))
     assert np.array_equal(c1.cpu().numpy(), c0.cpu().numpy())
+
+
+def _sig_bound(inp, q, w, bias):
+    """Per-chunk bound on |S' - S| that the matrix-core sigmoid score states
+    (two ulps per operation, Cauchy-Schwarz, 1/4-Lipschitz sigmoid, 2^-14 per
+    head for the two sigmoids), in float64 from the decoded inputs."""
+    cfg = inp.cfg
+    u2, d, H = 2.0 ** -22, cfg.d, cfg.H
+    gam = lambda n: n * u2 / (1 - n * u2)
+    qv = oracle.decode(cfg.q_dtype, q).astype(np.float64).reshape(cfg.batch, H, d)
+    kic = inp["kic_windows"][0]
+    kv = oracle.decode(cfg.idx_dtype, kic).astype(np.float64).reshape(-1, d)
+    sc = inp["kic_scale_windows"][0].astype(np.float64) if cfg.idx_dtype == FP8 else np.ones(len(kv))
+    E = np.zeros(len(kv))
+    for r in range(cfg.batch):
+        a, n = int(inp["chunk_off"][r]), int(inp["n_hist"][r])
+        if n == 0:
+            continue
+        wa = np.abs(w[r].astype(np.float64))
+        x = sc[a:a + n, None] * (kv[a:a + n] @ qv[r].T) + float(bias[r])
+        da = np.abs(sc[a:a + n]) * 2 * gam(d) * np.linalg.norm(kv[a:a + n], axis=1) * \
+            (wa * np.linalg.norm(qv[r], axis=1)).sum()
+        dx = da + 4 * u2 * (np.abs(x) @ wa + da)
+        E[a:a + n] = 0.25 * dx + wa.sum() * (2.0 ** -14 + 2 * gam(H + 24))
+    return E * 1.01
+
+
+def _check_sigmoid(inp, dev, o, q=None, w=None, bias=None, exact=False):
+    q = inp["q_coarse"] if q is None else q
+    w = inp["w_coarse"] if w is None else w
+    bias = inp["bias"] if bias is None else bias
+    S, sel, cnt = dev.score_select_sigmoid(q=q, w=w, bias=bias)
+    torch.cuda.synchronize()
+    S_o, sel_o, cnt_o = o.score_select_sigmoid(q=q, w=w, bias=bias)
+    S = S.cpu().numpy()
+    c = cnt.cpu().numpy()
+    assert np.array_equal(c, cnt_o)
+    s = sel.cpu().numpy()
+    for r in range(inp.cfg.batch):
+        a = int(inp["chunk_off"][r])
+        assert np.array_equal(s[a:a + c[r]], sel_o[a:a + c[r]])
+    if exact:
+        assert np.array_equal(S.view(np.uint32), S_o.view(np.uint32))
+        return S, S_o, 0
+    E = _sig_bound(inp, q, w, bias)
+    err = np.abs(S.astype(np.float64) - S_o)
+    assert np.all(err <= E), (err.max(), E[np.argmax(err - E)])
+    # an output this close to the threshold cannot be an unchecked S': it
+    # is the canonical value
+    w1 = np.abs(np.asarray(w, np.float64)).sum(axis=1).min()
+    near = np.abs(S.astype(np.float64) - 0.5) <= w1 * 2.0 ** -14
+    assert np.array_equal(S[near].view(np.uint32), S_o[near].view(np.uint32))
+    return S, S_o, int(near.sum())
+
+
+SIG_EXACT = ["f32", "bf16_qf32", "fp8_qf32"]      # fp32 queries: one lane per chunk
+SIG_MFMA = ["bf16", "fp8", "bf16_h128", "bf16_h8", "cfg1", "cfg3"]
+
+
+@pytest.mark.parametrize("kind", SIG_EXACT)
+def test_score_sigmoid_exact_path(kind):
+    """Per-head sigmoid score, fp32 queries: S bitwise, the chunks above 0.5 exactly."""
+    inp, dev, o = setup(kind)
+    _check_sigmoid(inp, dev, o, exact=True)
+
+
+@pytest.mark.parametrize("kind", SIG_MFMA)
+def test_score_sigmoid_matrix_core(kind):
+    """Matrix-core sigmoid score: the fetched set exactly, S within its bound,
+    canonical where it sits near the threshold."""
+    inp, dev, o = setup(kind)
+    _check_sigmoid(inp, dev, o)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "bf16_h8"])
+def test_score_sigmoid_near_threshold(kind):
+    """Queries scaled by 2^-16 and zero bias: every S sits within about 1e-5
+    of 0.5, inside the bound, so (nearly) every chunk takes the canonical
+    re-score and the fetch decisions turn on the last bits."""
+    inp, dev, o = setup(kind)
+    q = inp["q_coarse"]
+    qs = synth.to_bf16_bits((q.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** -16))
+    bias = np.zeros_like(inp["bias"])
+    S, S_o, near = _check_sigmoid(inp, dev, o, q=qs, bias=bias)
+    assert near >= 0.9 * len(S)
+    assert 0 < int((S_o > 0.5).sum()) < len(S)
