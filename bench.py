@@ -251,8 +251,11 @@ def sustained_scoring(label, B, L, idx_dt, H=64, d=128, window=8192, seed=0, rep
            "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
            "trigger_us": round(trig_us, 2)}
     if sigmoid:
+        # matrix-core dot products, and (chunk, head) sigmoids on the vector
+        # units, per second
         flops = 2.0 * nh * H * d
         out["tflops"] = round(flops / (us[kname] * 1e-6) / 1e12, 1)
+        out["sigmoids_per_ns"] = round(nh * H / (us[kname] * 1e3), 1)
     return out
 
 
@@ -495,7 +498,8 @@ def main():
         result["scoring_sustained"] = [
             sustained_scoring("500k", 64, 512000, synth.FP8, seed=101),
             sustained_scoring("128k", 64, 131072, synth.BF16, seed=102),
-            sustained_scoring("500k_union3", 64, 512000, synth.FP8, seed=106, layers=3)]
+            sustained_scoring("500k_union3", 64, 512000, synth.FP8, seed=106, layers=3),
+            sustained_scoring("500k_sigmoid", 64, 512000, synth.FP8, seed=108, sigmoid=True)]
         result["attention_sustained"] = [
             sustained_attention("500k", 4, 512000, seed=103),
             sustained_attention("500k_b8", 8, 512000, seed=104),
