@@ -479,6 +479,77 @@ int lsao_decode_units(const lsao_batch* b, int32_t n_units, const int32_t* unit_
     return err;
 }
 
+/* ------------------------------------------------------------------ */
+/* O10: attention mass per history chunk                               */
+/* ------------------------------------------------------------------ */
+
+/* The pages' oracle experiment ranks history chunks by the attention weight
+ * that the full decode actually gives them, and keeps the top 50, 25 or 10
+ * percent (cjcn.com.cn explainer, section 六).  Read here: for each given
+ * decode step j and query head h, the softmax of x_s = sm * q_{j,h} . K_s
+ * over EVERY token s of [0, L) (nothing selected, nothing left out); a
+ * history chunk's mass is the sum of those probabilities over its C tokens,
+ * over the steps and over the heads:
+ *     mass_c = sum_j sum_h sum_{s in chunk c} p_{j,h,s},
+ * and rec_mass is the same sum over the recent tokens [rs, L), so that
+ * sum_c mass_c + rec_mass = n_steps * Hq.  fp64 from the decoded inputs.
+ * q is [n_steps, Hq, Dk] in the KV dtype.  Each (step, head) unit is
+ * computed alone and the units are added in order, so the result does not
+ * depend on the thread count. */
+int lsao_chunk_mass(const lsao_batch* b, int32_t r, int32_t n_steps, const void* q, double sm,
+                    double* mass, double* rec_mass, int32_t n_threads) {
+    int64_t chunk0, rec0, g[3];
+    o_offsets(b, r, &chunk0, &rec0, g);
+    const int64_t rs = g[0], N = g[1], L = b->seq_len[r];
+    const int32_t nU = n_steps * b->Hq;
+    const int64_t kes = o_esize(b->kv_dt);
+    double* part = (double*)calloc((size_t)nU * (size_t)(N + 1), sizeof(double));
+    if (!part) return -1;
+    int err = 0;
+#ifdef _OPENMP
+    if (n_threads <= 0) n_threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads)
+#endif
+    for (int32_t u = 0; u < nU; u++) {
+        const uint8_t* qh = (const uint8_t*)q + (int64_t)u * b->Dk * kes;
+        double* pu = part + (int64_t)u * (N + 1);
+        double* x = (double*)malloc(sizeof(double) * (size_t)L);
+        if (!x) {
+#ifdef _OPENMP
+#pragma omp critical
+#endif
+            err = -1;
+            continue;
+        }
+        double m = -INFINITY;
+        for (int64_t t = 0; t < L; t++) {
+            const void* row = o_kv_row(b, chunk0, rec0, rs, t);
+            double acc = 0.0;
+            for (int32_t e = 0; e < b->Dk; e++)
+                acc += (double)o_elem(b->kv_dt, qh, e) * (double)o_elem(b->kv_dt, row, e);
+            x[t] = sm * acc;
+            if (x[t] > m) m = x[t];
+        }
+        double l = 0.0;
+        for (int64_t t = 0; t < L; t++) l += exp(x[t] - m);
+        for (int64_t t = 0; t < L; t++) {
+            const double p = exp(x[t] - m) / l;
+            if (t < rs) pu[t / b->C] += p;
+            else pu[N] += p;
+        }
+        free(x);
+    }
+    (void)n_threads;
+    for (int64_t c = 0; c <= N; c++) {
+        double acc = 0.0;
+        for (int32_t u = 0; u < nU; u++) acc += part[(int64_t)u * (N + 1) + c];
+        if (c < N) mass[c] = acc;
+        else *rec_mass = acc;
+    }
+    free(part);
+    return err;
+}
+
 int lsao_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -68,6 +68,8 @@ def load(path: str):
     _lib.lsao_decode_units.argtypes = [C.POINTER(Batch), I32, P, P, P, P, P, P, P, I32, D,
                                        P, P, P, P, I32]
     _lib.lsao_decode_units.restype = C.c_int
+    _lib.lsao_chunk_mass.argtypes = [C.POINTER(Batch), I32, I32, P, D, P, P, I32]
+    _lib.lsao_chunk_mass.restype = C.c_int
     _lib.lsao_max_threads.restype = C.c_int
     return _lib
 
@@ -215,6 +217,58 @@ class Oracle:
                                      _p(out), _p(lse), threads)
         assert rc == 0
         return [tk[i, :tc[i]].copy() for i in range(n)], out, lse
+
+
+    def chunk_mass(self, r: int, q_steps, sm: float, threads: int = 0):
+        """Attention mass of every history chunk of request r under the full
+        softmax of each given step's queries (q_steps [n_steps, Hq, Dk] in the
+        KV dtype), summed over steps and heads.  Returns (mass [N] float64,
+        recent-window mass)."""
+        q = np.ascontiguousarray(q_steps)
+        n_steps = q.shape[0]
+        n = int(self.inp["n_hist"][r])
+        mass = np.zeros(max(n, 1), np.float64)
+        rec = np.zeros(1, np.float64)
+        rc = lib().lsao_chunk_mass(C.byref(self.batch), r, n_steps, _p(q), float(sm), _p(mass),
+                                   _p(rec), threads)
+        assert rc == 0
+        return mass[:n], float(rec[0])
+
+
+# ------------------------------------------------------------------ policies
+# The pages compare LSA with a recency-only scheme (the recent 8K only), a
+# scheme that keeps a random 10 % of the history chunks, and an oracle that
+# keeps the top 50 / 25 / 10 % of history chunks by true attention weight
+# (cjcn.com.cn explainer, sections 五 and 六).  Readings: a policy keeping
+# pct percent of N chunks keeps ceil(N * pct / 100) of them; the random
+# policy keeps the chunks with the smallest of N uniformly drawn 32-bit keys
+# (a uniform sample without replacement); the oracle policy keeps the
+# chunks of largest mass; ties go to the lower chunk index; the kept chunks
+# are listed ascending.
+
+def policy_count(n: int, pct: int) -> int:
+    return (int(n) * int(pct) + 99) // 100
+
+
+def select_smallest(keys, m: int):
+    """The m chunks of smallest key, ties to the lower index, ascending."""
+    keys = np.asarray(keys)
+    order = np.lexsort((np.arange(len(keys)), keys))
+    return np.sort(order[:m]).astype(np.int32)
+
+
+def select_largest(mass, m: int):
+    """The m chunks of largest mass, ties to the lower index, ascending."""
+    mass = np.asarray(mass, dtype=np.float64)
+    order = np.lexsort((np.arange(len(mass)), -mass))
+    return np.sort(order[:m]).astype(np.int32)
+
+
+def mass_recall(mass, sel) -> float:
+    """Share of the history chunks' attention mass held by the chunks in sel."""
+    mass = np.asarray(mass, dtype=np.float64)
+    tot = mass.sum()
+    return float(mass[np.asarray(sel, dtype=np.int64)].sum() / tot) if tot > 0 else 0.0
 
 
 def sigmoid(x: float) -> float:

@@ -51,6 +51,11 @@ MUTATIONS = {
     "sigscore_weight_of_request0": ("acc_s = fmaf(w[(int64_t)r * b->H + h],", "acc_s = fmaf(w[h],"),
     "sigscore_relu": ("acc_s = fmaf(w[(int64_t)r * b->H + h], lsao_sigmoid(x), acc_s);",
                       "acc_s = fmaf(w[(int64_t)r * b->H + h], x > 0.0f ? x : 0.0f, acc_s);"),
+    "mass_chunk_index_shift": ("if (t < rs) pu[t / b->C] += p;", "if (t < rs) pu[(t + 1) / b->C] += p;"),
+    "mass_recent_left_out": ("for (int64_t t = 0; t < L; t++) l += exp(x[t] - m);",
+                             "for (int64_t t = 0; t < rs; t++) l += exp(x[t] - m);"),
+    "mass_scale_dropped": ("x[t] = sm * acc;", "x[t] = acc;"),
+    "mass_first_step_only": ("const int32_t nU = n_steps * b->Hq;", "const int32_t nU = b->Hq;"),
 }
 
 PIN_CALLS = [
@@ -71,6 +76,8 @@ PIN_CALLS = [
     "p.test_sigmoid_against_double_and_closed_forms()",
     "p.test_sigmoid_score_brute_force(0)",
     "p.test_sigmoid_score_special_cases()",
+    "p.test_chunk_mass_brute_force('f32_sep')",
+    "p.test_chunk_mass_total_and_closed_forms()",
 ]
 
 RUNNER = """

@@ -482,3 +482,93 @@ def test_sigmoid_score_special_cases():
     inp["kic"][1::2] = -0.5
     S, sel, cnt = oracle.Oracle(inp).score_select_sigmoid()
     assert (S[0::2] > 0.5).all() and (S[1::2] < 0.5).all()
+
+
+# ------------------------------------------- NEXT-3 comparison policies
+def _q_steps(inp, r):
+    return np.ascontiguousarray(inp["q_attn"][:, r])
+
+
+@pytest.mark.parametrize("kind", ["f32_sep", "bf16_latent"])
+def test_chunk_mass_brute_force(kind):
+    """Per-chunk attention mass against a dense fp64 softmax over every token
+    (numpy matrix product, then per-chunk sums of the probabilities)."""
+    if kind == "f32_sep":
+        inp = helpers.tiny_inputs()
+    else:
+        inp = synth.generate(synth.small_config(seq_lens=(700, 1500), window=256, H=2, d=16,
+                                                Hq=4, steps=2))
+    cfg = inp.cfg
+    o = oracle.Oracle(inp)
+    for r in range(cfg.batch):
+        K, _ = helpers.kv_rows(inp, r)
+        q = oracle.decode(cfg.kv_dtype, _q_steps(inp, r)).astype(np.float64).reshape(-1, cfg.Dk)
+        x = cfg.sm_scale * (q @ K.T)                        # [steps*Hq, L]
+        p = np.exp(x - x.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        rs, n = int(inp["rs"][r]), int(inp["n_hist"][r])
+        want = p[:, :rs].sum(axis=0).reshape(n, cfg.chunk).sum(axis=1)
+        mass, rec = o.chunk_mass(r, _q_steps(inp, r), cfg.sm_scale)
+        np.testing.assert_allclose(mass, want, rtol=1e-11, atol=1e-15)
+        assert math.isclose(rec, p[:, rs:].sum(), rel_tol=1e-11)
+
+
+def test_chunk_mass_total_and_closed_forms():
+    inp = helpers.tiny_inputs(seq_lens=(40, 23, 64))
+    cfg = inp.cfg
+    o = oracle.Oracle(inp)
+    for r in range(cfg.batch):
+        q = _q_steps(inp, r)
+        L, rs = int(inp["seq_len"][r]), int(inp["rs"][r])
+        units = q.shape[0] * cfg.Hq
+        mass, rec = o.chunk_mass(r, q, cfg.sm_scale)
+        # every softmax sums to one
+        assert math.isclose(mass.sum() + rec, units, rel_tol=1e-13)
+        # Q = 0: every token gets 1/L of each unit
+        mass0, rec0 = o.chunk_mass(r, np.zeros_like(q), cfg.sm_scale)
+        np.testing.assert_allclose(mass0, units * cfg.chunk / L, rtol=1e-13)
+        assert math.isclose(rec0, units * (L - rs) / L, rel_tol=1e-13)
+    # one token whose key lies along every query: its chunk takes all the mass
+    inp = helpers.tiny_inputs(seq_lens=(40, 23))
+    cfg = inp.cfg
+    r, tok = 0, 13                                   # chunk 3, a history token
+    q = np.zeros_like(_q_steps(inp, r))
+    q[..., 0] = 1.0
+    pages = inp["pages"].view(np.float32).reshape(inp["pages"].shape[0], -1)
+    rw = cfg.kv_row_bytes // 4                       # a page starts with its C KV rows
+    pages[tok // cfg.chunk, (tok % cfg.chunk) * rw] = 1e4
+    mass, rec = oracle.Oracle(inp).chunk_mass(r, q, cfg.sm_scale)
+    units = q.shape[0] * cfg.Hq
+    assert mass[tok // cfg.chunk] > units * (1 - 1e-12) and mass.argmax() == tok // cfg.chunk
+
+
+def test_chunk_mass_deterministic_across_threads():
+    inp = synth.generate(synth.small_config(seq_lens=(900,), window=256, H=2, d=16, Hq=4,
+                                            steps=2))
+    o = oracle.Oracle(inp)
+    a = o.chunk_mass(0, _q_steps(inp, 0), inp.cfg.sm_scale, threads=1)
+    b = o.chunk_mass(0, _q_steps(inp, 0), inp.cfg.sm_scale, threads=4)
+    assert np.array_equal(a[0], b[0]) and a[1] == b[1]
+
+
+def test_policy_selections_textbook():
+    rng = np.random.default_rng(3)
+    for n in (0, 1, 7, 100, 1000):
+        keys = rng.integers(0, 50, n).astype(np.uint32)   # many ties
+        mass = rng.integers(0, 50, n).astype(np.float32) / 7
+        for pct in (10, 25, 50, 100):
+            m = oracle.policy_count(n, pct)
+            assert m == -(-n * pct // 100) and m >= n * pct / 100 > m - 1 or n == 0
+            want_s = sorted(sorted(range(n), key=lambda c: (int(keys[c]), c))[:m])
+            want_l = sorted(sorted(range(n), key=lambda c: (-float(mass[c]), c))[:m])
+            assert oracle.select_smallest(keys, m).tolist() == want_s
+            assert oracle.select_largest(mass, m).tolist() == want_l
+    # all equal: the lowest indices; zero and all
+    assert oracle.select_smallest(np.zeros(9, np.uint32), 4).tolist() == [0, 1, 2, 3]
+    assert oracle.select_largest(np.ones(9, np.float32), 4).tolist() == [0, 1, 2, 3]
+    assert oracle.select_largest(np.arange(5.0), 0).tolist() == []
+    assert oracle.select_largest(np.arange(5.0), 5).tolist() == [0, 1, 2, 3, 4]
+    # recall: everything is 1, nothing is 0, the top half of a ramp is 3/4
+    mass = np.arange(1, 9, dtype=np.float64)
+    assert oracle.mass_recall(mass, range(8)) == 1.0 and oracle.mass_recall(mass, []) == 0.0
+    assert math.isclose(oracle.mass_recall(mass, oracle.select_largest(mass, 4)), 26 / 36)
