@@ -259,6 +259,92 @@ def sustained_scoring(label, B, L, idx_dt, H=64, d=128, window=8192, seed=0, rep
     return out
 
 
+def policy_comparison(inp, n_time=8, mass_steps=64, boost=2.5):
+    """The pages' comparison policies on one window of the workload: LSA's
+    threshold selection, recency-only (no history chunk), a random 10 % of
+    the history chunks, and the top 50 / 25 / 10 % of history chunks by the
+    attention mass the full decode of the window's steps gives them.  The
+    inputs get an attention focus on the indexer's planted chunks
+    (synth.attention_focus) and a cold tier in HBM.  Per policy: chunks
+    kept, bytes resident, share of the history's attention mass kept, and
+    the time of one decode step (refine, top-k, attention over the kept
+    chunks plus the recent window).  Also the attention-mass pass itself."""
+    import dataclasses
+    import numpy as np
+    import torch
+    from learned_sparse_kv_amd import lsa, runner, synth
+    t0 = time.perf_counter()
+    f = synth.attention_focus(inp, boost=boost)
+    cfg = dataclasses.replace(inp.cfg, host_cold=False)
+    f.cfg = cfg
+    dev = runner.DeviceInputs(f)
+    B, k = cfg.batch, cfg.topk
+    n_hist = [int(x) for x in f["n_hist"]]
+    off = [int(x) for x in f["chunk_off"]]
+    mass_steps = min(mass_steps, dev.q_attn.shape[0])
+    lsa.lsa_timing_reset()
+    lsa.lsa_timing_enable(True)
+    mass, rec = dev.chunk_mass(dev.q_attn[:mass_steps])
+    torch.cuda.synchronize()
+    lsa.lsa_timing_enable(False)
+    n_ml, ms_ml = lsa.lsa_timing_read("k_chunk_ml")
+    lsa.lsa_timing_reset()
+    ml_bytes = mass_steps * int(np.sum(f["seq_len"])) * 1152  # key bytes of every row, per step
+    ml_gbs = ml_bytes / (ms_ml * 1e-3) / 1e9
+    share = lambda n, pct: (n * pct + 99) // 100
+    pols = {}
+    _, sel, cnt = dev.score_select(theta=0.0, window=0)
+    pols["lsa"] = (sel, cnt)
+    pols["recency_only"] = (torch.zeros_like(sel), torch.zeros_like(cnt))
+    pols["random_10pct"] = dev.select_ranked(synth.policy_keys(f), lsa.RANK_SMALLEST_U32,
+                                             [share(n, 10) for n in n_hist])
+    for pct in (50, 25, 10):
+        pols[f"attn_mass_top{pct}pct"] = dev.select_ranked(mass, lsa.RANK_LARGEST_F32,
+                                                           [share(n, pct) for n in n_hist])
+    hist_mass = float(mass.double().sum())
+    rec_total = float(rec.double().sum())
+    full_kv = int(np.sum(f["seq_len"])) * cfg.kv_row_bytes
+    out = {"workload": cfg.name.replace("hostcold", "hbmcold") + "_window0_attention_focus",
+           "attention_focus_boost": boost, "mass_steps": mass_steps,
+           "history_mass_share": round(hist_mass / (hist_mass + rec_total), 4),
+           "chunk_mass_pass": {"k_chunk_ml_ms": round(ms_ml / max(n_ml, 1), 3), "launches": n_ml,
+                               "alg_bytes": ml_bytes, "gbs": round(ml_gbs, 1),
+                               "pct_peak": round(100 * ml_gbs / HBM_PEAK_GBS, 1)},
+           "policies": {}}
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, (sel, cnt) in pols.items():
+        torch.cuda.synchronize()
+        c = cnt.cpu().numpy()
+        keep = torch.zeros_like(mass, dtype=torch.bool)
+        s_h = sel.cpu().numpy()
+        idx = np.concatenate([off[r] + s_h[off[r]:off[r] + c[r]] for r in range(B)] + [np.zeros(0, np.int64)])
+        if len(idx):
+            keep[torch.from_numpy(idx.astype(np.int64)).cuda()] = True
+        recall = float(mass.double()[keep].sum()) / hist_mass if hist_mass > 0 else 0.0
+        for j in range(2):  # warm
+            topk, tcnt = dev.refine_topk(sel, cnt, j, k)
+            dev.attend(topk, tcnt, j, k)
+        torch.cuda.synchronize()
+        ev0.record()
+        for j in range(n_time):
+            topk, tcnt = dev.refine_topk(sel, cnt, j % dev.q_attn.shape[0], k)
+            dev.attend(topk, tcnt, j % dev.q_attn.shape[0], k)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / n_time
+        kept = int(c.sum())
+        resident = kept * cfg.chunk * cfg.kv_row_bytes + int(np.sum(f["n_rec"])) * cfg.kv_row_bytes
+        out["policies"][name] = {
+            "chunks_kept": kept, "chunk_share": round(kept / max(sum(n_hist), 1), 4),
+            "resident_gb": round(resident / 1e9, 3), "resident_share_of_full_kv": round(resident / full_kv, 4),
+            "history_mass_recall": round(recall, 4),
+            "step_ms": round(ms, 3), "steps_per_s": round(1e3 / ms, 1)}
+    del dev, mass, rec, pols
+    torch.cuda.empty_cache()
+    out["seconds"] = round(time.perf_counter() - t0, 1)
+    return out
+
+
 def sustained_attention(label, B, L, nbatch=6, reps=3, k=2048, Hq=64, Dk=576, Dv=512,
                         window=8192, seed=0):
     """lsa_sparse_decode_attn rotating over nbatch independent batches (pages,
@@ -329,6 +415,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sustained", action="store_true",
                     help="skip the cold-cache scoring / attention GB/s points at 128K and 500K")
+    ap.add_argument("--no-policies", action="store_true",
+                    help="skip the comparison policies (recency-only, random 10 %%, attention-mass top shares)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -512,6 +600,9 @@ def main():
         log(f"[bench] sustained points in {time.perf_counter() - t0:.1f}s: "
             + json.dumps({"scoring": result["scoring_sustained"],
                           "attention": result["attention_sustained"]}))
+    if not args.no_policies:
+        result["policy_comparison"] = policy_comparison(inp)
+        log("[bench] policies: " + json.dumps(result["policy_comparison"]))
     if not args.no_cpu_baseline:
         threads = min(16, len(os.sched_getaffinity(0)))
         result["cpu_baseline"] = cpu_baseline(inp, cfg, threads)

@@ -235,6 +235,50 @@ lsa_status lsa_sparse_decode_attn(const lsa_geom* g, const void* q, int32_t Hq,
                                   void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Comparison policies.  The pages set LSA against a recency-only scheme
+ * (the recent 8K tokens only: lsa_select_threshold with theta = +inf), a
+ * scheme that keeps a random 10 % of the history chunks, and an oracle that
+ * keeps the top 50 / 25 / 10 % of history chunks by the attention weight
+ * the full decode gives them (cjcn.com.cn explainer, sections 五 and 六).
+ *
+ * lsa_select_ranked keeps, per request r, the min(m[r], N_r) best history
+ * chunks by a per-chunk key, ties to the lower chunk, and lists them
+ * ascending in sel_ids like lsa_select_threshold:
+ *   LSA_RANK_SMALLEST_U32  keys (device) [sum N] uint32, smallest first
+ *                          (uniform random keys give a uniform sample);
+ *   LSA_RANK_LARGEST_F32   keys (device) [sum N] f32 (no NaN), largest first
+ *                          (-0 ranks as +0).
+ *   m (host) [B] int32 >= 0;  sel_ids (device) [sum N];  sel_cnt (device) [B]
+ * No workspace.
+ * ---------------------------------------------------------------------- */
+typedef enum { LSA_RANK_SMALLEST_U32 = 0, LSA_RANK_LARGEST_F32 = 1 } lsa_rank_kind;
+
+lsa_status lsa_select_ranked(const lsa_geom* g, const void* keys, lsa_rank_kind kind,
+                             const int32_t* m, int32_t* sel_ids, int32_t* sel_cnt, void* stream);
+
+/* lsa_chunk_attn_mass: the attention mass of every history chunk under the
+ * full softmax of n_steps decode steps' queries over EVERY token [0, L_r):
+ *     mass[c] = sum_j sum_h sum_{s in chunk c} p_{j,h,s},
+ *     p_{j,h,s} = softmax over s of sm_scale * q[j,r,h] . K_s,
+ * and rec_mass[r] the same sum over the recent tokens [rs_r, L_r), so that
+ * sum_c mass[c] + rec_mass[r] = n_steps * Hq up to rounding.  fp32
+ * arithmetic (scores on the matrix cores from the bf16 rows, fp32
+ * accumulation).  The history rows are read from pages (page_table or the
+ * identity, as lsa_sparse_decode_attn), the recent ones from recent.
+ *   q (device) [n_steps, B, Hq, Dk] in the KV dtype
+ *   mass (device) [sum N] f32 out;  rec_mass (device) [B] f32 out
+ *   ws (device) >= lsa_chunk_mass_ws_bytes(g, Hq, n_steps) bytes
+ * Supported: bf16 latent rows (Dk 576, v_off 0), Hq a multiple of 64,
+ * 1 <= n_steps and n_steps * Hq <= 16384.
+ * ---------------------------------------------------------------------- */
+size_t lsa_chunk_mass_ws_bytes(const lsa_geom* g, int32_t Hq, int32_t n_steps);
+lsa_status lsa_chunk_attn_mass(const lsa_geom* g, const void* q, int32_t Hq, int32_t n_steps,
+                               const lsa_kv_layout* kv, const void* pages,
+                               const int32_t* page_table, const void* recent, float sm_scale,
+                               float* mass, float* rec_mass, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* ------------------------------------------------------------------------
  * a4. Slot pool and candidate fetch.  Selected chunks move from the cold
  * pool (CPU memory) into GPU memory; the rest stay behind (cjcn.com.cn
  * section 二 and Q&A 1; gist.science 2.1 "Dynamisches Fetching").
@@ -345,7 +389,7 @@ lsa_status lsa_step64(lsa_ctx* ctx, const lsa_window_in* in, lsa_window_out* out
  * the recorded events and returns, for one kernel name (k_fuse_query,
  * k_score, k_select, k_refine, k_topk, k_refine_mfma, k_band_fine,
  * k_band_list, k_topk_band, k_attn_mla, k_attn_f32, k_attn_merge,
- * k_gather, k_stream_read, k_score_sig), the number of timed launches and their summed duration in
+ * k_gather, k_stream_read, k_score_sig, k_select_ranked, k_chunk_ml), the number of timed launches and their summed duration in
  * milliseconds since the last reset.  lsa_timing_only(name) restricts the
  * timing to that one kernel (NULL: all; a name of 64 or more characters is
  * LSA_ERR_INVALID_ARG), so that one kernel can be timed inside a run with

@@ -15,6 +15,15 @@
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static int64_t esize(lsa_dtype t) { return t == LSA_F32 ? 4 : (t == LSA_BF16 ? 2 : 1); }
 
+static lsa_status check_kv(const lsa_kv_layout* kv) {
+    if (!kv) return LSA_ERR_INVALID_ARG;
+    if (kv->Dk < 1 || kv->Dv < 1 || kv->v_off < 0) return LSA_ERR_INVALID_ARG;
+    const int64_t need = esize(kv->kv_dtype) * (kv->Dk > kv->v_off + kv->Dv ? kv->Dk : kv->v_off + kv->Dv);
+    if (kv->row_bytes < need) return LSA_ERR_INVALID_ARG;
+    if (kv->page_bytes < kv->row_bytes * LSA_CHUNK) return LSA_ERR_INVALID_ARG;
+    return LSA_OK;
+}
+
 lsa_status geom_derive(const lsa_geom* g, GeomDev* d) {
     if (!g || !d || !g->seq_len) return LSA_ERR_INVALID_ARG;
     if (g->batch < 1 || g->batch > LSA_MAX_BATCH) return LSA_ERR_INVALID_ARG;
@@ -160,6 +169,71 @@ lsa_status lsa_select_threshold(const lsa_geom* g, const float* z, float theta, 
     return LSA_OK;
 }
 
+lsa_status lsa_select_ranked(const lsa_geom* g, const void* keys, lsa_rank_kind kind,
+                             const int32_t* m, int32_t* sel_ids, int32_t* sel_cnt, void* stream) {
+    GeomDev gd;
+    lsa_status st = geom_derive(g, &gd);
+    if (st != LSA_OK) return st;
+    if (!m || !sel_cnt) return LSA_ERR_INVALID_ARG;
+    if (kind != LSA_RANK_SMALLEST_U32 && kind != LSA_RANK_LARGEST_F32) return LSA_ERR_INVALID_ARG;
+    if (gd.chunk_off[gd.B] > 0 && (!keys || !sel_ids)) return LSA_ERR_INVALID_ARG;
+    RankCounts rc;
+    for (int r = 0; r < gd.B; ++r) {
+        if (m[r] < 0) return LSA_ERR_INVALID_ARG;
+        rc.m[r] = m[r];
+    }
+    LSA_HIP(launch_select_ranked(gd, keys, (int)kind, rc, sel_ids, sel_cnt, (hipStream_t)stream));
+    return LSA_OK;
+}
+
+static size_t mass_ws_layout(const GeomDev& gd, int Hq, int n_steps, MassGeom* mg, size_t* o_lse,
+                             size_t* o_rec) {
+    mass_geom(gd, Hq, n_steps, mg);
+    size_t off = align_up((size_t)mg->ml_total * 8, 256);
+    *o_lse = off;
+    off += align_up((size_t)gd.B * n_steps * Hq * 4, 256);
+    *o_rec = off;
+    off += align_up((size_t)mg->rc_total * 4 + 4, 256);
+    return off;
+}
+
+size_t lsa_chunk_mass_ws_bytes(const lsa_geom* g, int32_t Hq, int32_t n_steps) {
+    GeomDev gd;
+    if (geom_derive(g, &gd) != LSA_OK || Hq < 1 || n_steps < 1) return 0;
+    MassGeom mg;
+    size_t a, b;
+    return mass_ws_layout(gd, Hq, n_steps, &mg, &a, &b);
+}
+
+lsa_status lsa_chunk_attn_mass(const lsa_geom* g, const void* q, int32_t Hq, int32_t n_steps,
+                               const lsa_kv_layout* kv, const void* pages,
+                               const int32_t* page_table, const void* recent, float sm_scale,
+                               float* mass, float* rec_mass, void* ws, size_t ws_bytes,
+                               void* stream) {
+    GeomDev gd;
+    lsa_status st = geom_derive(g, &gd);
+    if (st != LSA_OK) return st;
+    st = check_kv(kv);
+    if (st != LSA_OK) return st;
+    if (kv->kv_dtype != LSA_BF16 || kv->Dk != 576 || kv->v_off != 0 || kv->row_bytes % 16 != 0 ||
+        kv->page_bytes % 16 != 0)
+        return LSA_ERR_UNSUPPORTED;
+    if (Hq < 64 || Hq % 64 != 0 || n_steps < 1 || (int64_t)n_steps * Hq > 16384)
+        return LSA_ERR_UNSUPPORTED;
+    if (!q || !recent || !rec_mass || !ws || !(sm_scale == sm_scale)) return LSA_ERR_INVALID_ARG;
+    if (gd.chunk_off[gd.B] > 0 && (!pages || !mass)) return LSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(recent) || !aligned16(ws) || (pages && !aligned16(pages)))
+        return LSA_ERR_INVALID_ARG;
+    MassGeom mg;
+    size_t o_lse, o_rec;
+    if (ws_bytes < mass_ws_layout(gd, Hq, n_steps, &mg, &o_lse, &o_rec)) return LSA_ERR_WORKSPACE;
+    uint8_t* w = (uint8_t*)ws;
+    LSA_HIP(launch_chunk_mass(gd, mg, q, Hq, n_steps, pages, kv->page_bytes, page_table, recent,
+                              kv->row_bytes, sm_scale, mass, rec_mass, (float2*)w, (float*)(w + o_lse),
+                              (float*)(w + o_rec), (hipStream_t)stream));
+    return LSA_OK;
+}
+
 size_t lsa_refine_ws_bytes(const lsa_geom* g, int32_t k) {
     GeomDev gd;
     (void)k;
@@ -207,15 +281,6 @@ lsa_status lsa_topk_refine(const lsa_geom* g, const int32_t* sel_ids, const int3
         LSA_HIP(launch_refine(gd, sel_ids, sel_cnt, pages, page_bytes, ikey_off, page_table, idx_dt,
                               ikey_scale, q, q_dt, w, H, d, scores, 0, s));
     LSA_HIP(launch_topk(gd, sel_ids, sel_cnt, scores, k, topk_idx, topk_cnt, s));
-    return LSA_OK;
-}
-
-static lsa_status check_kv(const lsa_kv_layout* kv) {
-    if (!kv) return LSA_ERR_INVALID_ARG;
-    if (kv->Dk < 1 || kv->Dv < 1 || kv->v_off < 0) return LSA_ERR_INVALID_ARG;
-    const int64_t need = esize(kv->kv_dtype) * (kv->Dk > kv->v_off + kv->Dv ? kv->Dk : kv->v_off + kv->Dv);
-    if (kv->row_bytes < need) return LSA_ERR_INVALID_ARG;
-    if (kv->page_bytes < kv->row_bytes * LSA_CHUNK) return LSA_ERR_INVALID_ARG;
     return LSA_OK;
 }
 

@@ -45,6 +45,28 @@ hipError_t launch_refine(const GeomDev& g, const int32_t* sel, const int32_t* cn
 hipError_t launch_topk(const GeomDev& g, const int32_t* sel, const int32_t* cnt,
                        const float* scores, int k, int32_t* topk, int32_t* tcnt, hipStream_t s);
 
+// Per-request keep counts of lsa_select_ranked (by value).
+struct RankCounts {
+    int32_t m[LSA_MAX_BATCH];
+};
+// Pseudo-chunks of the attention-mass pass: the history chunks, then the
+// recent window cut into 64-token pieces; offsets of each request's
+// (m, l) partials and recent-window pieces.
+struct MassGeom {
+    int32_t nc[LSA_MAX_BATCH];
+    int32_t rc_off[LSA_MAX_BATCH];
+    int64_t ml_off[LSA_MAX_BATCH];
+    int64_t ml_total;
+    int64_t rc_total;
+};
+void mass_geom(const GeomDev& g, int Hq, int n_steps, MassGeom* mg);
+hipError_t launch_select_ranked(const GeomDev& g, const void* keys, int kind, const RankCounts& m,
+                                int32_t* sel, int32_t* cnt, hipStream_t s);
+hipError_t launch_chunk_mass(const GeomDev& g, const MassGeom& mg, const void* q, int Hq, int n_steps,
+                             const void* pages, int64_t page_bytes, const int32_t* page_table,
+                             const void* recent, int64_t row_bytes, float sm_scale, float* mass,
+                             float* rec, float2* ml, float* lse2, float* recbuf, hipStream_t s);
+
 struct AttnPlan {
     int mode;        // 0: f32 VALU, 1: bf16 MFMA latent 576/512
     int n_splits;    // splits per request

@@ -1,5 +1,5 @@
-// Device helpers shared by the matrix-core kernels that carry a rigorous
-// error bound (refine band, sigmoid chunk score).  Included by .hip sources only.
+// Device helpers shared by the matrix-core kernels (refine band, sigmoid
+// chunk score, chunk attention mass).  Included by .hip sources only.
 #pragma once
 
 #include "lsa_internal.h"
@@ -54,6 +54,15 @@ __device__ __forceinline__ float add_xor16(float x) {
 __device__ __forceinline__ float add_xor32(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 }  // namespace lsa_dev

@@ -86,6 +86,10 @@ def _load():
         "lsa_select_threshold": ([G, P, F, P, P, P], I),
         "lsa_score_chunks_union": ([G, I32, P, I, P, P, I32, I32, P, I, P, P, P, SZ, P], I),
         "lsa_score_chunks_sigmoid": ([G, P, I, P, P, F, I32, I32, P, I, P, P, P], I),
+        "lsa_select_ranked": ([G, P, I, P, P, P, P], I),
+        "lsa_chunk_mass_ws_bytes": ([G, I32, I32], SZ),
+        "lsa_chunk_attn_mass": ([G, P, I32, I32, C.POINTER(lsa_kv_layout), P, P, P, F, P, P, P, SZ, P],
+                                I),
         "lsa_refine_ws_bytes": ([G, I32], SZ),
         "lsa_topk_refine": ([G, P, P, P, I64, I64, P, I, P, P, I, P, I32, I32, I32, P, P, P, SZ,
                              P], I),
@@ -188,6 +192,29 @@ def lsa_score_chunks_sigmoid(g: Geom, q, q_dt, w, bias, theta, H, d, kic, kic_dt
     _check("lsa_score_chunks_sigmoid",
            _lib.lsa_score_chunks_sigmoid(g.ref, _ptr(q), q_dt, _ptr(w), _ptr(bias), float(theta), H, d,
                                          _ptr(kic), kic_dt, _ptr(kic_scale), _ptr(S), _stream(stream)))
+
+
+RANK_SMALLEST_U32, RANK_LARGEST_F32 = 0, 1
+
+
+def lsa_select_ranked(g: Geom, keys, kind, m, sel_ids, sel_cnt, stream=None):
+    m = np.ascontiguousarray(m, dtype=np.int32)
+    _check("lsa_select_ranked",
+           _lib.lsa_select_ranked(g.ref, _ptr(keys), int(kind), m.ctypes.data, _ptr(sel_ids),
+                                  _ptr(sel_cnt), _stream(stream)))
+
+
+def lsa_chunk_mass_ws_bytes(g: Geom, Hq, n_steps):
+    return _lib.lsa_chunk_mass_ws_bytes(g.ref, Hq, n_steps)
+
+
+def lsa_chunk_attn_mass(g: Geom, q, Hq, n_steps, kv: lsa_kv_layout, pages, page_table, recent, sm_scale,
+                        mass, rec_mass, ws, stream=None):
+    _check("lsa_chunk_attn_mass",
+           _lib.lsa_chunk_attn_mass(g.ref, _ptr(q), Hq, n_steps, C.byref(kv), _ptr(pages),
+                                    _ptr(page_table), _ptr(recent), float(sm_scale), _ptr(mass),
+                                    _ptr(rec_mass), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)))
 
 
 def lsa_select_threshold(g: Geom, z, theta, sel_ids, sel_cnt, stream=None):
@@ -303,7 +330,7 @@ def lsa_step64(ctx: Ctx, win, out, main=None, copy=None):
 # ---------------------------------------------------------------- diagnostics
 KERNELS = ("k_fuse_query", "k_score", "k_select", "k_refine", "k_topk", "k_refine_mfma",
            "k_band_fine", "k_band_list", "k_topk_band", "k_attn_mla", "k_attn_f32", "k_attn_merge",
-           "k_gather", "k_stream_read", "k_score_sig")
+           "k_gather", "k_stream_read", "k_score_sig", "k_select_ranked", "k_chunk_ml")
 
 
 def lsa_timing_enable(on: bool):

@@ -86,6 +86,32 @@ class DeviceInputs:
         lsa.lsa_select_threshold(self.geom, S, theta, sel, cnt, stream)
         return S[:self.nh], sel, cnt
 
+    def select_ranked(self, keys, kind, m, stream=None):
+        """The m[r] best history chunks of each request by key (host array
+        or device tensor), ties to the lower chunk, ascending."""
+        d = self.device
+        if isinstance(keys, np.ndarray):
+            keys = _dev(np.ascontiguousarray(keys), d)
+        sel = torch.full((max(self.nh, 1),), -1, dtype=torch.int32, device=d)
+        cnt = torch.zeros(self.B, dtype=torch.int32, device=d)
+        lsa.lsa_select_ranked(self.geom, keys, kind, m, sel, cnt, stream)
+        return sel, cnt
+
+    def chunk_mass(self, q_steps=None, pages=None, page_table=None, stream=None):
+        """Attention mass of every history chunk under the full softmax of
+        the given steps' queries ([n_steps, B, Hq, Dk]; all the inputs'
+        steps by default), and each request's recent-window mass."""
+        cfg, d = self.cfg, self.device
+        q = self.q_attn if q_steps is None else q_steps
+        pages = self.pages if pages is None else pages
+        n_steps = q.shape[0]
+        mass = torch.empty(max(self.nh, 1), dtype=torch.float32, device=d)
+        rec = torch.empty(self.B, dtype=torch.float32, device=d)
+        ws = _ws(lsa.lsa_chunk_mass_ws_bytes(self.geom, cfg.Hq, n_steps), d)
+        lsa.lsa_chunk_attn_mass(self.geom, q, cfg.Hq, n_steps, self.kv, pages, page_table, self.recent,
+                                cfg.sm_scale, mass, rec, ws, stream)
+        return mass[:self.nh], rec
+
     def score_select_union(self, layers, theta=0.0, stream=None):
         """OR-mode union over indexer layers (list of dicts with q_coarse,
         w_coarse, bias, kic, kic_scale as host arrays)."""

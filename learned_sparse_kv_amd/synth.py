@@ -185,6 +185,8 @@ def seq_lens_of(cfg: LsaConfig):
 # ----------------------------------------------------------------------------
 _T_KIC, _T_PLANT, _T_QC, _T_IKEY, _T_KVH, _T_KVR, _T_QR, _T_QA, _T_DRIFT = range(9)
 _T_LAYER = 100  # tensor ids of indexer layer l >= 1: _T_LAYER + 10 l + {0: KIComp, 1: planted, 2: query}
+_T_POLICY = 200  # random-policy keys of window w: _T_POLICY + w
+_T_FOCUS = 300
 
 
 def _rng(root: np.random.SeedSequence, tensor: int, req: int = 0):
@@ -319,6 +321,54 @@ def small_config(name="small_bf16", seed=11, seq_lens=(5000, 3000), window=1024,
                      q_dtype=(F32 if kv == F32 else BF16) if q_dtype is None else q_dtype,
                      idx_dtype=idx, planted=planted, topk=topk, Hq=Hq, Dk=Dk, Dv=Dv,
                      kv_dtype=kv, separate_v=separate_v, steps=steps)
+
+
+def attention_focus(inp: Inputs, boost: float = 2.5, window: int = 0) -> Inputs:
+    """A copy of inp in which attention prefers the planted chunks of the
+    given window, as the method presumes (the indexer predicts the history
+    the next steps attend to).  Per request, one seeded unit direction v_r
+    (Dk dims) is added with weight a = sqrt(boost / sm) to the key part of
+    every KV row of those chunks and to every attention query, so that
+    sm * q . k rises by about boost (natural-log units) for their tokens.
+    Only pages and q_attn change; the copy owns new arrays for them."""
+    cfg = inp.cfg
+    if cfg.kv_dtype != BF16:
+        raise ValueError("attention_focus writes bf16 rows")
+    root = np.random.SeedSequence(cfg.seed)
+    a = np.sqrt(boost / cfg.sm_scale)
+    C, Dk, rw = cfg.chunk, cfg.Dk, cfg.kv_row_bytes // 2
+    out = Inputs(inp)
+    out.cfg = cfg
+    pages = inp["pages"].copy()
+    qa = (inp["q_attn"].astype(np.uint32) << 16).view(np.float32).copy()
+    for r in range(cfg.batch):
+        v = _rng(root, _T_FOCUS, r).standard_normal(Dk)
+        v = (v / np.linalg.norm(v) * a).astype(np.float32)
+        qa[:, r] += v
+        pl = np.asarray(inp["planted"][window][r], dtype=np.int64)
+        if len(pl) == 0:
+            continue
+        rows = pages[int(inp["chunk_off"][r]) + pl, :cfg.ikey_off].view(np.uint16).reshape(len(pl), C, rw)
+        k = (rows[:, :, :Dk].astype(np.uint32) << 16).view(np.float32) + v
+        rows[:, :, :Dk] = to_bf16_bits(k)
+        pages[int(inp["chunk_off"][r]) + pl, :cfg.ikey_off] = rows.reshape(len(pl), -1).view(np.uint8)
+    out["pages"] = pages
+    out["q_attn"] = to_bf16_bits(qa)
+    return out
+
+
+def policy_keys(inp: Inputs, window: int = 0) -> np.ndarray:
+    """Uniform 32-bit keys, one per history chunk ([sum N] uint32, one stream
+    per request and window): keeping the chunks of smallest key is a uniform
+    random sample without replacement (the random-share policy)."""
+    cfg = inp.cfg
+    root = np.random.SeedSequence(cfg.seed)
+    n_hist = inp["n_hist"]
+    out = np.zeros(int(inp["chunk_off"][-1]), np.uint32)
+    for r in range(cfg.batch):
+        a, n = int(inp["chunk_off"][r]), int(n_hist[r])
+        out[a:a + n] = _rng(root, _T_POLICY + window, r).integers(0, 2 ** 32, n, dtype=np.uint32)
+    return out
 
 
 def indexer_layers(inp: Inputs, n_layers: int = 3, window: int = 0):
