@@ -345,6 +345,67 @@ def policy_comparison(inp, n_time=8, mass_steps=64, boost=2.5):
     return out
 
 
+def growing_decode(inp, n_windows=4):
+    """Growing-context decode on the workload's shapes: every request starts
+    64 * n_windows tokens short of the workload's context and gains one token
+    per step (lsa_append_kv); each 64-step window starts with a trigger
+    (scoring and selection of the current history) and ends with
+    lsa_commit_chunk (the recent region's oldest full chunk joins the
+    history).  Cold tier in HBM; the per-step queries repeat after the
+    inputs' 64.  Window 0 runs with per-kernel timing (append and commit
+    times); the other windows are timed with events."""
+    import numpy as np
+    import torch
+    from learned_sparse_kv_amd import lsa, runner
+    cfg = inp.cfg
+    k = cfg.topk
+    L0 = np.asarray(inp["seq_len"], np.int64) - 64 * n_windows
+    t0 = time.perf_counter()
+    g = runner.Growing(inp, L0, n_windows)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+
+    def window(m):
+        g.trigger()
+        for _ in range(64):
+            g.step(k)
+        g.commit(m)
+
+    lsa.lsa_timing_reset()
+    lsa.lsa_timing_enable(True)
+    window(0)
+    torch.cuda.synchronize()
+    lsa.lsa_timing_enable(False)
+    kt = {}
+    for name in ("k_append_kv", "k_commit_chunk", "k_score", "k_select", "k_attn_mla", "k_refine_mfma"):
+        n, ms = lsa.lsa_timing_read(name)
+        if n:
+            kt[name] = {"launches": n, "avg_us": round(ms * 1e3 / n, 2)}
+    lsa.lsa_timing_reset()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    w0 = time.perf_counter()
+    for m in range(1, n_windows):
+        window(m)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1)
+    steps = 64 * (n_windows - 1)
+    commit_bytes = 2 * int(np.sum(np.asarray(inp["n_rec"]))) * cfg.kv_row_bytes  # recent rows read + written
+    out = {"workload": cfg.name.replace("hostcold", "hbmcold") + "_growing",
+           "start_context": int(L0[0]), "end_context": int(inp["seq_len"][0]), "windows_timed": n_windows - 1,
+           "steps_timed": steps, "decode_steps_per_s": round(steps / (ms * 1e-3), 1),
+           "ms_per_step": round(ms / steps, 4), "wall_steps_per_s": round(steps / wall, 1),
+           "history_chunks_end": [int(x) // cfg.chunk for x in g.rs],
+           "kernels_window0": kt, "commit_moved_bytes": commit_bytes, "setup_s": round(setup_s, 1)}
+    if "k_commit_chunk" in kt:
+        out["commit_gbs"] = round(commit_bytes / (kt["k_commit_chunk"]["avg_us"] * 1e-6) / 1e9, 1)
+    del g
+    torch.cuda.empty_cache()
+    return out
+
+
 def sustained_attention(label, B, L, nbatch=6, reps=3, k=2048, Hq=64, Dk=576, Dv=512,
                         window=8192, seed=0):
     """lsa_sparse_decode_attn rotating over nbatch independent batches (pages,
@@ -415,6 +476,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sustained", action="store_true",
                     help="skip the cold-cache scoring / attention GB/s points at 128K and 500K")
+    ap.add_argument("--no-growing", action="store_true",
+                    help="skip the growing-context decode (append per step, chunk commit per window)")
     ap.add_argument("--no-policies", action="store_true",
                     help="skip the comparison policies (recency-only, random 10 %%, attention-mass top shares)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -603,6 +666,9 @@ def main():
     if not args.no_policies:
         result["policy_comparison"] = policy_comparison(inp)
         log("[bench] policies: " + json.dumps(result["policy_comparison"]))
+    if not args.no_growing:
+        result["growing_context"] = growing_decode(inp)
+        log("[bench] growing context: " + json.dumps(result["growing_context"]))
     if not args.no_cpu_baseline:
         threads = min(16, len(os.sched_getaffinity(0)))
         result["cpu_baseline"] = cpu_baseline(inp, cfg, threads)

@@ -39,7 +39,19 @@
  *     chunk_off[r] = sum_{i<r} N_i,   rec_off[r] = sum_{i<r} R_i
  * Arrays "over chunks" are concatenated over requests: request r owns
  * entries [chunk_off[r], chunk_off[r] + N_r).  Recent KV rows likewise own
- * rows [rec_off[r], rec_off[r] + R_r).
+ * rows [rec_off[r], rec_off[r] + R_r).  "[sum N]" below means
+ * chunk_off[B] entries and "[sum R]" rec_off[B] rows.
+ *
+ * Growing context.  During decode every step appends one token, and at each
+ * trigger the oldest full chunk of the recent region joins the history.
+ * For that the
+ * geometry can fix rs_r explicitly (hist_tokens, so the recent region stays
+ * anchored between triggers while L_r grows), and give each request fixed
+ * capacities so that one request's growth moves no other's rows:
+ *     chunk_cap > 0:  chunk_off[r] = r * chunk_cap   (N_r <= chunk_cap)
+ *     recent_cap > 0: rec_off[r]   = r * recent_cap  (R_r <= recent_cap)
+ * Every entry point reads its arrays through chunk_off and rec_off, so the
+ * same kernels serve both layouts.
  *
  * Pages.  The cold tier and the HBM slot pool store one chunk per page of
  * page_bytes: C KV rows of row_bytes, then, at byte ikey_off, C index-key
@@ -73,12 +85,17 @@ typedef enum {
 typedef enum { LSA_F32 = 0, LSA_BF16 = 1, LSA_FP8_E4M3FN = 2 } lsa_dtype;
 
 /* Batch geometry.  seq_len is a host array of B contexts (each >= 1); the
- * library derives rs, N, R and the offsets above from it. */
+ * library derives rs, N, R and the offsets above from it.  The last three
+ * fields are zero / NULL for the packed layout. */
 typedef struct {
-    int32_t batch;          /* B, 1..LSA_MAX_BATCH                      */
-    int32_t chunk;          /* C, must be LSA_CHUNK (64)                */
-    int32_t window;         /* W >= 0, recent tokens always attended    */
-    const int32_t* seq_len; /* (host) [B]                               */
+    int32_t batch;              /* B, 1..LSA_MAX_BATCH                          */
+    int32_t chunk;              /* C, must be LSA_CHUNK (64)                    */
+    int32_t window;             /* W >= 0, recent tokens always attended        */
+    const int32_t* seq_len;     /* (host) [B]                                   */
+    const int32_t* hist_tokens; /* (host) [B] rs_r (a multiple of C, <= L_r), or
+                                   NULL for C * floor(max(L_r - W, 0) / C)      */
+    int32_t chunk_cap;          /* > 0: chunk_off[r] = r * chunk_cap            */
+    int32_t recent_cap;         /* > 0: rec_off[r] = r * recent_cap             */
 } lsa_geom;
 
 /* Layout of one KV row and of a page. */
@@ -235,6 +252,44 @@ lsa_status lsa_sparse_decode_attn(const lsa_geom* g, const void* q, int32_t Hq,
                                   void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Growing context (geometry with recent_cap > 0 and chunk_cap > 0; see the
+ * top of this file).  The pages' indexer fires every 64 decode steps to
+ * predict the history the next 64 steps need (cjcn.com.cn explainer,
+ * section 二); between triggers each step adds one token to the recent
+ * region, and at a trigger the region's oldest full chunk becomes history.
+ *
+ * lsa_append_kv writes each request's newest token: row r of rows goes to
+ * recent row rec_off[r] + (L_r - 1 - rs_r).  g must already count the new
+ * token (L_r - 1 >= rs_r).
+ *   rows (device) [B, kv->row_bytes];  recent (device) [B * recent_cap rows]
+ *
+ * lsa_commit_chunk moves, for every request with R_r >= W + C (g before the
+ * commit), the chunk c = N_r made of recent rows [0, C) into the history:
+ * its KV rows into cold page chunk_off[r] + c, new_ikeys[r] (its C
+ * index-key rows, d elements in idx_dt) to the same page at kv->ikey_off,
+ * new_kic[r] (its KIComp row) to kic row chunk_off[r] + c, and the fp8
+ * scales (new_ikey_scale[r], new_kic_scale[r]) to ikey_scale / kic_scale;
+ * recent rows [C, R_r) move to recent_dst rows [0, R_r - C).  Other requests
+ * copy recent rows [0, R_r) to recent_dst unchanged.  hist_out (host) [B]
+ * receives the new rs_r (rs_r + C or rs_r), written before the call returns.
+ *   cold (device or pinned host) cold-tier page array, identity-indexed
+ *   recent_src, recent_dst (device, not overlapping) [B * recent_cap rows]
+ *   new_ikeys (device) [B, C, d];  new_kic (device) [B, d]  (idx_dt)
+ *   new_ikey_scale, new_kic_scale (device) [B] f32, fp8 only (else NULL)
+ *   kic (device) [B * chunk_cap, d];  kic_scale, ikey_scale (device)
+ *   [B * chunk_cap] f32, fp8 only
+ * Needs N_r + 1 <= chunk_cap for every committing request.
+ * ---------------------------------------------------------------------- */
+lsa_status lsa_append_kv(const lsa_geom* g, const lsa_kv_layout* kv, const void* rows,
+                         void* recent, void* stream);
+lsa_status lsa_commit_chunk(const lsa_geom* g, const lsa_kv_layout* kv, const void* recent_src,
+                            void* recent_dst, void* cold, lsa_dtype idx_dt, int32_t d,
+                            const void* new_ikeys, const float* new_ikey_scale,
+                            float* ikey_scale, const void* new_kic,
+                            const float* new_kic_scale, void* kic, float* kic_scale,
+                            int32_t* hist_out, void* stream);
+
+/* ------------------------------------------------------------------------
  * Comparison policies.  The pages set LSA against a recency-only scheme
  * (the recent 8K tokens only: lsa_select_threshold with theta = +inf), a
  * scheme that keeps a random 10 % of the history chunks, and an oracle that
@@ -389,7 +444,8 @@ lsa_status lsa_step64(lsa_ctx* ctx, const lsa_window_in* in, lsa_window_out* out
  * the recorded events and returns, for one kernel name (k_fuse_query,
  * k_score, k_select, k_refine, k_topk, k_refine_mfma, k_band_fine,
  * k_band_list, k_topk_band, k_attn_mla, k_attn_f32, k_attn_merge,
- * k_gather, k_stream_read, k_score_sig, k_select_ranked, k_chunk_ml), the number of timed launches and their summed duration in
+ * k_gather, k_stream_read, k_score_sig, k_select_ranked, k_chunk_ml, k_append_kv,
+ * k_commit_chunk), the number of timed launches and their summed duration in
  * milliseconds since the last reset.  lsa_timing_only(name) restricts the
  * timing to that one kernel (NULL: all; a name of 64 or more characters is
  * LSA_ERR_INVALID_ARG), so that one kernel can be timed inside a run with

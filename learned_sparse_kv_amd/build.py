@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "liblsa.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["score_select.hip", "score_sigmoid.hip", "policy.hip", "refine_topk.hip", "refine_band.hip", "attn_decode.hip", "gather.hip",
+SOURCES = ["score_select.hip", "score_sigmoid.hip", "policy.hip", "grow.hip", "refine_topk.hip", "refine_band.hip", "attn_decode.hip", "gather.hip",
            "api.cpp", "pool.cpp", "step64.cpp", "timing.cpp"]
 
 # -ffp-contract=off + explicit fmaf: the scores that decide selections follow

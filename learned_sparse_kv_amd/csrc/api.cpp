@@ -28,6 +28,7 @@ lsa_status geom_derive(const lsa_geom* g, GeomDev* d) {
     if (!g || !d || !g->seq_len) return LSA_ERR_INVALID_ARG;
     if (g->batch < 1 || g->batch > LSA_MAX_BATCH) return LSA_ERR_INVALID_ARG;
     if (g->chunk != LSA_CHUNK || g->window < 0) return LSA_ERR_INVALID_ARG;
+    if (g->chunk_cap < 0 || g->recent_cap < 0) return LSA_ERR_INVALID_ARG;
     std::memset(d, 0, sizeof(*d));
     d->B = g->batch;
     d->W = g->window;
@@ -36,20 +37,30 @@ lsa_status geom_derive(const lsa_geom* g, GeomDev* d) {
     for (int r = 0; r < g->batch; ++r) {
         const int32_t L = g->seq_len[r];
         if (L < 1) return LSA_ERR_INVALID_ARG;
-        int64_t h = (int64_t)L - g->window;
-        if (h < 0) h = 0;
-        const int64_t rs = (int64_t)LSA_CHUNK * (h / LSA_CHUNK);
+        int64_t rs;
+        if (g->hist_tokens) {
+            rs = g->hist_tokens[r];
+            if (rs < 0 || rs > L || rs % LSA_CHUNK != 0) return LSA_ERR_INVALID_ARG;
+        } else {
+            int64_t h = (int64_t)L - g->window;
+            if (h < 0) h = 0;
+            rs = (int64_t)LSA_CHUNK * (h / LSA_CHUNK);
+        }
         d->L[r] = L;
         d->rs[r] = (int32_t)rs;
         d->nhist[r] = (int32_t)(rs / LSA_CHUNK);
         d->nrec[r] = (int32_t)(L - rs);
-        d->chunk_off[r] = co;
-        d->rec_off[r] = ro;
+        if (g->chunk_cap > 0 && d->nhist[r] > g->chunk_cap) return LSA_ERR_INVALID_ARG;
+        if (g->recent_cap > 0 && d->nrec[r] > g->recent_cap) return LSA_ERR_INVALID_ARG;
+        d->chunk_off[r] = g->chunk_cap > 0 ? (int64_t)r * g->chunk_cap : co;
+        d->rec_off[r] = g->recent_cap > 0 ? (int64_t)r * g->recent_cap : ro;
         d->tile_off[r] = (int32_t)to;
         co += d->nhist[r];
         ro += d->nrec[r];
         to += (d->nhist[r] + 63) / 64;
     }
+    if (g->chunk_cap > 0) co = (int64_t)g->batch * g->chunk_cap;
+    if (g->recent_cap > 0) ro = (int64_t)g->batch * g->recent_cap;
     d->chunk_off[g->batch] = co;
     d->rec_off[g->batch] = ro;
     d->tile_off[g->batch] = (int32_t)to;
@@ -166,6 +177,58 @@ lsa_status lsa_select_threshold(const lsa_geom* g, const float* z, float theta, 
     if (gd.chunk_off[gd.B] > 0 && (!z || !sel_ids)) return LSA_ERR_INVALID_ARG;
     if (theta != theta) return LSA_ERR_INVALID_ARG;  // NaN threshold
     LSA_HIP(launch_select(gd, z, theta, sel_ids, sel_cnt, (hipStream_t)stream));
+    return LSA_OK;
+}
+
+lsa_status lsa_append_kv(const lsa_geom* g, const lsa_kv_layout* kv, const void* rows,
+                         void* recent, void* stream) {
+    GeomDev gd;
+    lsa_status st = geom_derive(g, &gd);
+    if (st != LSA_OK) return st;
+    st = check_kv(kv);
+    if (st != LSA_OK) return st;
+    if (g->recent_cap <= 0 || !rows || !recent || kv->row_bytes % 16 != 0) return LSA_ERR_INVALID_ARG;
+    if (!aligned16(rows) || !aligned16(recent)) return LSA_ERR_INVALID_ARG;
+    for (int r = 0; r < gd.B; ++r)
+        if (gd.nrec[r] < 1) return LSA_ERR_INVALID_ARG;
+    LSA_HIP(launch_append_kv(gd, rows, kv->row_bytes, recent, (hipStream_t)stream));
+    return LSA_OK;
+}
+
+lsa_status lsa_commit_chunk(const lsa_geom* g, const lsa_kv_layout* kv, const void* recent_src,
+                            void* recent_dst, void* cold, lsa_dtype idx_dt, int32_t d,
+                            const void* new_ikeys, const float* new_ikey_scale,
+                            float* ikey_scale, const void* new_kic,
+                            const float* new_kic_scale, void* kic, float* kic_scale,
+                            int32_t* hist_out, void* stream) {
+    GeomDev gd;
+    lsa_status st = geom_derive(g, &gd);
+    if (st != LSA_OK) return st;
+    st = check_kv(kv);
+    if (st != LSA_OK) return st;
+    if (g->recent_cap <= 0 || g->chunk_cap <= 0 || !hist_out) return LSA_ERR_INVALID_ARG;
+    if (idx_dt != LSA_F32 && idx_dt != LSA_BF16 && idx_dt != LSA_FP8_E4M3FN) return LSA_ERR_INVALID_ARG;
+    const int64_t krb = (int64_t)d * esize(idx_dt);
+    if (d < 1 || krb % 16 != 0 || kv->row_bytes % 16 != 0 || kv->page_bytes % 16 != 0 ||
+        kv->ikey_off % 16 != 0 || kv->ikey_off < kv->row_bytes * LSA_CHUNK ||
+        kv->ikey_off + krb * LSA_CHUNK > kv->page_bytes)
+        return LSA_ERR_INVALID_ARG;
+    if (!recent_src || !recent_dst || !cold || !new_ikeys || !new_kic || !kic) return LSA_ERR_INVALID_ARG;
+    const bool fp8 = idx_dt == LSA_FP8_E4M3FN;
+    if (fp8 && (!new_ikey_scale || !new_kic_scale || !ikey_scale || !kic_scale)) return LSA_ERR_INVALID_ARG;
+    const size_t rb = (size_t)g->batch * g->recent_cap * kv->row_bytes;
+    const uint8_t *a = (const uint8_t*)recent_src, *b = (const uint8_t*)recent_dst;
+    if (a < b + rb && b < a + rb) return LSA_ERR_INVALID_ARG;  // the two buffers overlap
+    int32_t nh[LSA_MAX_BATCH];
+    for (int r = 0; r < gd.B; ++r) {
+        const bool commit = gd.nrec[r] >= gd.W + LSA_CHUNK;
+        if (commit && gd.nhist[r] + 1 > g->chunk_cap) return LSA_ERR_CAPACITY;
+        nh[r] = gd.rs[r] + (commit ? LSA_CHUNK : 0);
+    }
+    LSA_HIP(launch_commit_chunk(gd, kv->row_bytes, kv->page_bytes, kv->ikey_off, recent_src, recent_dst,
+                                cold, krb, new_ikeys, new_ikey_scale, ikey_scale, new_kic, new_kic_scale,
+                                kic, kic_scale, fp8, (hipStream_t)stream));
+    for (int r = 0; r < gd.B; ++r) hist_out[r] = nh[r];
     return LSA_OK;
 }
 

@@ -45,6 +45,14 @@ hipError_t launch_refine(const GeomDev& g, const int32_t* sel, const int32_t* cn
 hipError_t launch_topk(const GeomDev& g, const int32_t* sel, const int32_t* cnt,
                        const float* scores, int k, int32_t* topk, int32_t* tcnt, hipStream_t s);
 
+hipError_t launch_append_kv(const GeomDev& g, const void* rows, int64_t row_bytes, void* recent,
+                            hipStream_t s);
+hipError_t launch_commit_chunk(const GeomDev& g, int64_t row_bytes, int64_t page_bytes, int64_t ikey_off,
+                               const void* rsrc, void* rdst, void* cold, int64_t key_row_bytes,
+                               const void* new_ikeys, const float* new_iks, float* ikey_scale,
+                               const void* new_kic, const float* new_kcs, void* kic, float* kic_scale,
+                               bool fp8, hipStream_t s);
+
 // Per-request keep counts of lsa_select_ranked (by value).
 struct RankCounts {
     int32_t m[LSA_MAX_BATCH];

@@ -31,7 +31,8 @@ class LsaError(RuntimeError):
 
 class lsa_geom(C.Structure):
     _fields_ = [("batch", C.c_int32), ("chunk", C.c_int32), ("window", C.c_int32),
-                ("seq_len", C.c_void_p)]
+                ("seq_len", C.c_void_p), ("hist_tokens", C.c_void_p), ("chunk_cap", C.c_int32),
+                ("recent_cap", C.c_int32)]
 
 
 class lsa_kv_layout(C.Structure):
@@ -87,6 +88,8 @@ def _load():
         "lsa_score_chunks_union": ([G, I32, P, I, P, P, I32, I32, P, I, P, P, P, SZ, P], I),
         "lsa_score_chunks_sigmoid": ([G, P, I, P, P, F, I32, I32, P, I, P, P, P], I),
         "lsa_select_ranked": ([G, P, I, P, P, P, P], I),
+        "lsa_append_kv": ([G, C.POINTER(lsa_kv_layout), P, P, P], I),
+        "lsa_commit_chunk": ([G, C.POINTER(lsa_kv_layout), P, P, P, I, I32, P, P, P, P, P, P, P, P, P], I),
         "lsa_chunk_mass_ws_bytes": ([G, I32, I32], SZ),
         "lsa_chunk_attn_mass": ([G, P, I32, I32, C.POINTER(lsa_kv_layout), P, P, P, F, P, P, P, SZ, P],
                                 I),
@@ -149,11 +152,16 @@ def _check(fn, code):
 
 
 class Geom:
-    """lsa_geom plus the host array it points to."""
+    """lsa_geom plus the host arrays it points to.  hist_tokens, chunk_cap and
+    recent_cap describe a growing context (None / 0: packed layout)."""
 
-    def __init__(self, seq_len, window: int, chunk: int = LSA_CHUNK):
+    def __init__(self, seq_len, window: int, chunk: int = LSA_CHUNK, hist_tokens=None,
+                 chunk_cap: int = 0, recent_cap: int = 0):
         self.seq_len = np.ascontiguousarray(seq_len, dtype=np.int32)
-        self.s = lsa_geom(len(self.seq_len), chunk, window, self.seq_len.ctypes.data)
+        self.hist_tokens = None if hist_tokens is None else np.ascontiguousarray(hist_tokens, dtype=np.int32)
+        self.s = lsa_geom(len(self.seq_len), chunk, window, self.seq_len.ctypes.data,
+                          None if self.hist_tokens is None else self.hist_tokens.ctypes.data,
+                          int(chunk_cap), int(recent_cap))
 
     @property
     def ref(self):
@@ -192,6 +200,22 @@ def lsa_score_chunks_sigmoid(g: Geom, q, q_dt, w, bias, theta, H, d, kic, kic_dt
     _check("lsa_score_chunks_sigmoid",
            _lib.lsa_score_chunks_sigmoid(g.ref, _ptr(q), q_dt, _ptr(w), _ptr(bias), float(theta), H, d,
                                          _ptr(kic), kic_dt, _ptr(kic_scale), _ptr(S), _stream(stream)))
+
+
+def lsa_append_kv(g: Geom, kv: lsa_kv_layout, rows, recent, stream=None):
+    _check("lsa_append_kv", _lib.lsa_append_kv(g.ref, C.byref(kv), _ptr(rows), _ptr(recent), _stream(stream)))
+
+
+def lsa_commit_chunk(g: Geom, kv: lsa_kv_layout, recent_src, recent_dst, cold, idx_dt, d, new_ikeys,
+                     new_ikey_scale, ikey_scale, new_kic, new_kic_scale, kic, kic_scale, stream=None):
+    """Returns the new hist_tokens (host int32 array)."""
+    out = np.zeros(g.s.batch, np.int32)
+    _check("lsa_commit_chunk",
+           _lib.lsa_commit_chunk(g.ref, C.byref(kv), _ptr(recent_src), _ptr(recent_dst), _ptr(cold), idx_dt, d,
+                                 _ptr(new_ikeys), _ptr(new_ikey_scale), _ptr(ikey_scale), _ptr(new_kic),
+                                 _ptr(new_kic_scale), _ptr(kic), _ptr(kic_scale), out.ctypes.data,
+                                 _stream(stream)))
+    return out
 
 
 RANK_SMALLEST_U32, RANK_LARGEST_F32 = 0, 1
@@ -330,7 +354,8 @@ def lsa_step64(ctx: Ctx, win, out, main=None, copy=None):
 # ---------------------------------------------------------------- diagnostics
 KERNELS = ("k_fuse_query", "k_score", "k_select", "k_refine", "k_topk", "k_refine_mfma",
            "k_band_fine", "k_band_list", "k_topk_band", "k_attn_mla", "k_attn_f32", "k_attn_merge",
-           "k_gather", "k_stream_read", "k_score_sig", "k_select_ranked", "k_chunk_ml")
+           "k_gather", "k_stream_read", "k_score_sig", "k_select_ranked", "k_chunk_ml",
+           "k_append_kv", "k_commit_chunk")
 
 
 def lsa_timing_enable(on: bool):

@@ -228,3 +228,155 @@ class Pipeline:
         torch.cuda.synchronize()
         self.ctx.close()
         self.pool.close()
+
+
+def token_row(inp, r: int, s: int) -> np.ndarray:
+    """Stored bytes of token s's KV row of request r (history page or recent)."""
+    cfg = inp.cfg
+    rs = int(inp["rs"][r])
+    if s < rs:
+        pg = inp["pages"][int(inp["chunk_off"][r]) + s // cfg.chunk]
+        o = (s % cfg.chunk) * cfg.kv_row_bytes
+        return pg[o:o + cfg.kv_row_bytes]
+    return inp["recent"][int(inp["rec_off"][r]) + s - rs]
+
+
+class Growing:
+    """Growing-context decode over the tokens of `full` (inputs generated at
+    the final context lengths).  The run starts at contexts L0 and adds one
+    token per step; every 64 steps (a window) it scores and selects the
+    current history, and at the end of each window it commits the recent
+    region's oldest full chunk into the history.  Device state uses fixed
+    capacities per request (chunk_cap chunks, recent_cap recent rows): a
+    cold tier of pages, KIComp rows and scales, and two recent buffers used
+    in turn.  The rows each step appends and each committed chunk's index
+    keys and KIComp row come from `full`."""
+
+    def __init__(self, full, L0, n_windows: int, device="cuda"):
+        cfg = full.cfg
+        C, W = cfg.chunk, cfg.window
+        self.full, self.cfg, self.device, self.B = full, cfg, device, cfg.batch
+        self.L = np.asarray(L0, np.int64).copy()
+        if not np.array_equal(self.L + C * n_windows, np.asarray(full["seq_len"], np.int64)):
+            raise ValueError("full must hold the contexts L0 + 64 * n_windows")
+        self.rs = C * (np.maximum(self.L - W, 0) // C)
+        self.n_windows = n_windows
+        self.chunk_cap = max(int(np.max(full["n_hist"])), 1)
+        self.recent_cap = W + 2 * C
+        B, rb, pb = self.B, cfg.kv_row_bytes, cfg.page_bytes
+        kb = cfg.d * synth.ELEM_BYTES[cfg.idx_dtype]
+        pages = np.zeros((B * self.chunk_cap, pb), np.uint8)
+        kic = np.zeros((B * self.chunk_cap, kb), np.uint8)
+        ksc = np.ones(B * self.chunk_cap, np.float32)
+        isc = np.ones(B * self.chunk_cap, np.float32)
+        rec = np.zeros((B * self.recent_cap, rb), np.uint8)
+        fk = full["kic_windows"][0].reshape(int(full["chunk_off"][-1]), -1).view(np.uint8)
+        for r in range(B):
+            f0, n0, o = int(full["chunk_off"][r]), int(self.rs[r]) // C, r * self.chunk_cap
+            pages[o:o + n0] = full["pages"][f0:f0 + n0]
+            kic[o:o + n0] = fk[f0:f0 + n0]
+            ksc[o:o + n0] = full["kic_scale_windows"][0][f0:f0 + n0]
+            isc[o:o + n0] = full["ikey_scale"][f0:f0 + n0]
+            for i, s in enumerate(range(int(self.rs[r]), int(self.L[r]))):
+                rec[r * self.recent_cap + i] = token_row(full, r, s)
+        T = C * n_windows
+        app = np.zeros((T, B, rb), np.uint8)
+        for t in range(T):
+            for r in range(B):
+                app[t, r] = token_row(full, r, int(self.L[r]) + t)
+        # per window: the chunk each request would commit at its end
+        nik = np.zeros((n_windows, B, C * kb), np.uint8)
+        nkc = np.zeros((n_windows, B, kb), np.uint8)
+        nis = np.ones((n_windows, B), np.float32)
+        nks = np.ones((n_windows, B), np.float32)
+        rs = self.rs.copy()
+        for m in range(n_windows):
+            Lm = self.L + C * (m + 1)
+            for r in range(B):
+                if Lm[r] - rs[r] >= W + C:
+                    c = int(full["chunk_off"][r]) + int(rs[r]) // C
+                    nik[m, r] = full["pages"][c, cfg.ikey_off:cfg.ikey_off + C * kb]
+                    nkc[m, r] = fk[c]
+                    nis[m, r] = full["ikey_scale"][c]
+                    nks[m, r] = full["kic_scale_windows"][0][c]
+                    rs[r] += C
+        d = device
+        self.pages = _dev(pages.reshape(-1), d)
+        self.kic, self.kic_scale, self.ikey_scale = _dev(kic.reshape(-1), d), _dev(ksc, d), _dev(isc, d)
+        self.recent = [_dev(rec.reshape(-1), d), torch.zeros(rec.size, dtype=torch.uint8, device=d)]
+        self.app = _dev(app, d)
+        self.nik, self.nkc, self.nis, self.nks = _dev(nik, d), _dev(nkc, d), _dev(nis, d), _dev(nks, d)
+        self.q_coarse, self.w_coarse = _dev(full["q_coarse"], d), _dev(full["w_coarse"], d)
+        self.bias = _dev(full["bias"], d)
+        self.q_refine, self.w_refine = _dev(full["q_refine"], d), _dev(full["w_refine"], d)
+        self.q_attn = _dev(full["q_attn"], d)
+        self.kv = lsa.kv_layout(cfg.kv_dtype, cfg.Dk, cfg.Dv, cfg.v_off, rb, pb, cfg.ikey_off)
+        self.cur = 0
+        self.t = 0
+        self.n_q = int(full["q_attn"].shape[0])  # per-step queries are reused cyclically past this
+        self.sel = torch.full((B * self.chunk_cap,), -1, dtype=torch.int32, device=d)
+        self.cnt = torch.zeros(B, dtype=torch.int32, device=d)
+        self.z = torch.empty(B * self.chunk_cap, dtype=torch.float32, device=d)
+        self._ws = {}
+        self._k = None
+
+    def _scratch(self, name, nbytes):
+        w = self._ws.get(name)
+        if w is None or w.numel() < nbytes:
+            w = _ws(nbytes, self.device)
+            self._ws[name] = w
+        return w
+
+    def _outputs(self, k):
+        if self._k != k:
+            cfg, d = self.cfg, self.device
+            odt = torch.float32 if cfg.kv_dtype == synth.F32 else torch.int16
+            self._topk = torch.full((self.B, k), -1, dtype=torch.int32, device=d)
+            self._tcnt = torch.zeros(self.B, dtype=torch.int32, device=d)
+            self._out = torch.empty((self.B, cfg.Hq, cfg.Dv), dtype=odt, device=d)
+            self._lse = torch.empty((self.B, cfg.Hq), dtype=torch.float32, device=d)
+            self._k = k
+        return self._topk, self._tcnt, self._out, self._lse
+
+    def geom(self):
+        return lsa.Geom(self.L, self.cfg.window, self.cfg.chunk, hist_tokens=self.rs,
+                        chunk_cap=self.chunk_cap, recent_cap=self.recent_cap)
+
+    def trigger(self, theta=0.0, stream=None):
+        """Score and select the current history (the window's trigger)."""
+        cfg, g = self.cfg, self.geom()
+        ws = self._scratch("score", lsa.lsa_score_ws_bytes(g, cfg.d))
+        lsa.lsa_score_chunks(g, self.q_coarse, cfg.q_dtype, self.w_coarse, self.bias, cfg.H, cfg.d,
+                             self.kic, cfg.idx_dtype, self.kic_scale, self.z, ws, stream)
+        lsa.lsa_select_threshold(g, self.z, theta, self.sel, self.cnt, stream)
+        return self.sel, self.cnt
+
+    def step(self, k, stream=None):
+        """One decode step: append the next token, refine and top-k over the
+        window's selection, attend over the top-k and the grown recent region."""
+        cfg, t = self.cfg, self.t
+        tq = t % self.n_q
+        self.L += 1
+        g = self.geom()
+        lsa.lsa_append_kv(g, self.kv, self.app[t], self.recent[self.cur], stream)
+        topk, tcnt, out, lse = self._outputs(k)
+        ws = self._scratch("refine", lsa.lsa_refine_ws_bytes(g, k))
+        lsa.lsa_topk_refine(g, self.sel, self.cnt, self.pages, cfg.page_bytes, cfg.ikey_off, None,
+                            cfg.idx_dtype, self.ikey_scale, self.q_refine[tq], cfg.q_dtype,
+                            self.w_refine[tq], cfg.H, cfg.d, k, topk, tcnt, ws, stream)
+        ws = self._scratch("attn", lsa.lsa_attn_ws_bytes(g, self.kv, cfg.Hq, k, 0))
+        lsa.lsa_sparse_decode_attn(g, self.q_attn[tq], cfg.Hq, self.kv, self.pages, None,
+                                   self.recent[self.cur], topk, tcnt, k, cfg.sm_scale, out, lse, 0, ws,
+                                   stream)
+        self.t += 1
+        return topk, tcnt, out, lse
+
+    def commit(self, m: int, stream=None):
+        """End of window m: the oldest full recent chunk joins the history."""
+        cfg, g = self.cfg, self.geom()
+        self.rs = lsa.lsa_commit_chunk(g, self.kv, self.recent[self.cur], self.recent[1 - self.cur],
+                                       self.pages, cfg.idx_dtype, cfg.d, self.nik[m], self.nis[m],
+                                       self.ikey_scale, self.nkc[m], self.nks[m], self.kic,
+                                       self.kic_scale, stream).astype(np.int64)
+        self.cur = 1 - self.cur
+        return self.rs

@@ -61,3 +61,41 @@ def dense_attention(q, K, V, sm):
     p = np.exp(x - m)
     l = p.sum(axis=1, keepdims=True)
     return (p @ V) / l, (m + np.log(l))[:, 0]
+
+
+def stored_row(inp, r, s):
+    """Stored bytes of token s's KV row of request r (its page or the recent rows)."""
+    cfg = inp.cfg
+    rs = int(inp["rs"][r])
+    if s < rs:
+        o = (s % cfg.chunk) * cfg.kv_row_bytes
+        return inp["pages"][int(inp["chunk_off"][r]) + s // cfg.chunk][o:o + cfg.kv_row_bytes]
+    return inp["recent"][int(inp["rec_off"][r]) + s - rs]
+
+
+def growing_snapshot(full, r, L, rs):
+    """Request r of `full` (inputs generated at the final contexts) as a
+    growing-context run holds it at context L with history boundary rs:
+    history chunks [0, rs/C) with their pages, KIComp rows and scales,
+    tokens [rs, L) as recent rows, and the request's per-step queries.  One
+    request, packed; the window is L - rs so the geometry puts rs there."""
+    cfg = full.cfg
+    C = cfg.chunk
+    n = rs // C
+    sc = dataclasses.replace(cfg, batch=1, seq_lens=(L,), window=L - rs)
+    inp = synth.Inputs()
+    inp.cfg = sc
+    f0 = int(full["chunk_off"][r])
+    inp.update(seq_len=np.array([L], np.int32), chunk_off=np.array([0, n], np.int64),
+               rec_off=np.array([0, L - rs], np.int64), rs=np.array([rs], np.int64),
+               n_hist=np.array([n], np.int64), n_rec=np.array([L - rs], np.int64))
+    inp["pages"] = np.ascontiguousarray(full["pages"][f0:f0 + n])
+    inp["ikey_scale"] = np.ascontiguousarray(full["ikey_scale"][f0:f0 + n])
+    inp["kic"] = np.ascontiguousarray(full["kic_windows"][0][f0:f0 + n])
+    inp["kic_scale"] = np.ascontiguousarray(full["kic_scale_windows"][0][f0:f0 + n])
+    inp["recent"] = np.stack([stored_row(full, r, s) for s in range(rs, L)])
+    for key in ("q_coarse", "w_coarse", "bias"):
+        inp[key] = np.ascontiguousarray(full[key][r:r + 1])
+    for key in ("q_refine", "w_refine", "q_attn"):
+        inp[key] = np.ascontiguousarray(full[key][:, r:r + 1])
+    return inp

@@ -462,3 +462,69 @@ def test_chunk_mass_parity(kind):
             edge = np.sort(mo)[::-1][m - 1]
             for c in got ^ want:
                 assert abs(mo[c] - edge) <= 2 * MASS_RTOL * edge, (pct, c, mo[c], edge)
+
+
+# ------------------------------------------------- growing context
+@pytest.mark.parametrize("idx", ["bf16", "fp8"])
+def test_growing_context_matches_oracle(idx):
+    """Two windows of growing-context decode (one token appended per step,
+    the oldest full recent chunk committed at each window's end) on ragged
+    requests, one too short to commit: every trigger's selection and every
+    step's top-k bit-exact against the oracle on the packed state of that
+    step, attention within tolerance on sampled steps, and the end state
+    (history pages, KIComp rows, recent rows) equal to the generated data."""
+    from tests import helpers
+    runner = _runner()
+    W, k, nw = 1024, 256, 2
+    L0 = [5000, 3100, 900]
+    dt = BF16 if idx == "bf16" else FP8
+    cfg = synth.small_config("grow_" + idx, 31 if idx == "bf16" else 32, tuple(L + 64 * nw for L in L0),
+                             window=W, idx=dt, H=16, topk=k, steps=64 * nw)
+    full = synth.generate(cfg)
+    g = runner.Growing(full, L0, nw)
+    tol, lse_tol = tol_of(cfg)
+    t = 0
+    for m in range(nw):
+        L_trig, rs_m = g.L.copy(), g.rs.copy()
+        print(f"[grow] {idx} window {m}: L={list(L_trig)} rs={list(rs_m)}", flush=True)
+        sel, cnt = g.trigger()
+        torch.cuda.synchronize()
+        s_h, c_h = sel.cpu().numpy(), cnt.cpu().numpy()
+        sel_ref = []
+        for r in range(cfg.batch):
+            snap = helpers.growing_snapshot(full, r, int(L_trig[r]), int(rs_m[r]))
+            _, sel_o, cnt_o = oracle.Oracle(snap).score_select()
+            a = r * g.chunk_cap
+            assert c_h[r] == cnt_o[0], (m, r)
+            assert np.array_equal(s_h[a:a + c_h[r]], sel_o[:cnt_o[0]]), (m, r)
+            sel_ref.append(np.ascontiguousarray(sel_o[:cnt_o[0]]))
+        for j in range(64):
+            topk, tcnt, out, lse = g.step(k)
+            torch.cuda.synchronize()
+            tk, tc = topk.cpu().numpy(), tcnt.cpu().numpy()
+            check_att = j in (0, 1, 40, 63)
+            got = runner.out_to_f32(out, cfg) if check_att else None
+            for r in range(cfg.batch):
+                snap = helpers.growing_snapshot(full, r, int(L_trig[r]) + j + 1, int(rs_m[r]))
+                o = oracle.Oracle(snap)
+                want = o.refine_topk(0, sel_ref[r], snap["q_refine"][t, 0], snap["w_refine"][t, 0], k)
+                assert tc[r] == len(want), (m, j, r)
+                assert np.array_equal(tk[r, :tc[r]], want), (m, j, r)
+                if check_att:
+                    ref, lse_ref = o.attend(0, want, snap["q_attn"][t, 0], cfg.sm_scale)
+                    assert rel_err(got[r], ref).max() <= tol, (m, j, r)
+                    assert np.abs(lse.cpu().numpy()[r] - lse_ref).max() <= lse_tol * max(1.0, np.abs(lse_ref).max())
+            t += 1
+        g.commit(m)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.L, full["seq_len"]) and np.array_equal(g.rs, full["rs"])
+    pages = g.pages.cpu().numpy().reshape(cfg.batch * g.chunk_cap, -1)
+    kic = g.kic.cpu().numpy().reshape(cfg.batch * g.chunk_cap, -1)
+    rec = g.recent[g.cur].cpu().numpy().reshape(cfg.batch * g.recent_cap, -1)
+    fk = full["kic_windows"][0].reshape(int(full["chunk_off"][-1]), -1).view(np.uint8)
+    for r in range(cfg.batch):
+        c0, n, a = int(full["chunk_off"][r]), int(full["n_hist"][r]), r * g.chunk_cap
+        assert np.array_equal(pages[a:a + n], full["pages"][c0:c0 + n]), r
+        assert np.array_equal(kic[a:a + n], fk[c0:c0 + n]), r
+        q0, nr = int(full["rec_off"][r]), int(full["n_rec"][r])
+        assert np.array_equal(rec[r * g.recent_cap:r * g.recent_cap + nr], full["recent"][q0:q0 + nr]), r

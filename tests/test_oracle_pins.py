@@ -572,3 +572,28 @@ def test_policy_selections_textbook():
     mass = np.arange(1, 9, dtype=np.float64)
     assert oracle.mass_recall(mass, range(8)) == 1.0 and oracle.mass_recall(mass, []) == 0.0
     assert math.isclose(oracle.mass_recall(mass, oracle.select_largest(mass, 4)), 26 / 36)
+
+
+# ------------------------------------------------- NEXT-4 growing context
+def test_growing_snapshot_at_the_final_state_is_the_generated_request():
+    """The test-side snapshot of a growing run, taken at a request's final
+    context and boundary, holds exactly the generator's packed data of that
+    request; at an earlier state its rows are the same tokens' rows."""
+    cfg = synth.small_config("grow", 31, (2200, 1500), window=512, H=4, d=64, steps=2)
+    full = synth.generate(cfg)
+    o_full = oracle.Oracle(full)
+    z_full, _, cnt_full = o_full.score_select()
+    for r in range(cfg.batch):
+        L, rs = int(full["seq_len"][r]), int(full["rs"][r])
+        snap = helpers.growing_snapshot(full, r, L, rs)
+        c0, n = int(full["chunk_off"][r]), int(full["n_hist"][r])
+        assert np.array_equal(snap["pages"], full["pages"][c0:c0 + n])
+        q0 = int(full["rec_off"][r])
+        assert np.array_equal(snap["recent"], full["recent"][q0:q0 + L - rs])
+        z, _, cnt = oracle.Oracle(snap).score_select()
+        assert np.array_equal(z.view(np.uint32), z_full[c0:c0 + n].view(np.uint32)) and cnt[0] == cnt_full[r]
+        # 100 tokens earlier, two chunks fewer in the history: same rows, moved
+        early = helpers.growing_snapshot(full, r, L - 100, rs - 128)
+        K_e, _ = helpers.kv_rows(early, 0)
+        K_f, _ = helpers.kv_rows(full, r)
+        assert np.array_equal(K_e, K_f[:L - 100])
