@@ -340,7 +340,12 @@ lsa_status lsa_chunk_attn_mass(const lsa_geom* g, const void* q, int32_t Hq, int
  * The pool gives request r the slots [r*slots_per_req, (r+1)*slots_per_req)
  * of slot_mem (device, B*slots_per_req*page_bytes bytes, caller-owned).  The
  * cold tier holds page (chunk_off[r] + c) for every history chunk; it is
- * pinned host memory (cold_on_host = 1) or device memory (0).
+ * host memory (cold_on_host = 1; pinned memory is fastest for the host's
+ * packing copies) or device memory (0).  For the host tier a gather packs
+ * the missing chunks on the host into pinned staging (up to 1,024 chunks per
+ * batch, several threads) and sends each batch with one DMA copy, then
+ * scatters it into the slots on the device; for the device tier it copies
+ * with one kernel launch.  Both run on the copy stream.
  * lsa_pool_create allocates only host bookkeeping and one small device copy
  * list; it borrows slot_mem and cold until lsa_pool_destroy.
  * ---------------------------------------------------------------------- */
@@ -350,7 +355,7 @@ typedef struct {
     int64_t fetched;  /* chunks copied by the last gather                 */
     int64_t resident; /* chunks resident after it                         */
     int64_t evicted;  /* chunks released by it                            */
-    int64_t copies;   /* copy commands issued (runs are coalesced)        */
+    int64_t copies;   /* packed batches (host tier) or copy launches        */
     int64_t bytes;    /* bytes copied                                     */
 } lsa_gather_stats;
 
@@ -449,10 +454,15 @@ lsa_status lsa_step64(lsa_ctx* ctx, const lsa_window_in* in, lsa_window_out* out
  * milliseconds since the last reset.  lsa_timing_only(name) restricts the
  * timing to that one kernel (NULL: all; a name of 64 or more characters is
  * LSA_ERR_INVALID_ARG), so that one kernel can be timed inside a run with
- * little disturbance.  Process-wide; the hooks are thread-safe.
+ * little disturbance.  lsa_timing_every(n) brackets only every n-th launch
+ * of each timed kernel (n >= 1; 1 is the default), which spreads the events'
+ * own cost (a few microseconds per record on this GPU) over n launches.
+ * The events skip the system-scope fence.  Process-wide; the hooks are
+ * thread-safe.
  * ---------------------------------------------------------------------- */
 lsa_status lsa_timing_enable(int32_t on);
 lsa_status lsa_timing_only(const char* kernel);
+lsa_status lsa_timing_every(int32_t n);
 void lsa_timing_reset(void);
 lsa_status lsa_timing_read(const char* kernel, int64_t* launches, double* total_ms);
 

@@ -21,6 +21,8 @@
 // k_attn_f32: fp32 rows, VALU, for small head counts (fp32 path).
 #include "lsa_internal.h"
 
+#include <type_traits>
+
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
                                                         const int32_t* __restrict__ tcnt,
                                                         const uint16_t* __restrict__ q, int Hq,
                                                         int n_splits, int per_split, int hgroups,
-                                                        float sm_log2e, float* __restrict__ part_o,
+                                                        float sm_log2e, uint16_t* __restrict__ part_o,
                                                         float* __restrict__ part_ml) {
     constexpr int NB = 2 * kKSteps;                   // operand blocks per tile (36)
     constexpr int NLmax = (NB + NW - 1) / NW;         // tile loads per wave (the first NB % NW waves)
@@ -382,14 +384,16 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
         ++it;
     }
 
-    // ---- partial outputs: O^T lane (head l16, lq) holds dims 16 vbg + 4 lq .. +4 ----
+    // ---- partial outputs: O^T lane (head l16, lq) holds dims 16 vbg + 4 lq .. +4;
+    // rows are stored in bf16 (the output's own precision), m and l in fp32 ----
     const int64_t hbase = ((int64_t)r * n_splits + split) * Hq + h0;
 #pragma unroll
     for (int hb = 0; hb < HPW; ++hb) {
-        float* dst = part_o + (hbase + hb * 16 + l16) * MDV + 256 * vh + 4 * lq;
+        uint16_t* dst = part_o + (hbase + hb * 16 + l16) * MDV + 256 * vh + 4 * lq;
 #pragma unroll
         for (int vb = 0; vb < 16; ++vb)
-            *(float4*)(dst + 16 * vb) = make_float4(acc[hb][vb][0], acc[hb][vb][1], acc[hb][vb][2], acc[hb][vb][3]);
+            *(uint2*)(dst + 16 * vb) = make_uint2(pack_bf16(acc[hb][vb][0], acc[hb][vb][1]),
+                                                  pack_bf16(acc[hb][vb][2], acc[hb][vb][3]));
         const float l = add_xor32(add_xor16(l_lane[hb]));
         if (vh == 0 && lq == 0) {
             part_ml[(hbase + hb * 16 + l16) * 2 + 0] = m_ref[hb];
@@ -504,7 +508,8 @@ __global__ __launch_bounds__(256) void k_attn_f32(GeomDev g, PosMap pm, const in
 }
 
 // ----------------------------------------------------------------------------
-// merge of the splits: one wave per (request, head, 128 value columns).  The
+// merge of the splits: one wave per (request, head, 128 value columns); the
+// partial rows are fp32 (f32 path) or bf16 (bf16 latent path).  The
 // split weights 2^(m_s - m) and the total sum are formed by the wave in a
 // fixed order; then each lane combines two columns over all splits, in
 // split order, with up to 32 splits' loads in flight at once.
@@ -513,8 +518,8 @@ constexpr int kMergeMaxSplits = 1024;
 constexpr int kMergeCols = 128;
 constexpr int kMergeBatch = 32;
 
-template <int ODT>
-__global__ __launch_bounds__(64) void k_attn_merge(const float* __restrict__ part_o,
+template <int ODT, typename PT>
+__global__ __launch_bounds__(64) void k_attn_merge(const PT* __restrict__ part_o,
                                                    const float* __restrict__ part_ml, int Hq, int Dv,
                                                    int n_splits, void* __restrict__ out,
                                                    float* __restrict__ lse) {
@@ -526,14 +531,22 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float* __restrict__ par
     const int64_t b0 = (int64_t)r * n_splits * Hq + h;  // split s: (b0 + s*Hq)
     const int v = chunk * kMergeCols + 2 * L;
     const bool col = v < Dv;
-    const float* src = part_o + b0 * Dv + v;
+    const PT* src = part_o + b0 * Dv + v;
     const int64_t stride = (int64_t)Hq * Dv;
+    // two columns of a partial row as loaded (unpacked only where used, so a
+    // whole batch of loads stays in flight)
+    using Raw = typename std::conditional<sizeof(PT) == 4, float2, uint32_t>::type;
+    auto ld2 = [&](int64_t i) -> Raw { return *(const Raw*)(src + i); };
+    auto unpack = [](Raw w) -> float2 {
+        if constexpr (sizeof(PT) == 4) return w;
+        else return make_float2(bf16_lo(w), bf16_hi(w));
+    };
     // the first batch of partial rows is requested before the split weights
     // are formed, so both latencies overlap
-    float2 x[kMergeBatch];
+    Raw x[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u)
-        if (col && u < n_splits) x[u] = *(const float2*)(src + (int64_t)u * stride);
+        if (col && u < n_splits) x[u] = ld2((int64_t)u * stride);
     float m = -INFINITY;
     for (int s = L; s < n_splits; s += 64) m = fmaxf(m, part_ml[(b0 + (int64_t)s * Hq) * 2]);
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
@@ -554,15 +567,16 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float* __restrict__ par
             if (s0 > 0) {
 #pragma unroll
                 for (int u = 0; u < kMergeBatch; ++u)
-                    if (s0 + u < n_splits) x[u] = *(const float2*)(src + (int64_t)(s0 + u) * stride);
+                    if (s0 + u < n_splits) x[u] = ld2((int64_t)(s0 + u) * stride);
             }
 #pragma unroll
             for (int u = 0; u < kMergeBatch; ++u) {
                 if (s0 + u < n_splits) {
                     const float f = fac[s0 + u];
                     if (f != 0.0f) {
-                        ox += x[u].x * f;
-                        oy += x[u].y * f;
+                        const float2 xv = unpack(x[u]);
+                        ox += xv.x * f;
+                        oy += xv.y * f;
                     }
                 }
             }
@@ -630,7 +644,8 @@ lsa_status attn_plan(const GeomDev& g, const lsa_kv_layout* kv, int Hq, int k, i
         return LSA_ERR_UNSUPPORTED;
     }
     if (p.n_splits > kMergeMaxSplits) return LSA_ERR_UNSUPPORTED;
-    p.part_o_bytes = align_up((size_t)g.B * p.n_splits * Hq * kv->Dv * sizeof(float), 256);
+    // partial rows: bf16 on the bf16 latent path, fp32 on the f32 path
+    p.part_o_bytes = align_up((size_t)g.B * p.n_splits * Hq * kv->Dv * (p.mode == 1 ? 2 : 4), 256);
     p.part_ml_bytes = align_up((size_t)g.B * p.n_splits * Hq * 2 * sizeof(float), 256);
     *plan = p;
     return LSA_OK;
@@ -642,7 +657,7 @@ hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, in
                        float sm_scale, void* out, float* lse, void* ws, hipStream_t s) {
     PosMap pm{(const uint8_t*)pages, kv.page_bytes, kv.row_bytes, page_table,
               (const uint8_t*)recent, topk, k};
-    float* part_o = (float*)ws;
+    float* part_o = (float*)ws;  // fp32 rows (f32 path) or bf16 rows (latent path)
     float* part_ml = (float*)((uint8_t*)ws + plan.part_o_bytes);
     const float sm_log2e = sm_scale * 1.44269504088896340736f;
     if (plan.mode == 1) {
@@ -652,11 +667,11 @@ hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, in
         if (plan.waves == 8)
             hipLaunchKernelGGL((k_attn_mla<8, 1>), dim3(grid), dim3(512), 0, s, g, pm, tcnt,
                                (const uint16_t*)q, Hq, plan.n_splits, plan.per_split,
-                               plan.head_groups, sm_log2e, part_o, part_ml);
+                               plan.head_groups, sm_log2e, (uint16_t*)part_o, part_ml);
         else
             hipLaunchKernelGGL((k_attn_mla<4, 1>), dim3(grid), dim3(256), 0, s, g, pm, tcnt,
                                (const uint16_t*)q, Hq, plan.n_splits, plan.per_split,
-                               plan.head_groups, sm_log2e, part_o, part_ml);
+                               plan.head_groups, sm_log2e, (uint16_t*)part_o, part_ml);
         timing_end("k_attn_mla", s);
     } else {
         timing_begin("k_attn_f32", s);
@@ -669,12 +684,12 @@ hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, in
     if (e != hipSuccess) return e;
     const int nchunk = (kv.Dv + kMergeCols - 1) / kMergeCols;
     timing_begin("k_attn_merge", s);
-    if (kv.kv_dtype == LSA_F32)
-        hipLaunchKernelGGL(k_attn_merge<LSA_F32>, dim3(g.B * Hq * nchunk), dim3(64), 0, s, part_o,
-                           part_ml, Hq, kv.Dv, plan.n_splits, out, lse);
+    if (plan.mode != 1)
+        hipLaunchKernelGGL((k_attn_merge<LSA_F32, float>), dim3(g.B * Hq * nchunk), dim3(64), 0, s,
+                           (const float*)part_o, part_ml, Hq, kv.Dv, plan.n_splits, out, lse);
     else
-        hipLaunchKernelGGL(k_attn_merge<LSA_BF16>, dim3(g.B * Hq * nchunk), dim3(64), 0, s, part_o,
-                           part_ml, Hq, kv.Dv, plan.n_splits, out, lse);
+        hipLaunchKernelGGL((k_attn_merge<LSA_BF16, uint16_t>), dim3(g.B * Hq * nchunk), dim3(64), 0, s,
+                           (const uint16_t*)part_o, part_ml, Hq, kv.Dv, plan.n_splits, out, lse);
     timing_end("k_attn_merge", s);
     return hipGetLastError();
 }

@@ -5,14 +5,21 @@
 // gist.science summary, section 2.1 "Dynamisches Fetching").  The pool keeps
 // a chunk -> slot table per request on the host.  A gather releases every
 // resident chunk outside (new selection U kept selection), gives each
-// missing chunk the lowest free slot of its request, and copies it on the
-// copy stream: hipMemcpyAsync per run of consecutive chunks into
-// consecutive slots when the cold tier is pinned host memory (SDMA), or one
-// k_gather launch when it is device memory.  The page table for the new
-// selection then goes up from pinned staging on the same stream.
+// missing chunk the lowest free slot of its request, and copies them on the
+// copy stream.  Device cold tier: one k_gather launch (one block per chunk).
+// Host cold tier: the host packs the missing chunks into a pinned staging
+// buffer (several threads), one DMA copy takes the whole batch across the
+// host link, and k_gather scatters it from device staging into the slots.
+// One DMA command per scattered chunk would cost about 11 us of command
+// overhead each (a few hundred per window), and a kernel reading host memory
+// would hold compute units for the whole transfer; the packed copy runs at
+// the link's rate on the copy engine.  The page table for the new selection
+// then goes up from pinned staging on the same stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
+#include <thread>
 #include <vector>
 
 #include "lsa_internal.h"
@@ -32,7 +39,39 @@ struct lsa_pool {
     int32_t* h_pt = nullptr;                       // pinned [sum N]
     hipEvent_t staging_done = nullptr;
     bool staging_pending = false;
+    // host tier: packed batches of missing chunks
+    uint8_t* h_stage = nullptr;    // pinned [kStageChunks * page_bytes]
+    uint8_t* d_stage = nullptr;    // device [kStageChunks * page_bytes]
+    int32_t* h_spairs = nullptr;   // pinned [kStageChunks * 2]: (staging index, slot)
+    int32_t* d_spairs = nullptr;   // device copy
+    hipEvent_t stage_done = nullptr;  // the last batch's uploads have read h_stage
+    bool stage_pending = false;
 };
+
+namespace {
+
+constexpr int kStageChunks = 1024;  // chunks per packed batch (84 MB at 82 KB pages)
+constexpr int kPackThreads = 8;
+
+// dst[i] = src + idx[i] * pb for i in [0, n): contiguous ranges per thread
+void pack_chunks(uint8_t* dst, const uint8_t* src, const int32_t* pairs, int n, int64_t pb) {
+    auto work = [&](int a, int b) {
+        for (int i = a; i < b; ++i) std::memcpy(dst + (int64_t)i * pb, src + (int64_t)pairs[2 * i] * pb, pb);
+    };
+    const int nt = std::max(1, std::min(kPackThreads, n / 16));
+    if (nt == 1) {
+        work(0, n);
+        return;
+    }
+    std::vector<std::thread> th;
+    th.reserve(nt - 1);
+    const int per = (n + nt - 1) / nt;
+    for (int t = 1; t < nt; ++t) th.emplace_back(work, std::min(n, t * per), std::min(n, (t + 1) * per));
+    work(0, std::min(n, per));
+    for (auto& x : th) x.join();
+}
+
+}  // namespace
 
 void* lsa_pool_slots(const lsa_pool* p) { return p ? p->slots : nullptr; }
 int64_t lsa_pool_page_bytes(const lsa_pool* p) { return p ? p->page_bytes : 0; }
@@ -77,6 +116,15 @@ lsa_status lsa_pool_create(lsa_pool** pool, const lsa_geom* g, void* slot_mem,
         lsa_pool_destroy(p);
         return LSA_ERR_HIP;
     }
+    if (p->on_host &&
+        (hipHostMalloc((void**)&p->h_stage, (size_t)kStageChunks * page_bytes, hipHostMallocDefault) != hipSuccess ||
+         hipMalloc((void**)&p->d_stage, (size_t)kStageChunks * page_bytes) != hipSuccess ||
+         hipHostMalloc((void**)&p->h_spairs, (size_t)kStageChunks * 2 * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
+         hipMalloc((void**)&p->d_spairs, (size_t)kStageChunks * 2 * sizeof(int32_t)) != hipSuccess ||
+         hipEventCreateWithFlags(&p->stage_done, hipEventDisableTiming) != hipSuccess)) {
+        lsa_pool_destroy(p);
+        return LSA_ERR_HIP;
+    }
     *pool = p;
     return LSA_OK;
 }
@@ -87,9 +135,17 @@ void lsa_pool_destroy(lsa_pool* p) {
         if (p->staging_pending) (void)hipEventSynchronize(p->staging_done);
         (void)hipEventDestroy(p->staging_done);
     }
+    if (p->stage_done) {
+        if (p->stage_pending) (void)hipEventSynchronize(p->stage_done);
+        (void)hipEventDestroy(p->stage_done);
+    }
     if (p->h_pairs) (void)hipHostFree(p->h_pairs);
     if (p->h_pt) (void)hipHostFree(p->h_pt);
     if (p->d_pairs) (void)hipFree(p->d_pairs);
+    if (p->h_stage) (void)hipHostFree(p->h_stage);
+    if (p->d_stage) (void)hipFree(p->d_stage);
+    if (p->h_spairs) (void)hipHostFree(p->h_spairs);
+    if (p->d_spairs) (void)hipFree(p->d_spairs);
     delete p;
 }
 
@@ -185,31 +241,35 @@ lsa_status lsa_gather_kv(lsa_pool* p, const int32_t* sel_ids, const int32_t* sel
     hipStream_t cs = (hipStream_t)copy_stream;
     if (wait_event && hipStreamWaitEvent(cs, (hipEvent_t)wait_event, 0) != hipSuccess)
         return LSA_ERR_HIP;
-    if (npairs > 0) {
-        if (p->on_host) {
-            int i = 0;
-            while (i < npairs) {
-                int j = i + 1;
-                while (j < npairs && p->h_pairs[2 * j] == p->h_pairs[2 * (j - 1)] + 1 &&
-                       p->h_pairs[2 * j + 1] == p->h_pairs[2 * (j - 1) + 1] + 1)
-                    ++j;
-                const int64_t src = p->h_pairs[2 * i], dst = p->h_pairs[2 * i + 1];
-                if (hipMemcpyAsync(p->slots + dst * p->page_bytes, p->cold + src * p->page_bytes,
-                                   (size_t)(j - i) * p->page_bytes, hipMemcpyHostToDevice,
-                                   cs) != hipSuccess)
-                    return LSA_ERR_HIP;
-                ++st.copies;
-                i = j;
-            }
-        } else {
-            if (hipMemcpyAsync(p->d_pairs, p->h_pairs, (size_t)npairs * 2 * sizeof(int32_t),
-                               hipMemcpyHostToDevice, cs) != hipSuccess)
-                return LSA_ERR_HIP;
-            if (launch_gather(p->d_pairs, npairs, p->cold, p->slots, p->page_bytes, cs) !=
-                hipSuccess)
-                return LSA_ERR_HIP;
-            st.copies = 1;
+    if (npairs > 0 && !p->on_host) {
+        if (hipMemcpyAsync(p->d_pairs, p->h_pairs, (size_t)npairs * 2 * sizeof(int32_t),
+                           hipMemcpyHostToDevice, cs) != hipSuccess)
+            return LSA_ERR_HIP;
+        if (launch_gather(p->d_pairs, npairs, p->cold, p->slots, p->page_bytes, cs) != hipSuccess)
+            return LSA_ERR_HIP;
+        st.copies = 1;
+    }
+    for (int b0 = 0; p->on_host && b0 < npairs; b0 += kStageChunks) {
+        const int n = std::min(kStageChunks, npairs - b0);
+        if (p->stage_pending) {  // the previous batch's uploads still read h_stage
+            if (hipEventSynchronize(p->stage_done) != hipSuccess) return LSA_ERR_HIP;
+            p->stage_pending = false;
         }
+        pack_chunks(p->h_stage, p->cold, p->h_pairs + 2 * b0, n, p->page_bytes);
+        for (int i = 0; i < n; ++i) {
+            p->h_spairs[2 * i] = i;
+            p->h_spairs[2 * i + 1] = p->h_pairs[2 * (b0 + i) + 1];
+        }
+        if (hipMemcpyAsync(p->d_stage, p->h_stage, (size_t)n * p->page_bytes, hipMemcpyHostToDevice,
+                           cs) != hipSuccess ||
+            hipMemcpyAsync(p->d_spairs, p->h_spairs, (size_t)n * 2 * sizeof(int32_t),
+                           hipMemcpyHostToDevice, cs) != hipSuccess ||
+            hipEventRecord(p->stage_done, cs) != hipSuccess)
+            return LSA_ERR_HIP;
+        p->stage_pending = true;
+        if (launch_gather(p->d_spairs, n, p->d_stage, p->slots, p->page_bytes, cs) != hipSuccess)
+            return LSA_ERR_HIP;
+        ++st.copies;
     }
     // ---- page table of the new selection ----
     if (nh > 0) {

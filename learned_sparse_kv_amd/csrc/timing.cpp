@@ -22,6 +22,8 @@ struct Pair {
 };
 
 std::atomic<int> g_on{0};
+std::atomic<int> g_every{1};     // bracket every n-th launch of a timed kernel
+std::map<std::string, int64_t> g_seen;  // launches of each timed kernel (under g_mu)
 std::atomic<int> g_filtered{0};  // time only the kernel named in g_only
 char g_only[64] = {0};
 std::mutex g_mu;
@@ -39,8 +41,10 @@ hipEvent_t take_event() {
             return e;
         }
     }
+    // timing only: no system-scope fence (no cache writeback and invalidate
+    // between the bracketed kernel and its neighbours)
     hipEvent_t e = nullptr;
-    return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+    return hipEventCreateWithFlags(&e, hipEventDisableSystemFence) == hipSuccess ? e : nullptr;
 }
 
 }  // namespace
@@ -51,6 +55,11 @@ static bool wanted(const char* name) {
 
 void timing_begin(const char* name, hipStream_t s) {
     if (!g_on.load(std::memory_order_relaxed) || !wanted(name)) return;
+    const int every = g_every.load(std::memory_order_relaxed);
+    if (every > 1) {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if (g_seen[name]++ % every != 0) return;
+    }
     t_start = take_event();
     if (t_start) (void)hipEventRecord(t_start, s);
 }
@@ -88,6 +97,12 @@ lsa_status lsa_timing_enable(int32_t on) {
     return LSA_OK;
 }
 
+lsa_status lsa_timing_every(int32_t n) {
+    if (n < 1) return LSA_ERR_INVALID_ARG;
+    g_every.store(n);
+    return LSA_OK;
+}
+
 lsa_status lsa_timing_only(const char* kernel) {
     if (kernel && std::strlen(kernel) >= sizeof(g_only)) return LSA_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> lk(g_mu);
@@ -103,6 +118,7 @@ void lsa_timing_reset(void) {
     std::lock_guard<std::mutex> lk(g_mu);
     drain();
     g_done.clear();
+    g_seen.clear();
 }
 
 lsa_status lsa_timing_read(const char* kernel, int64_t* launches, double* total_ms) {

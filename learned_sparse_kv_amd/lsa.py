@@ -109,6 +109,7 @@ def _load():
         "lsa_step64": ([P, C.POINTER(lsa_window_in), C.POINTER(lsa_window_out), P, P], I),
         "lsa_timing_enable": ([I32], I),
         "lsa_timing_only": ([C.c_char_p], I),
+        "lsa_timing_every": ([I32], I),
         "lsa_timing_reset": ([], None),
         "lsa_timing_read": ([C.c_char_p, C.POINTER(I64), C.POINTER(C.c_double)], I),
         "lsa_stream_read": ([P, SZ, P, P], I),
@@ -364,6 +365,10 @@ def lsa_timing_enable(on: bool):
 
 def lsa_timing_only(kernel=None):
     _check("lsa_timing_only", _lib.lsa_timing_only(kernel.encode() if kernel else None))
+
+
+def lsa_timing_every(n: int):
+    _check("lsa_timing_every", _lib.lsa_timing_every(int(n)))
 
 
 def lsa_timing_reset():
