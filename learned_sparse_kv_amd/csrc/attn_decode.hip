@@ -227,10 +227,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
     __builtin_amdgcn_s_barrier();
 
     // wave w loads blocks w, w + NW, ... of a tile: slot L of block (tb, ks) is
-    // key row 16 tb + l16, bytes 64 ks + 16 lq .. +16
+    // key row 16 tb + (l16 ^ 8 (lq & 1)), bytes 64 ks + 16 lq .. +16.  The
+    // XOR puts the two 8-dim groups a transposed V read takes together (256 B
+    // apart, the same banks) on different halves of the banks.
+    const int l16x = l16 ^ ((lq & 1) << 3);
     auto load_tile = [&](int t, int buf) __attribute__((always_inline)) {
-        const uint8_t* ra0 = (const uint8_t*)rowp[t * MT + l16];
-        const uint8_t* ra1 = (const uint8_t*)rowp[t * MT + 16 + l16];
+        const uint8_t* ra0 = (const uint8_t*)rowp[t * MT + l16x];
+        const uint8_t* ra1 = (const uint8_t*)rowp[t * MT + 16 + l16x];
         const uint32_t dst = lds_u32(tiles[buf]);
 #pragma unroll
         for (int m = 0; m < NLmax; ++m) {
@@ -258,8 +261,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
 
     // V^T operand read offsets inside a tile (token half 0; half 1 is + 18 KB)
     // lane (n = l16, lq) points at row 4 lq + n / 4, dims 16 vbg + 4 (n % 4)
-    const int tr_slot_row = 4 * lq + (l16 >> 2);
     const int tr_lqp_lo = (l16 & 3) >> 1, tr_sub = 8 * (l16 & 1);
+    const int tr_slot_row = (4 * lq + (l16 >> 2)) ^ (tr_lqp_lo << 3);  // swizzled slot of the row
 
     float s[HPW][8], mx[HPW];  // s[hb][tb * 4 + i]: token 16 tb + 4 lq + i of head h0 + 16 hb + l16
     // scores of tile `it` (pair sum, scaled, masked) and their per-head max
@@ -284,7 +287,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
         for (int j = 0; j < 9; ++j)
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
-                const uint4 a = *(const uint4*)(tile + (tb * kKSteps + 9 * vh + j) * kBlk + L * 16);
+                const uint4 a = *(const uint4*)(tile + (tb * kKSteps + 9 * vh + j) * kBlk + (l16x + 16 * lq) * 16);
 #pragma unroll
                 for (int hb = 0; hb < HPW; ++hb)
                     c[tb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(Qb[hb][j]),
@@ -293,22 +296,22 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
         // swap the partials with the other wave of the pair; both waves add
         // first-half + second-half, so they hold the same S^T
         {
-            float4* mine = (float4*)(sx[w] + L * 8 * HPW);
+            float4* mine = (float4*)sx[w];  // [tb * HPW + hb][lane]: lane-contiguous, no bank conflicts
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                 for (int hb = 0; hb < HPW; ++hb)
-                    mine[tb * HPW + hb] = make_float4(c[tb][hb][0], c[tb][hb][1], c[tb][hb][2], c[tb][hb][3]);
+                    mine[(tb * HPW + hb) * 64 + L] = make_float4(c[tb][hb][0], c[tb][hb][1], c[tb][hb][2], c[tb][hb][3]);
         }
         wait_lds();
         __builtin_amdgcn_s_barrier();
-        const float4* other = (const float4*)(sx[w ^ 1] + L * 8 * HPW);
+        const float4* other = (const float4*)sx[w ^ 1];
         const int t0 = it * MT;
 #pragma unroll
         for (int hb = 0; hb < HPW; ++hb) {
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
-                const float4 o = other[tb * HPW + hb];
+                const float4 o = other[(tb * HPW + hb) * 64 + L];
                 const float ov[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
