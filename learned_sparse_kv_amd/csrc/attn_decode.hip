@@ -173,6 +173,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[kNBuf][kTileB];
     __shared__ __attribute__((aligned(16))) float sx[NW][64 * 8 * HPW];
     __shared__ uint64_t rowp[kMaxSplitPos];
+    __shared__ int pflag[NW];  // tiles whose partial scores wave w has published
 
     const int bi = blockIdx.x;
     const int xcd = bi & 7, jb = bi >> 3;
@@ -220,6 +221,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
             rowp[i] = (uint64_t)row;
         }
     }
+    if (L == 0) pflag[w] = 0;
     // every load of the compiler's own is done before the tile loads start,
     // so that the vmcnt waits in the loop count tile loads only
     wait_vm<0>();
@@ -231,9 +233,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
     // XOR puts the two 8-dim groups a transposed V read takes together (256 B
     // apart, the same banks) on different halves of the banks.
     const int l16x = l16 ^ ((lq & 1) << 3);
-    auto load_tile = [&](int t, int buf) __attribute__((always_inline)) {
-        const uint8_t* ra0 = (const uint8_t*)rowp[t * MT + l16x];
-        const uint8_t* ra1 = (const uint8_t*)rowp[t * MT + 16 + l16x];
+    // the two row addresses a lane loads from for tile t (read from LDS one
+    // tile ahead of their use, so the loads issue without waiting on LDS)
+    auto tile_rows = [&](int t, uint64_t& a0, uint64_t& a1) __attribute__((always_inline)) {
+        a0 = rowp[t * MT + l16x];
+        a1 = rowp[t * MT + 16 + l16x];
+    };
+    auto load_tile = [&](uint64_t a0, uint64_t a1, int buf) __attribute__((always_inline)) {
+        const uint8_t* ra0 = (const uint8_t*)a0;
+        const uint8_t* ra1 = (const uint8_t*)a1;
         const uint32_t dst = lds_u32(tiles[buf]);
 #pragma unroll
         for (int m = 0; m < NLmax; ++m) {
@@ -244,8 +252,16 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
             }
         }
     };
-    if (ntiles > 0) load_tile(0, 0);
-    if (ntiles > 1) load_tile(1, 1);
+    uint64_t na0 = 0, na1 = 0;  // row addresses of the next tile to load
+    if (ntiles > 0) {
+        tile_rows(0, na0, na1);
+        load_tile(na0, na1, 0);
+    }
+    if (ntiles > 1) {
+        tile_rows(1, na0, na1);
+        load_tile(na0, na1, 1);
+    }
+    if (ntiles > 2) tile_rows(2, na0, na1);
 
     f32x4_t acc[HPW][16];
 #pragma unroll
@@ -276,7 +292,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
             wait_vm<0>();
         }
         __builtin_amdgcn_s_barrier();  // tile `it` in LDS; tile it - 1 released
-        if (it + 2 < ntiles) load_tile(it + 2, (it + 2) % kNBuf);
+        if (it + 2 < ntiles) {
+            load_tile(na0, na1, (it + 2) % kNBuf);
+            if (it + 3 < ntiles) tile_rows(it + 3, na0, na1);
+        }
         const uint8_t* tile = tiles[it % kNBuf];
         f32x4_t c[2][HPW];
 #pragma unroll
@@ -303,10 +322,21 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
                 for (int hb = 0; hb < HPW; ++hb)
                     mine[(tb * HPW + hb) * 64 + L] = make_float4(c[tb][hb][0], c[tb][hb][1], c[tb][hb][2], c[tb][hb][3]);
         }
-        wait_lds();
-        __builtin_amdgcn_s_barrier();
+        // publish them (the release orders the data writes before the flag)
+        // and wait for the partner's: only the pair meets here, not the
+        // block.  The wait is bounded; the partner runs the same tile loop, so
+        // it always publishes.
+        __hip_atomic_store(&pflag[w], it + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        for (int spin = 0; spin < (1 << 20); ++spin) {
+            const int f = __hip_atomic_load(&pflag[w ^ 1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (__builtin_amdgcn_readfirstlane(f) > it) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
         const float4* other = (const float4*)sx[w ^ 1];
         const int t0 = it * MT;
+        // the sum of two terms is the same in either order, so both waves of
+        // the pair get the same scores; only a last, partial tile is masked
+        const bool partial = t0 + MT > npos;  // uniform
 #pragma unroll
         for (int hb = 0; hb < HPW; ++hb) {
 #pragma unroll
@@ -314,12 +344,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
                 const float4 o = other[(tb * HPW + hb) * 64 + L];
                 const float ov[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float lo = vh ? ov[i] : c[tb][hb][i];
-                    const float hi = vh ? c[tb][hb][i] : ov[i];
-                    const int tok = t0 + 16 * tb + 4 * lq + i;
-                    s[hb][tb * 4 + i] = tok < npos ? (lo + hi) * sm_log2e : -INFINITY;
-                }
+                for (int i = 0; i < 4; ++i) s[hb][tb * 4 + i] = (c[tb][hb][i] + ov[i]) * sm_log2e;
+            }
+            if (partial) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (t0 + 16 * (e >> 2) + 4 * lq + (e & 3) >= npos) s[hb][e] = -INFINITY;
             }
             float m = s[hb][0];
 #pragma unroll
@@ -511,45 +541,50 @@ __global__ __launch_bounds__(256) void k_attn_f32(GeomDev g, PosMap pm, const in
 }
 
 // ----------------------------------------------------------------------------
-// merge of the splits: one wave per (request, head, 128 value columns); the
-// partial rows are fp32 (f32 path) or bf16 (bf16 latent path).  The
-// split weights 2^(m_s - m) and the total sum are formed by the wave in a
-// fixed order; then each lane combines two columns over all splits, in
-// split order, with up to 32 splits' loads in flight at once.
+// merge of the splits: one wave per (request, head, 64 * VPL value columns),
+// VPL = 16 bytes of a partial row per lane (8 bf16 columns on the bf16 latent
+// path, 4 fp32 columns on the f32 path), so a wave reads a whole 1 KB
+// partial row per load and has up to kMergeBatch splits' rows in flight.
+// The split weights 2^(m_s - m) and the total sum are formed by the wave in
+// a fixed order; each lane then combines its columns over all splits in
+// split order.
 // ----------------------------------------------------------------------------
 constexpr int kMergeMaxSplits = 1024;
-constexpr int kMergeCols = 128;
-constexpr int kMergeBatch = 32;
+constexpr int kMergeWaves = 4;   // waves per block
+constexpr int kMergeBatch = 16;  // partial rows in flight per lane
+
+template <typename PT>
+__host__ __device__ inline int merge_col_blocks(int Dv) {
+    constexpr int VPL = 16 / (int)sizeof(PT);
+    return (Dv + 64 * VPL - 1) / (64 * VPL);
+}
 
 template <int ODT, typename PT>
-__global__ __launch_bounds__(64) void k_attn_merge(const PT* __restrict__ part_o,
-                                                   const float* __restrict__ part_ml, int Hq, int Dv,
-                                                   int n_splits, void* __restrict__ out,
-                                                   float* __restrict__ lse) {
-    __shared__ float fac[kMergeMaxSplits];
-    const int nchunk = (Dv + kMergeCols - 1) / kMergeCols;
-    const int rh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;  // rh = r * Hq + h
+__global__ __launch_bounds__(64 * kMergeWaves) void k_attn_merge(const PT* __restrict__ part_o,
+                                                               const float* __restrict__ part_ml,
+                                                               int B, int Hq, int Dv, int n_splits,
+                                                               void* __restrict__ out,
+                                                               float* __restrict__ lse) {
+    constexpr int VPL = 16 / (int)sizeof(PT);
+    __shared__ float fac_s[kMergeWaves][kMergeMaxSplits];
+    const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
+    const int ncb = merge_col_blocks<PT>(Dv);
+    const int unit = blockIdx.x * kMergeWaves + w;  // (r * Hq + h) * ncb + cb
+    if (unit >= B * Hq * ncb) return;               // uniform per wave
+    const int rh = unit / ncb, cb = unit % ncb;
     const int r = rh / Hq, h = rh % Hq;
-    const int L = threadIdx.x;
+    float* fac = fac_s[w];
     const int64_t b0 = (int64_t)r * n_splits * Hq + h;  // split s: (b0 + s*Hq)
-    const int v = chunk * kMergeCols + 2 * L;
-    const bool col = v < Dv;
+    const int v = (cb * 64 + L) * VPL;                  // first column of the lane
+    const bool col = v < Dv;                            // Dv is a multiple of VPL
     const PT* src = part_o + b0 * Dv + v;
     const int64_t stride = (int64_t)Hq * Dv;
-    // two columns of a partial row as loaded (unpacked only where used, so a
-    // whole batch of loads stays in flight)
-    using Raw = typename std::conditional<sizeof(PT) == 4, float2, uint32_t>::type;
-    auto ld2 = [&](int64_t i) -> Raw { return *(const Raw*)(src + i); };
-    auto unpack = [](Raw w) -> float2 {
-        if constexpr (sizeof(PT) == 4) return w;
-        else return make_float2(bf16_lo(w), bf16_hi(w));
-    };
     // the first batch of partial rows is requested before the split weights
     // are formed, so both latencies overlap
-    Raw x[kMergeBatch];
+    uint4 x[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u)
-        if (col && u < n_splits) x[u] = ld2((int64_t)u * stride);
+        if (col && u < n_splits) x[u] = *(const uint4*)(src + (int64_t)u * stride);
     float m = -INFINITY;
     for (int s = L; s < n_splits; s += 64) m = fmaxf(m, part_ml[(b0 + (int64_t)s * Hq) * 2]);
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
@@ -563,37 +598,62 @@ __global__ __launch_bounds__(64) void k_attn_merge(const PT* __restrict__ part_o
     // fixed-order tree over the lanes
     for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
     const float Lsum = part, inv = 1.0f / part;
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (col) {
-        float ox = 0.0f, oy = 0.0f;
+        float o[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) o[i] = 0.0f;
         for (int s0 = 0; s0 < n_splits; s0 += kMergeBatch) {
             if (s0 > 0) {
 #pragma unroll
                 for (int u = 0; u < kMergeBatch; ++u)
-                    if (s0 + u < n_splits) x[u] = ld2((int64_t)(s0 + u) * stride);
+                    if (s0 + u < n_splits) x[u] = *(const uint4*)(src + (int64_t)(s0 + u) * stride);
             }
 #pragma unroll
             for (int u = 0; u < kMergeBatch; ++u) {
                 if (s0 + u < n_splits) {
                     const float f = fac[s0 + u];
                     if (f != 0.0f) {
-                        const float2 xv = unpack(x[u]);
-                        ox += xv.x * f;
-                        oy += xv.y * f;
+                        const uint32_t wd[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+                        for (int i = 0; i < VPL; ++i) {
+                            float xv;
+                            if constexpr (sizeof(PT) == 4) xv = __uint_as_float(wd[i]);
+                            else xv = (i & 1) ? bf16_hi(wd[i >> 1]) : bf16_lo(wd[i >> 1]);
+                            o[i] += xv * f;
+                        }
                     }
                 }
             }
         }
-        // element stores: the output pointer carries no alignment promise
+        const int64_t ob = (int64_t)rh * Dv + v;
         if constexpr (ODT == LSA_F32) {
-            ((float*)out)[(int64_t)rh * Dv + v] = ox * inv;
-            ((float*)out)[(int64_t)rh * Dv + v + 1] = oy * inv;
+            float* dst = (float*)out + ob;
+            if (((uintptr_t)dst & 15) == 0) {
+                *(float4*)dst = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+            } else {
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) dst[i] = o[i] * inv;
+            }
         } else {
-            ((uint16_t*)out)[(int64_t)rh * Dv + v] = f2bf(ox * inv);
-            ((uint16_t*)out)[(int64_t)rh * Dv + v + 1] = f2bf(oy * inv);
+            uint16_t* dst = (uint16_t*)out + ob;
+            uint16_t y[VPL];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) y[i] = f2bf(o[i] * inv);
+            if (VPL == 8 && ((uintptr_t)dst & 15) == 0) {
+                uint32_t pk[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pk[i] = (uint32_t)y[2 * i] | ((uint32_t)y[2 * i + 1] << 16);
+                *(uint4*)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) dst[i] = y[i];
+            }
         }
     }
-    if (lse && chunk == 0 && L == 0) lse[rh] = (m + __log2f(Lsum)) * kLn2;
+    if (lse && cb == 0 && L == 0) lse[rh] = (m + __log2f(Lsum)) * kLn2;
 }
 
 }  // namespace
@@ -685,14 +745,17 @@ hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, in
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int nchunk = (kv.Dv + kMergeCols - 1) / kMergeCols;
+    const int units = g.B * Hq * (plan.mode == 1 ? merge_col_blocks<uint16_t>(kv.Dv)
+                                                 : merge_col_blocks<float>(kv.Dv));
+    const int mblocks = (units + kMergeWaves - 1) / kMergeWaves;
     timing_begin("k_attn_merge", s);
     if (plan.mode != 1)
-        hipLaunchKernelGGL((k_attn_merge<LSA_F32, float>), dim3(g.B * Hq * nchunk), dim3(64), 0, s,
-                           (const float*)part_o, part_ml, Hq, kv.Dv, plan.n_splits, out, lse);
+        hipLaunchKernelGGL((k_attn_merge<LSA_F32, float>), dim3(mblocks), dim3(64 * kMergeWaves), 0,
+                           s, (const float*)part_o, part_ml, g.B, Hq, kv.Dv, plan.n_splits, out, lse);
     else
-        hipLaunchKernelGGL((k_attn_merge<LSA_BF16, uint16_t>), dim3(g.B * Hq * nchunk), dim3(64), 0, s,
-                           (const uint16_t*)part_o, part_ml, Hq, kv.Dv, plan.n_splits, out, lse);
+        hipLaunchKernelGGL((k_attn_merge<LSA_BF16, uint16_t>), dim3(mblocks), dim3(64 * kMergeWaves),
+                           0, s, (const uint16_t*)part_o, part_ml, g.B, Hq, kv.Dv, plan.n_splits,
+                           out, lse);
     timing_end("k_attn_merge", s);
     return hipGetLastError();
 }
