@@ -81,7 +81,8 @@ __device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even
 // and l share the reference, the result is the same softmax.
 //
 // KV tiles: 32 rows land in LDS by direct global->LDS loads (16 bytes per
-// lane), three tiles deep.  The tile is kept in the operand layout of the
+// lane), three tiles deep; the loads of tile t + 2 are spread over the score
+// products of tile t.  The tile is kept in the operand layout of the
 // matrix core: block (token half tb, k-step ks) holds 64 slots of 16 bytes,
 // slot lq*16 + t = key row 16 tb + t, dims 32 ks + 8 lq .. +8, so the S
 // operand read of a wave is one contiguous 1 KB.  ds_read_b64_tr_b16 turns
@@ -186,13 +187,6 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
     const int h0 = hg * (8 * HPW * NW) + 16 * HPW * (w >> 1);  // first head of the pair
     const int nl = (NB % NW == 0 || w < NB % NW) ? NLmax : NLmax - 1;  // this wave's tile loads
 
-    const int kcnt = min(max(tcnt[r], 0), pm.k);
-    const int nrec = g.nrec[r];
-    const int P = nrec + kcnt;
-    const int p_begin = split * per_split;
-    const int npos = max(0, min(per_split, P - p_begin));
-    const int ntiles = (npos + MT - 1) / MT;
-
     // query slices (B operands): head h0 + 16 hb + l16, k-steps 9 vh .. 9 vh + 8
     u32x4_t Qb[HPW][9];
     {
@@ -202,28 +196,59 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
 #pragma unroll
             for (int j = 0; j < 9; ++j) Qb[hb][j] = *(const u32x4_t*)(qr + (hb * 16 + l16) * MDK + j * 32);
     }
-    // row address of every position of the split (the tail repeats the last)
+    const int nrec = g.nrec[r];
+    const int p_begin = split * per_split;
+    // A split inside the recent window needs neither the top-k count nor the
+    // list.  The others request the count and their share of the list (up to
+    // k entries, before the count is known) at once, then the page of each
+    // valid entry.
+    const bool rec_only = p_begin + per_split <= nrec;  // uniform
+    constexpr int kPT = kMaxSplitPos / (64 * NW);      // positions per thread, at most
+    int sl[kPT];
+    int tc = 0;
+#pragma unroll
+    for (int u = 0; u < kPT; ++u) sl[u] = 0;
+    if (!rec_only) {
+        const int32_t* tk = pm.topk + (int64_t)r * pm.k;
+        tc = tcnt[r];
+#pragma unroll
+        for (int u = 0; u < kPT; ++u) {
+            const int i = tid + 64 * NW * u, p = p_begin + i;
+            if (i < per_split && p >= nrec && p < nrec + pm.k) sl[u] = tk[p - nrec];
+        }
+    }
+    const int kcnt = min(max(tc, 0), pm.k);
+    const int npos = rec_only ? per_split : max(0, min(per_split, nrec + kcnt - p_begin));
+    const int ntiles = (npos + MT - 1) / MT;
+    // row address of every valid position of the split (the loads of the
+    // last tile's tail repeat position npos - 1)
     {
         const uint8_t* rec0 = pm.recent + g.rec_off[r] * pm.row_bytes;
         const int64_t coff = g.chunk_off[r];
-        const int32_t* tk = pm.topk + (int64_t)r * pm.k;
-        for (int i = tid; i < ntiles * MT; i += 64 * NW) {
-            const int p = p_begin + min(i, npos - 1);
-            const uint8_t* row;
-            if (p < nrec) {
-                row = rec0 + (int64_t)p * pm.row_bytes;
-            } else {
-                const int sl = tk[p - nrec];
-                const int64_t c = coff + (sl >> 6);
-                const int64_t slot = pm.pt ? (int64_t)pm.pt[c] : c;
-                row = pm.pages + slot * pm.page_bytes + (int64_t)(sl & 63) * pm.row_bytes;
+#pragma unroll
+        for (int u = 0; u < kPT; ++u) {
+            const int i = tid + 64 * NW * u, p = p_begin + i;
+            if (i < npos) {
+                const uint8_t* row;
+                if (p < nrec) {
+                    row = rec0 + (int64_t)p * pm.row_bytes;
+                } else {
+                    const int64_t c = coff + (sl[u] >> 6);
+                    const int64_t slot = pm.pt ? (int64_t)pm.pt[c] : c;
+                    row = pm.pages + slot * pm.page_bytes + (int64_t)(sl[u] & 63) * pm.row_bytes;
+                }
+                rowp[i] = (uint64_t)row;
             }
-            rowp[i] = (uint64_t)row;
         }
     }
     if (L == 0) pflag[w] = 0;
     // every load of the compiler's own is done before the tile loads start,
-    // so that the vmcnt waits in the loop count tile loads only
+    // so that the vmcnt waits in the loop count tile loads only (the uses of
+    // the query slices make the compiler wait for them here, not in the loop)
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb)
+#pragma unroll
+        for (int j = 0; j < 9; ++j) asm volatile("" : : "v"(Qb[hb][j]));
     wait_vm<0>();
     wait_lds();
     __builtin_amdgcn_s_barrier();
@@ -236,8 +261,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
     // the two row addresses a lane loads from for tile t (read from LDS one
     // tile ahead of their use, so the loads issue without waiting on LDS)
     auto tile_rows = [&](int t, uint64_t& a0, uint64_t& a1) __attribute__((always_inline)) {
-        a0 = rowp[t * MT + l16x];
-        a1 = rowp[t * MT + 16 + l16x];
+        a0 = rowp[min(t * MT + l16x, npos - 1)];
+        a1 = rowp[min(t * MT + 16 + l16x, npos - 1)];
     };
     auto load_tile = [&](uint64_t a0, uint64_t a1, int buf) __attribute__((always_inline)) {
         const uint8_t* ra0 = (const uint8_t*)a0;
@@ -250,6 +275,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
                 const int tb = b >= kKSteps ? 1 : 0, ks = b - kKSteps * tb;
                 lds_dma16((tb ? ra1 : ra0) + ks * 64 + lq * 16, dst + b * kBlk);
             }
+        }
+    };
+    // the wave's m-th block of a tile (the loop spreads these over its k-steps)
+    auto load_block = [&](uint64_t a0, uint64_t a1, int buf, int m) __attribute__((always_inline)) {
+        const int b = w + NW * m;
+        if (b < NB) {
+            const int tb = b >= kKSteps ? 1 : 0, ks = b - kKSteps * tb;
+            lds_dma16((const uint8_t*)(tb ? a1 : a0) + ks * 64 + lq * 16, lds_u32(tiles[buf]) + b * kBlk);
         }
     };
     uint64_t na0 = 0, na1 = 0;  // row addresses of the next tile to load
@@ -292,10 +325,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
             wait_vm<0>();
         }
         __builtin_amdgcn_s_barrier();  // tile `it` in LDS; tile it - 1 released
-        if (it + 2 < ntiles) {
-            load_tile(na0, na1, (it + 2) % kNBuf);
-            if (it + 3 < ntiles) tile_rows(it + 3, na0, na1);
-        }
+        // tile it + 2 goes into the buffer tile it - 1 released at the barrier;
+        // its loads issue one per k-step below: issued together right after
+        // the barrier, every wave's loads queue at once and hold the waves up
+        const bool more = it + 2 < ntiles;  // uniform
+        const int nbuf = (it + 2) % kNBuf;
         const uint8_t* tile = tiles[it % kNBuf];
         f32x4_t c[2][HPW];
 #pragma unroll
@@ -311,7 +345,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
                 for (int hb = 0; hb < HPW; ++hb)
                     c[tb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(Qb[hb][j]),
                                                                         c[tb][hb], 0, 0, 0);
+                if (tb == 1 && j < NLmax && more) load_block(na0, na1, nbuf, j);
             }
+        if (more && it + 3 < ntiles) tile_rows(it + 3, na0, na1);
         // swap the partials with the other wave of the pair; both waves add
         // first-half + second-half, so they hold the same S^T
         {
