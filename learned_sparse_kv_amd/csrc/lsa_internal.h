@@ -109,9 +109,15 @@ size_t band_ws_bytes(const GeomDev& g);
 hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_t* cnt,
                               const void* pages, int64_t page_bytes, int64_t ikey_off,
                               const int32_t* page_table, lsa_dtype idx_dt,
-                              const float* ikey_scale, const void* q, const float* w, int H,
+                              const float* ikey_scale, const int32_t* sel_slot,
+                              const float* sel_scale, const void* q, const float* w, int H,
                               int d, int k, int32_t* topk, int32_t* tcnt, void* ws, bool ws_clean,
                               hipStream_t s);
+// sel_slot / sel_scale: pages and scales of the selected chunks in selection
+// order (-1 past the count), for launch_refine_band (nullptr: looked up there).
+hipError_t launch_resolve_sel(const GeomDev& g, const int32_t* sel, const int32_t* cnt,
+                              const int32_t* page_table, const float* ikey_scale,
+                              int32_t* sel_slot, float* sel_scale, hipStream_t s);
 // Zeroes the part of a band workspace that must start at zero (every band
 // launch leaves it zero again).
 hipError_t launch_band_clear(const GeomDev& g, void* ws, hipStream_t s);

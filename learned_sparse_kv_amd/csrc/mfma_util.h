@@ -9,6 +9,15 @@ namespace lsa_dev {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// Block barrier for data shared through LDS only: it waits for the wave's
+// LDS operations but lets its global loads and stores stay in flight (the
+// workgroup release of a __syncthreads() waits for all of them).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Two ulps of fp32 per operation: Higham's gamma(n) = n u / (1 - n u) taken
 // with u = 2^-22, which also covers an accumulation that truncates.
 constexpr float kU2 = 2.384185791015625e-07f;

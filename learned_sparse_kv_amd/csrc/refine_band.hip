@@ -72,7 +72,7 @@ __device__ __forceinline__ int block_scan(int v, int* wsum, int& total) {
         if (lane >= o) incl += t;
     }
     if (lane == 63) wsum[wv] = incl;
-    __syncthreads();
+    lds_barrier();
     int wpre = 0, tot = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
@@ -80,7 +80,7 @@ __device__ __forceinline__ int block_scan(int v, int* wsum, int& total) {
         wpre += (i < wv) ? x : 0;
         tot += x;
     }
-    __syncthreads();
+    lds_barrier();
     total = tot;
     return wpre + incl - v;
 }
@@ -110,14 +110,14 @@ __device__ __forceinline__ void kth_bin(const uint32_t* hist, int k, int* wsum, 
         out[0] = NB - 1 - (tid * BPT + j);
         out[1] = acc;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // Copies n words of a histogram into LDS.
 __device__ __forceinline__ void load_hist(const uint32_t* gh, uint32_t* lds, int n) {
 #pragma unroll 8
     for (int i = threadIdx.x; i < n; i += blockDim.x) lds[i] = gh[i];
-    __syncthreads();
+    lds_barrier();
 }
 
 // ---------------------------------------------------------------------------
@@ -131,6 +131,7 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
     GeomDev g, const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
     const uint8_t* __restrict__ pages, int64_t page_bytes, int64_t ikey_off,
     const int32_t* __restrict__ page_table, const float* __restrict__ ikey_scale,
+    const int32_t* __restrict__ sel_slot, const float* __restrict__ sel_scale,
     const uint16_t* __restrict__ q, const float* __restrict__ w, uint2* __restrict__ lu,
     uint32_t* __restrict__ hist) {
     constexpr int EB = KDT == LSA_BF16 ? 2 : 1;
@@ -138,43 +139,62 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
     constexpr int KS = D / 32;   // MFMA k-steps
     constexpr int HB = H / 16;   // head blocks
     constexpr int NR = KDT == LSA_BF16 ? KS : KS / 2;  // 16-byte key loads per token row and lane
+    constexpr int QROW = D * 2 + 16;      // bytes per query row in LDS (padded: no bank conflicts)
     __shared__ uint32_t hl[2 * kCoarse];  // coarse L bins, then coarse U bins
     __shared__ float red[kWaves][64 * kRedStride];
+    __shared__ __attribute__((aligned(16))) uint8_t qs[H * QROW];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, lq = lane >> 4;
     const int r = blockIdx.y, X = gridDim.x;
-    const int nc = cnt[r];
-    for (int i = tid; i < 2 * kCoarse; i += 64 * kWaves) hl[i] = 0;
-    __syncthreads();
-    if ((int)blockIdx.x * kWaves < nc) {  // uniform across the block
-        const int64_t off = g.chunk_off[r];
-        const int stride = X * kWaves;
-        const int i0 = blockIdx.x * kWaves + wv;  // this wave's chunks: i0 + j * stride
-        const int nj = i0 < nc ? (nc - i0 + stride - 1) / stride : 0;
-        // chunk j0 + lane: page (slot) index and scale, 64 chunks at a time
-        int64_t pg_l = 0;
-        float sc_l = 1.0f;
-        auto load_idx = [&](int j0) __attribute__((always_inline)) {
-            if (j0 + lane < nj) {
-                const int c = sel[off + i0 + (j0 + lane) * stride];
+    const int64_t off = g.chunk_off[r];
+    const int nhr = g.nhist[r];
+    const int stride = X * kWaves;
+    const int i0 = blockIdx.x * kWaves + wv;  // this wave's chunks: i0 + j * stride
+    // chunk j0 + lane: page (slot) index and scale, 64 chunks at a time.  The
+    // first window is requested together with the selection count, before
+    // the count is known (bounded by the request's chunks, so in range); the
+    // entries past the count are never used.  With sel_slot the pages of the
+    // selected chunks come resolved (one load instead of two).
+    int64_t pg_l = 0;
+    float sc_l = 1.0f;
+    auto load_idx = [&](int j0, int nlim) __attribute__((always_inline)) {
+        if (j0 + lane < nlim) {
+            const int i = i0 + (j0 + lane) * stride;
+            if (sel_slot) {
+                pg_l = (int64_t)sel_slot[off + i];
+                if constexpr (KDT == LSA_FP8_E4M3FN) sc_l = sel_scale[off + i];
+            } else {
+                const int c = min(max(sel[off + i], 0), nhr - 1);
                 pg_l = page_table ? (int64_t)page_table[off + c] : off + c;
                 if constexpr (KDT == LSA_FP8_E4M3FN) sc_l = ikey_scale[off + c];
             }
-        };
-        // the dependent index loads go first, the query operands load behind
-        // them, the first key rows as soon as their pages are known, and the
-        // query norms are formed while the key rows are in flight
-        if (nj > 0) load_idx(0);
-        uint4 qb[HB][KS];
-        float wl[HB], wa[HB];
-        const uint16_t* qr = q + (int64_t)r * H * D;
+        }
+    };
+    const int nj_max = i0 < nhr ? (nhr - i0 + stride - 1) / stride : 0;
+    load_idx(0, nj_max);
+    const int nc = cnt[r];
+    // the query rows load behind the index loads, once per block into LDS
+    // (each wave takes its operands from there); the first key rows load as
+    // soon as their pages are known, and the query norms are formed while
+    // the key rows are in flight
+    {
+        const uint4* qr = (const uint4*)(q + (int64_t)r * H * D);
+        for (int e = tid; e < H * D / 8; e += 64 * kWaves)
+            *(uint4*)(qs + (e / (D / 8)) * QROW + (e % (D / 8)) * 16) = qr[e];
+    }
+    float wl[HB], wa[HB];
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
+    for (int hb = 0; hb < HB; ++hb) wl[hb] = w[(int64_t)r * H + hb * 16 + l16];
+    for (int i = tid; i < 2 * kCoarse; i += 64 * kWaves) hl[i] = 0;
+    lds_barrier();
+    if ((int)blockIdx.x * kWaves < nc) {  // uniform across the block
+        const int nj = i0 < nc ? (nc - i0 + stride - 1) / stride : 0;
+        uint4 qb[HB][KS];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                qb[hb][ks] = *(const uint4*)(qr + (hb * 16 + l16) * D + kdim<KDT>(ks, lq));
-            wl[hb] = w[(int64_t)r * H + hb * 16 + l16];
-        }
+                qb[hb][ks] = *(const uint4*)(qs + (hb * 16 + l16) * QROW + kdim<KDT>(ks, lq) * 2);
         // key rows of chunk j: A operands of tokens tb*16 + l16 (16 bytes per
         // load); DEPTH chunks are in flight ahead of the one computed (two
         // where the registers allow it)
@@ -234,12 +254,12 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
                     if (j + 2 < nj) {
                         // the index window moves 64 chunks at a time; its scales
                         // are read for chunk j above, so it may move now
-                        if (((j + 2) & 63) == 0) load_idx(j + 2);
+                        if (((j + 2) & 63) == 0) load_idx(j + 2, nj);
                         fetch(j + 2, raw2);
                     }
                 }
             } else if (j + 1 < nj) {
-                if (((j + 1) & 63) == 0) load_idx(j + 1);
+                if (((j + 1) & 63) == 0) load_idx(j + 1, nj);
                 fetch(j + 1, raw);
             }
             // |key|^2 on the matrix cores: the diagonal of the 16x16 Gram block
@@ -310,10 +330,34 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t* gh = hist + (int64_t)r * kHist;
     for (int i = tid; i < 2 * kCoarse; i += 64 * kWaves)
         if (hl[i]) atomicAdd(&gh[i], hl[i]);
+}
+
+// Pages (slots) and index-key scales of the selected chunks, in selection
+// order: sel_slot[off + i] for i below the request's count, -1 from there to
+// the request's chunk count.  The window pipeline forms them once per window
+// so that K1 reaches the key rows with one dependent load instead of two.
+__global__ __launch_bounds__(256) void k_resolve_sel(GeomDev g, const int32_t* __restrict__ sel,
+                                                     const int32_t* __restrict__ cnt,
+                                                     const int32_t* __restrict__ page_table,
+                                                     const float* __restrict__ ikey_scale,
+                                                     int32_t* __restrict__ sel_slot,
+                                                     float* __restrict__ sel_scale) {
+    const int r = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= g.nhist[r]) return;
+    const int64_t off = g.chunk_off[r];
+    int32_t slot = -1;
+    float sc = 0.0f;
+    if (i < cnt[r]) {
+        const int c = sel[off + i];
+        slot = page_table ? page_table[off + c] : (int32_t)(off + c);
+        sc = ikey_scale ? ikey_scale[off + c] : 1.0f;
+    }
+    sel_slot[off + i] = slot;
+    sel_scale[off + i] = sc;
 }
 
 // Chunks [c0, c1) of a request that block x of X takes in K2 and K3.
@@ -366,7 +410,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
     const uint32_t tau_c = cL << 22;
     if (blockIdx.x == 0 && tid == 0) cinfo[r] = make_int4(s_out[0], s_out[1], s_out[2], s_out[3]);
     for (int i = tid; i < 2 * kFine; i += blockDim.x) hf[i] = 0;
-    __syncthreads();
+    lds_barrier();
     const int64_t seg = (off + c0) * 64;
     const uint64_t lt = (1ull << lane) - 1;
     int np = 0;
@@ -385,13 +429,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
             const bool pre = have && cur.y >= tau_c;
             const uint64_t m = __ballot(pre);
             if (lane == 0) s_np[wv] = __popcll(m);
-            __syncthreads();
+            lds_barrier();
             int pb = np;
             for (int w2 = 0; w2 < kWaves; ++w2) {
                 pb += w2 < wv ? s_np[w2] : 0;
                 np += s_np[w2];
             }
-            __syncthreads();
+            lds_barrier();
             if (pre) plist[seg + pb + __popcll(m & lt)] = c * 64 + lane;
         }
         // next kPre rounds
@@ -402,7 +446,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
         }
     }
     if (tid == 0) pcnt[(int64_t)r * X + blockIdx.x] = np;
-    __syncthreads();
+    lds_barrier();
     uint32_t* gf = gh + 2 * kCoarse;
     for (int i = tid; i < 2 * kFine; i += blockDim.x)
         if (hf[i]) atomicAdd(&gf[i], hf[i]);
@@ -510,6 +554,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     if (tid == 0) scnt[(int64_t)r * X + blockIdx.x] = nb;
     if (nu == 0) return;  // uniform
     // canonical scores of this block's uncertain entries
+    // the lists in global memory written above are read by other threads
+    // below (past the LDS copies): a full block barrier
     __threadfence_block();
     __syncthreads();
     float* kr = kf[wv][ts];
@@ -629,7 +675,7 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
         if (tid < X) boff[tid] = ex;
         if (tid == 0) boff[X] = tot;
     }
-    __syncthreads();
+    lds_barrier();
     const int m = boff[X];
     const bool in_lds = m <= kListCap;
     auto gidx = [&](int j) -> int64_t {  // list position j -> workspace index
@@ -660,7 +706,7 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
             lkey[j] = bk[e];
             lpos[j] = bl[e];
         }
-        __syncthreads();
+        lds_barrier();
         // The certain entries (key 0xffffffff) are all in; the uncertain ones
         // (few) are ranked against each other by (score desc, token asc) and
         // the best k - #certain are taken.
@@ -679,13 +725,13 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
                 uj[t] = j;
             }
         }
-        __syncthreads();
+        lds_barrier();
         const int u = s_u;
         if (u <= kUncCap) {
             const int need = k - (m - u);
             if (u & 1) {  // pad to an even count with an entry below every other
                 if (tid == 0) uval[u] = 0ull;
-                __syncthreads();
+                lds_barrier();
             }
             const int u2 = (u + 1) & ~1;
             for (int t = tid; t < u; t += kT) {
@@ -698,7 +744,7 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
                 }
                 lkey[uj[t]] = rank < need ? 0xffffffffu : 0u;
             }
-            __syncthreads();
+            lds_barrier();
             // emit the taken entries in list (token) order: thread t takes a
             // contiguous run of the list
             const int per = (m + kT - 1) / kT;
@@ -718,14 +764,14 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
     for (int pass = 0; pass < 3; ++pass) {
         const int shift = shifts[pass], nb = 1 << widths[pass];
         for (int i = tid; i < nb; i += kT) hist[i] = 0;
-        __syncthreads();
+        lds_barrier();
         for (int j = tid; j < m; j += kT) {
             uint32_t key;
             int32_t pos;
             at(j, key, pos);
             if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
         }
-        __syncthreads();
+        lds_barrier();
         int c4[4], s4 = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -744,7 +790,7 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
             s_remaining = remaining - acc;
             s_eq = c4[j];
         }
-        __syncthreads();
+        lds_barrier();
         prefix = s_prefix;
         remaining = s_remaining;
         mask |= (uint32_t)(nb - 1) << shift;
@@ -851,7 +897,8 @@ hipError_t launch_band_clear(const GeomDev& g, void* ws, hipStream_t s) {
 hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_t* cnt,
                               const void* pages, int64_t page_bytes, int64_t ikey_off,
                               const int32_t* page_table, lsa_dtype idx_dt,
-                              const float* ikey_scale, const void* q, const float* w, int H,
+                              const float* ikey_scale, const int32_t* sel_slot,
+                              const float* sel_scale, const void* q, const float* w, int H,
                               int d, int k, int32_t* topk, int32_t* tcnt, void* ws, bool ws_clean,
                               hipStream_t s) {
     const size_t nc = (size_t)g.chunk_off[g.B] * 64 + 64;
@@ -884,8 +931,8 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
 #define LSA_K1(KDT, D, HH)                                                                        \
     if (idx_dt == KDT && d == D && Hh == HH) {                                                    \
         hipLaunchKernelGGL((k_refine_mfma<KDT, D, HH>), dim3(X1, g.B), dim3(64 * kWaves), 0, s, g, \
-                           sel, cnt, pg, page_bytes, ikey_off, page_table, ikey_scale, qq, w,      \
-                           lu, hist);                                                             \
+                           sel, cnt, pg, page_bytes, ikey_off, page_table, ikey_scale, sel_slot,  \
+                           sel_scale, qq, w, lu, hist);                                           \
         e = hipGetLastError();                                                                    \
     }
     LSA_K1(LSA_BF16, 128, 16) LSA_K1(LSA_BF16, 128, 32) LSA_K1(LSA_BF16, 128, 64)
@@ -924,5 +971,15 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
     hipLaunchKernelGGL(k_topk_band, dim3(g.B), dim3(kT), 0, s, g, sel, cnt, scnt, X2, bl, bk, k,
                        topk, tcnt, hist);
     timing_end("k_topk_band", s);
+    return hipGetLastError();
+}
+
+hipError_t launch_resolve_sel(const GeomDev& g, const int32_t* sel, const int32_t* cnt,
+                              const int32_t* page_table, const float* ikey_scale,
+                              int32_t* sel_slot, float* sel_scale, hipStream_t s) {
+    const int mh = max_hist(g);
+    if (mh == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_resolve_sel, dim3((mh + 255) / 256, g.B), dim3(256), 0, s, g, sel, cnt,
+                       page_table, ikey_scale, sel_slot, sel_scale);
     return hipGetLastError();
 }

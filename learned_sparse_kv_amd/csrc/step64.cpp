@@ -32,6 +32,8 @@ struct lsa_ctx {
     int32_t* tcnt_tmp = nullptr;
     void* attn_ws = nullptr;
     int32_t* pt[2] = {nullptr, nullptr};
+    int32_t* sel_slot = nullptr;  // pages of the running window's selected chunks
+    float* sel_scale = nullptr;   // and their index-key scales
     int32_t* h_sel[2] = {nullptr, nullptr};
     int32_t* h_cnt[2] = {nullptr, nullptr};
     hipEvent_t ev_sel = nullptr, ev_win[2] = {nullptr, nullptr}, ev_fetch[2] = {nullptr, nullptr};
@@ -54,7 +56,7 @@ struct Carve {
 };
 
 // Workspace layout; returns total bytes (0 on invalid description).
-size_t layout(const lsa_ctx_desc* d, GeomDev* g, AttnPlan* plan, size_t offs[12]) {
+size_t layout(const lsa_ctx_desc* d, GeomDev* g, AttnPlan* plan, size_t offs[14]) {
     if (!d) return 0;
     if (geom_derive(&d->geom, g) != LSA_OK) return 0;
     if (attn_plan(*g, &d->kv, d->Hq, d->k, 0, plan) != LSA_OK) return 0;
@@ -74,6 +76,8 @@ size_t layout(const lsa_ctx_desc* d, GeomDev* g, AttnPlan* plan, size_t offs[12]
     offs[9] = c.take(plan->part_o_bytes + plan->part_ml_bytes);  // attention partials
     offs[10] = c.take((size_t)nh * 4);                  // page table 0
     offs[11] = c.take((size_t)nh * 4);                  // page table 1
+    offs[12] = c.take((size_t)nh * 4);                  // pages of the selected chunks
+    offs[13] = c.take((size_t)nh * 4);                  // their scales
     return c.off;
 }
 
@@ -106,7 +110,7 @@ extern "C" {
 size_t lsa_ctx_ws_bytes(const lsa_ctx_desc* desc) {
     GeomDev g;
     AttnPlan p;
-    size_t offs[12];
+    size_t offs[14];
     return layout(desc, &g, &p, offs);
 }
 
@@ -115,7 +119,7 @@ lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc) {
     *ctx = nullptr;
     GeomDev g;
     AttnPlan plan;
-    size_t offs[12];
+    size_t offs[14];
     lsa_status st = geom_derive(&desc->geom, &g);
     if (st != LSA_OK) return st;
     if (desc->d != 64 && desc->d != 128) return LSA_ERR_UNSUPPORTED;
@@ -159,6 +163,8 @@ lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc) {
     x->attn_ws = base + offs[9];
     x->pt[0] = (int32_t*)(base + offs[10]);
     x->pt[1] = (int32_t*)(base + offs[11]);
+    x->sel_slot = (int32_t*)(base + offs[12]);
+    x->sel_scale = (float*)(base + offs[13]);
     const size_t nhb = (size_t)(x->nh > 0 ? x->nh : 1) * 4;
     bool ok = true;
     for (int i = 0; i < 2 && ok; ++i) {
@@ -227,6 +233,10 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
     const int cur = x->cur, nxt = cur ^ 1;
 
     if (hipStreamWaitEvent(ms, x->ev_fetch[cur], 0) != hipSuccess) return LSA_ERR_HIP;
+    const bool band = band_supported(d.idx_dt, d.q_dt, d.H, d.d);
+    if (band && launch_resolve_sel(g, x->sel[cur], x->cnt[cur], x->pt[cur], d.ikey_scale,
+                                   x->sel_slot, x->sel_scale, ms) != hipSuccess)
+        return LSA_ERR_HIP;
     if (in->next) {
         lsa_status st = score_select(x, in->next, nxt, ms);
         if (st != LSA_OK) return st;
@@ -241,13 +251,13 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
         int32_t* tc = out->topk_cnt ? out->topk_cnt + (size_t)j * g.B : x->tcnt_tmp;
         const uint8_t* qr = (const uint8_t*)in->q_refine + j * qr_step;
         const float* wr = in->w_refine + (size_t)j * g.B * d.H;
-        if (groups > 0 && band_supported(d.idx_dt, d.q_dt, d.H, d.d)) {
+        if (groups > 0 && band) {
             const bool clean = x->band_clean;
             x->band_clean = false;  // until the chain is queued whole
             if (launch_refine_band(g, x->sel[cur], x->cnt[cur], lsa_pool_slots(d.pool),
                                    d.kv.page_bytes, d.kv.ikey_off, x->pt[cur], d.idx_dt,
-                                   d.ikey_scale, qr, wr, d.H, d.d, d.k, tk, tc, x->scores, clean,
-                                   ms) != hipSuccess)
+                                   d.ikey_scale, x->sel_slot, x->sel_scale, qr, wr, d.H, d.d, d.k,
+                                   tk, tc, x->scores, clean, ms) != hipSuccess)
                 return LSA_ERR_HIP;
             x->band_clean = true;
         } else {
