@@ -113,10 +113,17 @@ __device__ __forceinline__ void kth_bin(const uint32_t* hist, int k, int* wsum, 
     lds_barrier();
 }
 
-// Copies n words of a histogram into LDS.
-__device__ __forceinline__ void load_hist(const uint32_t* gh, uint32_t* lds, int n) {
-#pragma unroll 8
-    for (int i = threadIdx.x; i < n; i += blockDim.x) lds[i] = gh[i];
+// Copies N words of a histogram into LDS (16 bytes per load, every load of
+// the block's NT threads in flight at once; both pointers 16-byte aligned).
+template <int N, int NT>
+__device__ __forceinline__ void load_hist(const uint32_t* gh, uint32_t* lds) {
+    constexpr int PER = N / 4 / NT;
+    static_assert(PER * 4 * NT == N, "histogram words must split evenly");
+    uint4 v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v[j] = ((const uint4*)gh)[threadIdx.x + NT * j];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) ((uint4*)lds)[threadIdx.x + NT * j] = v[j];
     lds_barrier();
 }
 
@@ -382,7 +389,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
     const uint2* __restrict__ lu, int k, uint32_t* __restrict__ hist, int4* __restrict__ cinfo,
     int32_t* __restrict__ plist, int32_t* __restrict__ pcnt, int32_t* __restrict__ topk,
     int32_t* __restrict__ tcnt) {
-    __shared__ uint32_t hf[2 * kFine];
+    __shared__ __attribute__((aligned(16))) uint32_t hf[2 * kFine];
     __shared__ int wsum[kWaves], s_out[4], s_np[kWaves];
     const int r = blockIdx.y, X = gridDim.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nc = cnt[r], n = nc * 64;
@@ -403,7 +410,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
         f[u] = c < c1 ? lu[(off + c) * 64 + lane] : make_uint2(0u, 0u);
     }
     uint32_t* gh = hist + (int64_t)r * kHist;
-    load_hist(gh, hf, 2 * kCoarse);
+    load_hist<2 * kCoarse, 64 * kWaves>(gh, hf);
     kth_bin<kCoarse, kWaves>(hf, k, wsum, &s_out[0]);
     kth_bin<kCoarse, kWaves>(hf + kCoarse, k, wsum, &s_out[2]);
     const uint32_t cL = (uint32_t)s_out[0], cU = (uint32_t)s_out[2];
@@ -468,6 +475,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     const int32_t* __restrict__ pcnt, int k,
     const uint8_t* __restrict__ pages, int64_t page_bytes, int64_t ikey_off,
     const int32_t* __restrict__ page_table, const float* __restrict__ ikey_scale,
+    const int32_t* __restrict__ sel_slot, const float* __restrict__ sel_scale,
     const uint16_t* __restrict__ q, const float* __restrict__ w, int32_t* __restrict__ bl,
     uint32_t* __restrict__ bk, int32_t* __restrict__ ul, int32_t* __restrict__ scnt) {
     constexpr int TPT = H < 64 ? H : 64;  // lanes per token
@@ -478,7 +486,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     __shared__ __attribute__((aligned(16))) float kf[kWaves][TPW][D];
     __shared__ float rel[kWaves][TPW][H];
     __shared__ float wf[H];
-    __shared__ uint32_t hf[2 * kFine];
+    __shared__ __attribute__((aligned(16))) uint32_t hf[2 * kFine];
     __shared__ int wsum[kWaves], s_out[4];
     __shared__ int64_t pgb[kPgCap];  // page (slot) of chunk c0 + t
     __shared__ float psc[kPgCap];    // its index-key scale
@@ -491,12 +499,25 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     block_chunks(nc, X, blockIdx.x, c0, c1);
     const int nch = c1 - c0;
     const bool pg_lds = nch <= kPgCap;
-    // independent loads first: page and scale of this block's chunks, the
-    // weights and the query rows (for the re-score)
+    // The fine histograms, the coarse bins, the block's pre-band count and
+    // the first pre-band entry of each thread load first (read with the
+    // count unknown; within the block's list space); the loads that only
+    // the re-score needs go out behind them.
+    const int64_t seg = (off + c0) * 64;
+    const int4 ci = cinfo[r];
+    const int npre = pcnt[(int64_t)r * X + blockIdx.x];
+    const int p_first = tid < nch * 64 ? plist[seg + tid] : 0;
+    load_hist<2 * kFine, 64 * kWaves>(hist + (int64_t)r * kHist + 2 * kCoarse, hf);
+    // page and scale of this block's chunks, the weights and the query rows
     if (pg_lds && tid < nch) {
-        const int c = sel[off + c0 + tid];
-        pgb[tid] = page_table ? (int64_t)page_table[off + c] : off + c;
-        psc[tid] = KDT == LSA_FP8_E4M3FN ? ikey_scale[off + c] : 1.0f;
+        if (sel_slot) {
+            pgb[tid] = (int64_t)sel_slot[off + c0 + tid];
+            psc[tid] = sel_scale[off + c0 + tid];
+        } else {
+            const int c = sel[off + c0 + tid];
+            pgb[tid] = page_table ? (int64_t)page_table[off + c] : off + c;
+            psc[tid] = KDT == LSA_FP8_E4M3FN ? ikey_scale[off + c] : 1.0f;
+        }
     }
     for (int e = tid; e < H; e += blockDim.x) wf[e] = w[(int64_t)r * H + e];
     const int lt2 = lane % TPT, ts = lane / TPT;
@@ -515,21 +536,17 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     }
     // tau: lowest key of the fine bin holding the k-th largest L; edge: first
     // key above the fine bin holding the k-th largest U
-    const int4 ci = cinfo[r];
-    load_hist(hist + (int64_t)r * kHist + 2 * kCoarse, hf, 2 * kFine);
     kth_bin<kFine, kWaves>(hf, k - ci.y, wsum, &s_out[0]);
     kth_bin<kFine, kWaves>(hf + kFine, k - ci.w, wsum, &s_out[2]);
     const uint32_t tau = ((uint32_t)ci.x << 22) | ((uint32_t)s_out[0] << 11);
     const uint64_t edge = ((uint64_t)(uint32_t)ci.z << 22) + ((uint64_t)(s_out[2] + 1) << 11);
-    const int64_t seg = (off + c0) * 64;
-    const int npre = pcnt[(int64_t)r * X + blockIdx.x];
     const uint2* lur = lu + off * 64;
     // ordered lists over the pre-band entries, one per thread per round
     int nb = 0, nu = 0;
     for (int b0 = 0; b0 < npre; b0 += 64 * kWaves) {  // uniform
         const int idx = b0 + tid;
         const bool have = idx < npre;
-        const int p = have ? plist[seg + idx] : 0;
+        const int p = have ? (b0 == 0 ? p_first : plist[seg + idx]) : 0;
         const uint2 cur = have ? lur[p] : make_uint2(0u, 0u);
         const bool band = have && cur.y >= tau;
         const bool sure = band && (uint64_t)cur.x >= edge;
@@ -580,9 +597,14 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
                 pg = pgb[(p >> 6) - c0];
                 scale = psc[(p >> 6) - c0];
             } else {
-                const int c = sel[off + (p >> 6)];
-                pg = page_table ? (int64_t)page_table[off + c] : off + c;
-                if constexpr (KDT == LSA_FP8_E4M3FN) scale = ikey_scale[off + c];
+                if (sel_slot) {
+                    pg = (int64_t)sel_slot[off + (p >> 6)];
+                    scale = sel_scale[off + (p >> 6)];
+                } else {
+                    const int c = sel[off + (p >> 6)];
+                    pg = page_table ? (int64_t)page_table[off + c] : off + c;
+                    if constexpr (KDT == LSA_FP8_E4M3FN) scale = ikey_scale[off + c];
+                }
             }
             const uint8_t* row = pages + pg * page_bytes + ikey_off + (int64_t)(p & 63) * ROWB;
             for (int e4 = lt2; e4 < D / 4; e4 += TPT) {
@@ -955,7 +977,7 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
     if (idx_dt == KDT && d == D && Hh == HH) {                                                    \
         hipLaunchKernelGGL((k_band_list<KDT, D, HH>), dim3(X2, g.B), dim3(64 * kWaves), 0, s, g,   \
                            sel, cnt, lu, hist, cinfo, plist, pcnt, k, pg, page_bytes, ikey_off,   \
-                           page_table, ikey_scale, qq, w, bl, bk, ul, scnt);                      \
+                           page_table, ikey_scale, sel_slot, sel_scale, qq, w, bl, bk, ul, scnt); \
         e = hipGetLastError();                                                                    \
     }
     LSA_K3(LSA_BF16, 128, 16) LSA_K3(LSA_BF16, 128, 32) LSA_K3(LSA_BF16, 128, 64)
