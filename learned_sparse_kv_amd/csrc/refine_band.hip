@@ -683,16 +683,18 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
     __shared__ uint32_t s_prefix;
     __shared__ int s_remaining, s_eq, s_u;
     const int r = blockIdx.x, tid = threadIdx.x;
+    const int64_t off = g.chunk_off[r];
+    // the count and the K3 block counts load at once
     const int nc = cnt[r];
+    const int v_scnt = tid < X ? scnt[(int64_t)r * X + tid] : 0;
     // the request's histograms were last read by the previous kernel: clear
     // them for the next launch
     for (int i = tid; i < kHist; i += kT) bhist[(int64_t)r * kHist + i] = 0;
     if (nc * 64 <= k) return;  // k_band_fine already wrote the result
-    const int64_t off = g.chunk_off[r];
     const int C = (nc + X - 1) / X;  // chunks per K3 block
     int tot;
     {
-        const int v = tid < X ? scnt[(int64_t)r * X + tid] : 0;
+        const int v = v_scnt;
         const int ex = block_scan<kTW>(v, wsum, tot);
         if (tid < X) boff[tid] = ex;
         if (tid == 0) boff[X] = tot;
