@@ -390,7 +390,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
     int32_t* __restrict__ plist, int32_t* __restrict__ pcnt, int32_t* __restrict__ topk,
     int32_t* __restrict__ tcnt) {
     __shared__ __attribute__((aligned(16))) uint32_t hf[2 * kFine];
-    __shared__ int wsum[kWaves], s_out[4], s_np[kWaves];
+    __shared__ int wsum[kWaves], s_out[4], s_np[kPre][kWaves];
     const int r = blockIdx.y, X = gridDim.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nc = cnt[r], n = nc * 64;
     const int64_t off = g.chunk_off[r];
@@ -422,29 +422,35 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
     const uint64_t lt = (1ull << lane) - 1;
     int np = 0;
     for (int cb0 = c0; cb0 < c1; cb0 += kWaves * kPre) {  // uniform
+        // every round's ballot first, then one barrier for all their counts;
+        // the list stays in token order (round-major, then wave)
+        uint64_t mk[kPre];
 #pragma unroll
         for (int u = 0; u < kPre; ++u) {
-            const int cb = cb0 + kWaves * u;
-            if (cb >= c1) break;  // uniform
-            const int c = cb + wv;
+            const int c = cb0 + kWaves * u + wv;
             const bool have = c < c1;
             const uint2 cur = f[u];
             if (have) {
                 if ((cur.x >> 22) == cL) atomicAdd(&hf[(cur.x >> 11) & (kFine - 1)], 1u);
                 if ((cur.y >> 22) == cU) atomicAdd(&hf[kFine + ((cur.y >> 11) & (kFine - 1))], 1u);
             }
-            const bool pre = have && cur.y >= tau_c;
-            const uint64_t m = __ballot(pre);
-            if (lane == 0) s_np[wv] = __popcll(m);
-            lds_barrier();
-            int pb = np;
-            for (int w2 = 0; w2 < kWaves; ++w2) {
-                pb += w2 < wv ? s_np[w2] : 0;
-                np += s_np[w2];
-            }
-            lds_barrier();
-            if (pre) plist[seg + pb + __popcll(m & lt)] = c * 64 + lane;
+            mk[u] = __ballot(have && cur.y >= tau_c);
+            if (lane == 0) s_np[u][wv] = __popcll(mk[u]);
         }
+        lds_barrier();
+#pragma unroll
+        for (int u = 0; u < kPre; ++u) {
+            int pb = np;
+#pragma unroll
+            for (int w2 = 0; w2 < kWaves; ++w2) {
+                const int x = s_np[u][w2];
+                pb += w2 < wv ? x : 0;
+                np += x;
+            }
+            if ((mk[u] >> lane) & 1ull)
+                plist[seg + pb + __popcll(mk[u] & lt)] = (cb0 + kWaves * u + wv) * 64 + lane;
+        }
+        lds_barrier();  // s_np is rewritten by the next rounds
         // next kPre rounds
 #pragma unroll
         for (int u = 0; u < kPre; ++u) {
