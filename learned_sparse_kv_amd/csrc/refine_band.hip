@@ -731,10 +731,28 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
     int32_t* out = topk + (int64_t)r * k;
     if (in_lds) {
         if (tid == 0) s_u = 0;
-        for (int j = tid; j < m; j += kT) {
-            const int64_t e = gidx(j);
-            lkey[j] = bk[e];
-            lpos[j] = bl[e];
+        // every entry's loads in flight before any is stored (kGB per thread)
+        constexpr int kGB = 4;
+        for (int j0 = 0; j0 < m; j0 += kT * kGB) {
+            uint32_t kk[kGB];
+            int32_t pp[kGB];
+#pragma unroll
+            for (int u = 0; u < kGB; ++u) {
+                const int j = j0 + tid + kT * u;
+                if (j < m) {
+                    const int64_t e = gidx(j);
+                    kk[u] = bk[e];
+                    pp[u] = bl[e];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kGB; ++u) {
+                const int j = j0 + tid + kT * u;
+                if (j < m) {
+                    lkey[j] = kk[u];
+                    lpos[j] = pp[u];
+                }
+            }
         }
         lds_barrier();
         // The certain entries (key 0xffffffff) are all in; the uncertain ones
@@ -764,15 +782,22 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
                 lds_barrier();
             }
             const int u2 = (u + 1) & ~1;
-            for (int t = tid; t < u; t += kT) {
-                const uint64_t vt = uval[t];
+            // kRP neighbouring lanes rank one entry, each over every kRP-th pair
+            constexpr int kRP = 4;
+            for (int t0 = 0; t0 < u; t0 += kT / kRP) {  // uniform trip count
+                const int t = t0 + tid / kRP, q = tid % kRP;
                 int rank = 0;
-#pragma unroll 8
-                for (int s2 = 0; s2 < u2; s2 += 2) {
-                    const ulonglong2 v2 = *(const ulonglong2*)&uval[s2];
-                    rank += (v2.x > vt) + (v2.y > vt);
+                if (t < u) {
+                    const uint64_t vt = uval[t];
+#pragma unroll 4
+                    for (int s2 = 2 * q; s2 < u2; s2 += 2 * kRP) {
+                        const ulonglong2 v2 = *(const ulonglong2*)&uval[s2];
+                        rank += (v2.x > vt) + (v2.y > vt);
+                    }
                 }
-                lkey[uj[t]] = rank < need ? 0xffffffffu : 0u;
+                rank += __shfl_xor(rank, 1);
+                rank += __shfl_xor(rank, 2);
+                if (t < u && q == 0) lkey[uj[t]] = rank < need ? 0xffffffffu : 0u;
             }
             lds_barrier();
             // emit the taken entries in list (token) order: thread t takes a
