@@ -514,18 +514,23 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     const int npre = pcnt[(int64_t)r * X + blockIdx.x];
     const int p_first = tid < nch * 64 ? plist[seg + tid] : 0;
     load_hist<2 * kFine, 64 * kWaves>(hist + (int64_t)r * kHist + 2 * kCoarse, hf);
-    // page and scale of this block's chunks, the weights and the query rows
+    // page and scale of this block's chunks, the weights and the query rows:
+    // held in registers until the lists are done, so that no barrier before
+    // then waits for them (the pages are two dependent loads without sel_slot)
+    int64_t pg_v = 0;
+    float sc_v = 1.0f, w_v = 0.0f;
     if (pg_lds && tid < nch) {
         if (sel_slot) {
-            pgb[tid] = (int64_t)sel_slot[off + c0 + tid];
-            psc[tid] = sel_scale[off + c0 + tid];
+            pg_v = (int64_t)sel_slot[off + c0 + tid];
+            sc_v = sel_scale[off + c0 + tid];
         } else {
             const int c = sel[off + c0 + tid];
-            pgb[tid] = page_table ? (int64_t)page_table[off + c] : off + c;
-            psc[tid] = KDT == LSA_FP8_E4M3FN ? ikey_scale[off + c] : 1.0f;
+            pg_v = page_table ? (int64_t)page_table[off + c] : off + c;
+            if constexpr (KDT == LSA_FP8_E4M3FN) sc_v = ikey_scale[off + c];
         }
     }
-    for (int e = tid; e < H; e += blockDim.x) wf[e] = w[(int64_t)r * H + e];
+    static_assert(H <= 64 * kWaves, "one weight per thread");
+    if (tid < H) w_v = w[(int64_t)r * H + tid];
     const int lt2 = lane % TPT, ts = lane / TPT;
     uint32_t qp[HPT][D / 2];
 #pragma unroll
@@ -576,6 +581,11 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     }
     if (tid == 0) scnt[(int64_t)r * X + blockIdx.x] = nb;
     if (nu == 0) return;  // uniform
+    if (pg_lds && tid < nch) {
+        pgb[tid] = pg_v;
+        psc[tid] = sc_v;
+    }
+    if (tid < H) wf[tid] = w_v;
     // canonical scores of this block's uncertain entries
     // the lists in global memory written above are read by other threads
     // below (past the LDS copies): a full block barrier
