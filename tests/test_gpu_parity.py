@@ -192,6 +192,32 @@ def test_split_count_invariance_and_determinism(kind):
         assert rel_err(x, outs[0]).max() <= tol
 
 
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_attention_output_at_unaligned_address(kind):
+    """The output pointer carries no alignment promise: the same launch with
+    the output one element past a 16-byte boundary gives the same values
+    (the merge then stores element by element)."""
+    inp, dev, o = setup(kind)
+    cfg = inp.cfg
+    lsa = _lsa()
+    z, sel, cnt = dev.score_select()
+    topk, tcnt = dev.refine_topk(sel, cnt, 0, cfg.topk)
+    ref, _ = dev.attend(topk, tcnt, 0, cfg.topk)
+    odt = torch.float32 if kind == "f32" else torch.int16
+    n = dev.B * cfg.Hq * cfg.Dv
+    buf = torch.zeros(n + 8, dtype=odt, device="cuda")
+    out = buf[1:1 + n].view(dev.B, cfg.Hq, cfg.Dv)
+    assert out.data_ptr() % 16 != 0
+    lse = torch.empty((dev.B, cfg.Hq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lsa.lsa_attn_ws_bytes(dev.geom, dev.kv, cfg.Hq, cfg.topk, 0), dtype=torch.uint8,
+                     device="cuda")
+    lsa.lsa_sparse_decode_attn(dev.geom, dev.q_attn[0], cfg.Hq, dev.kv, dev.pages, None, dev.recent, topk,
+                               tcnt, cfg.topk, cfg.sm_scale, out, lse, 0, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), ref.cpu())
+    assert torch.count_nonzero(buf[:1]) == 0 and torch.count_nonzero(buf[1 + n:]) == 0
+
+
 def test_topk_k1_and_k_exceeding_candidates():
     inp, dev, o = setup("bf16")
     cfg = inp.cfg
