@@ -335,8 +335,8 @@ lsa_status lsa_topk_refine(const lsa_geom* g, const int32_t* sel_ids, const int3
     hipStream_t s = (hipStream_t)stream;
     if (n > 0 && band_supported(idx_dt, q_dt, H, d)) {
         LSA_HIP(launch_refine_band(gd, sel_ids, sel_cnt, pages, page_bytes, ikey_off, page_table,
-                                   idx_dt, ikey_scale, nullptr, nullptr, q, w, H, d, k, topk_idx,
-                                   topk_cnt, ws, false, s));
+                                   idx_dt, ikey_scale, nullptr, nullptr, nullptr, q, w, H, d, k,
+                                   topk_idx, topk_cnt, ws, false, s));
         return LSA_OK;
     }
     float* scores = (float*)ws;

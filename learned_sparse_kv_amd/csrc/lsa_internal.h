@@ -110,9 +110,14 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
                               const void* pages, int64_t page_bytes, int64_t ikey_off,
                               const int32_t* page_table, lsa_dtype idx_dt,
                               const float* ikey_scale, const int32_t* sel_slot,
-                              const float* sel_scale, const void* q, const float* w, int H,
-                              int d, int k, int32_t* topk, int32_t* tcnt, void* ws, bool ws_clean,
-                              hipStream_t s);
+                              const float* sel_scale, const float* kn2, const void* q,
+                              const float* w, int H, int d, int k, int32_t* topk, int32_t* tcnt,
+                              void* ws, bool ws_clean, hipStream_t s);
+// |key|^2 of every token of the selected chunks (selection order, 64 per
+// chunk) for launch_refine_band's kn2 (nullptr: formed there per step).
+hipError_t launch_key_norm2(const GeomDev& g, const int32_t* cnt, const int32_t* sel_slot,
+                            const void* pages, int64_t page_bytes, int64_t ikey_off,
+                            lsa_dtype idx_dt, int d, float* kn2, hipStream_t s);
 // sel_slot / sel_scale: pages and scales of the selected chunks in selection
 // order (-1 past the count), for launch_refine_band (nullptr: looked up there).
 hipError_t launch_resolve_sel(const GeomDev& g, const int32_t* sel, const int32_t* cnt,

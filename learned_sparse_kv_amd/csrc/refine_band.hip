@@ -139,8 +139,8 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
     const uint8_t* __restrict__ pages, int64_t page_bytes, int64_t ikey_off,
     const int32_t* __restrict__ page_table, const float* __restrict__ ikey_scale,
     const int32_t* __restrict__ sel_slot, const float* __restrict__ sel_scale,
-    const uint16_t* __restrict__ q, const float* __restrict__ w, uint2* __restrict__ lu,
-    uint32_t* __restrict__ hist) {
+    const float* __restrict__ kn2g, const uint16_t* __restrict__ q, const float* __restrict__ w,
+    uint2* __restrict__ lu, uint32_t* __restrict__ hist) {
     constexpr int EB = KDT == LSA_BF16 ? 2 : 1;
     constexpr int ROWB = D * EB;
     constexpr int KS = D / 32;   // MFMA k-steps
@@ -242,6 +242,8 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
         float* pr = red[wv];
         for (int j = 0; j < nj; ++j) {
             const int i = i0 + j * stride;
+            // |key|^2 of the lane's token, formed once per window when given
+            const float kn2_pre = kn2g ? kn2g[(off + i) * 64 + lane] : 0.0f;
             uint4 ka[4][KS];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
@@ -269,19 +271,22 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
                 if (((j + 1) & 63) == 0) load_idx(j + 1, nj);
                 fetch(j + 1, raw);
             }
-            // |key|^2 on the matrix cores: the diagonal of the 16x16 Gram block
-            // of tokens tb*16..; lane (l16, lq) holds rows 4lq..4lq+3 of column l16
+            // |key|^2 on the matrix cores (unless given): the diagonal of the
+            // 16x16 Gram block of tokens tb*16..; lane (l16, lq) holds rows
+            // 4lq..4lq+3 of column l16
+            if (!kn2g) {  // uniform
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                f32x4_t gm = {0.f, 0.f, 0.f, 0.f};
+                for (int tb = 0; tb < 4; ++tb) {
+                    f32x4_t gm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, ka[tb][ks]),
-                        __builtin_bit_cast(bf16x8_t, ka[tb][ks]), gm, 0, 0, 0);
-                const int e = l16 & 3;
-                const float dv = e == 0 ? gm[0] : (e == 1 ? gm[1] : (e == 2 ? gm[2] : gm[3]));
-                if ((l16 >> 2) == lq) pr[(tb * 16 + l16) * kRedStride + 32] = dv;
+                    for (int ks = 0; ks < KS; ++ks)
+                        gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, ka[tb][ks]),
+                            __builtin_bit_cast(bf16x8_t, ka[tb][ks]), gm, 0, 0, 0);
+                    const int e = l16 & 3;
+                    const float dv = e == 0 ? gm[0] : (e == 1 ? gm[1] : (e == 2 ? gm[2] : gm[3]));
+                    if ((l16 >> 2) == lq) pr[(tb * 16 + l16) * kRedStride + 32] = dv;
+                }
             }
             // partial head sums per lane (heads hb*16 + l16), then through LDS
             // to one lane per token: red[token][l16], fixed summation order
@@ -322,7 +327,7 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
                 sI += pr[lane * kRedStride + j];
                 sW += pr[lane * kRedStride + 16 + j];
             }
-            const float kn2 = pr[lane * kRedStride + 32];
+            const float kn2 = kn2g ? kn2_pre : pr[lane * kRedStride + 32];
             const float kn = sqrtf(kn2 * (1.0f + gam(D + 8))) * (1.0f + 4 * kU2);
             const float ek = gam(D) * 2.0f * kn * wq;  // sum_h |w_h| eps_h
             float E = ek + 2.0f * gam(H + 24) * (sW + ek);
@@ -365,6 +370,49 @@ __global__ __launch_bounds__(256) void k_resolve_sel(GeomDev g, const int32_t* _
     }
     sel_slot[off + i] = slot;
     sel_scale[off + i] = sc;
+}
+
+// |key|^2 of every token of the selected chunks, in selection order:
+// kn2[(off + i) * 64 + t] for i below the request's count.  Products of the
+// (exactly converted) key values are exact in fp32 and the sum has error
+// within gamma(D) of the exact one in any order, which is what the refine
+// pass's bound allows for its own |key|^2.  One wave per chunk, lane = token.
+template <int KDT, int D>
+__global__ __launch_bounds__(256) void k_key_norm2(GeomDev g, const int32_t* __restrict__ cnt,
+                                                   const int32_t* __restrict__ sel_slot,
+                                                   const uint8_t* __restrict__ pages,
+                                                   int64_t page_bytes, int64_t ikey_off,
+                                                   float* __restrict__ kn2) {
+    constexpr int ROWB = D * (KDT == LSA_BF16 ? 2 : 1);
+    const int r = blockIdx.y, lane = threadIdx.x & 63;
+    const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= cnt[r]) return;
+    const int64_t off = g.chunk_off[r];
+    const uint8_t* row = pages + (int64_t)sel_slot[off + i] * page_bytes + ikey_off + (int64_t)lane * ROWB;
+    uint4 v[ROWB / 16];
+#pragma unroll
+    for (int n = 0; n < ROWB / 16; ++n) v[n] = *(const uint4*)(row + 16 * n);
+    float s = 0.0f;
+#pragma unroll
+    for (int n = 0; n < ROWB / 16; ++n) {
+        const uint32_t wd[4] = {v[n].x, v[n].y, v[n].z, v[n].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (KDT == LSA_BF16) {
+                const float a = __uint_as_float(wd[e] << 16), b = __uint_as_float(wd[e] & 0xffff0000u);
+                s = __builtin_fmaf(a, a, s);
+                s = __builtin_fmaf(b, b, s);
+            } else {
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[e], false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[e], true);
+                s = __builtin_fmaf(lo[0], lo[0], s);
+                s = __builtin_fmaf(lo[1], lo[1], s);
+                s = __builtin_fmaf(hi[0], hi[0], s);
+                s = __builtin_fmaf(hi[1], hi[1], s);
+            }
+        }
+    }
+    kn2[(off + i) * 64 + lane] = s;
 }
 
 // Chunks [c0, c1) of a request that block x of X takes in K2 and K3.
@@ -963,9 +1011,9 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
                               const void* pages, int64_t page_bytes, int64_t ikey_off,
                               const int32_t* page_table, lsa_dtype idx_dt,
                               const float* ikey_scale, const int32_t* sel_slot,
-                              const float* sel_scale, const void* q, const float* w, int H,
-                              int d, int k, int32_t* topk, int32_t* tcnt, void* ws, bool ws_clean,
-                              hipStream_t s) {
+                              const float* sel_scale, const float* kn2, const void* q,
+                              const float* w, int H, int d, int k, int32_t* topk, int32_t* tcnt,
+                              void* ws, bool ws_clean, hipStream_t s) {
     const size_t nc = (size_t)g.chunk_off[g.B] * 64 + 64;
     const int X1 = k1_blocks(g), X2 = k23_blocks(g);
     hipError_t e;
@@ -997,7 +1045,7 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
     if (idx_dt == KDT && d == D && Hh == HH) {                                                    \
         hipLaunchKernelGGL((k_refine_mfma<KDT, D, HH>), dim3(X1, g.B), dim3(64 * kWaves), 0, s, g, \
                            sel, cnt, pg, page_bytes, ikey_off, page_table, ikey_scale, sel_slot,  \
-                           sel_scale, qq, w, lu, hist);                                           \
+                           sel_scale, kn2, qq, w, lu, hist);                                      \
         e = hipGetLastError();                                                                    \
     }
     LSA_K1(LSA_BF16, 128, 16) LSA_K1(LSA_BF16, 128, 32) LSA_K1(LSA_BF16, 128, 64)
@@ -1046,5 +1094,25 @@ hipError_t launch_resolve_sel(const GeomDev& g, const int32_t* sel, const int32_
     if (mh == 0) return hipSuccess;
     hipLaunchKernelGGL(k_resolve_sel, dim3((mh + 255) / 256, g.B), dim3(256), 0, s, g, sel, cnt,
                        page_table, ikey_scale, sel_slot, sel_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_key_norm2(const GeomDev& g, const int32_t* cnt, const int32_t* sel_slot,
+                            const void* pages, int64_t page_bytes, int64_t ikey_off,
+                            lsa_dtype idx_dt, int d, float* kn2, hipStream_t s) {
+    const int mh = max_hist(g);
+    if (mh == 0) return hipSuccess;
+    const dim3 grid((mh + 3) / 4, g.B);
+    const uint8_t* pg = (const uint8_t*)pages;
+    if (idx_dt == LSA_BF16 && d == 128)
+        hipLaunchKernelGGL((k_key_norm2<LSA_BF16, 128>), grid, dim3(256), 0, s, g, cnt, sel_slot, pg, page_bytes, ikey_off, kn2);
+    else if (idx_dt == LSA_BF16 && d == 64)
+        hipLaunchKernelGGL((k_key_norm2<LSA_BF16, 64>), grid, dim3(256), 0, s, g, cnt, sel_slot, pg, page_bytes, ikey_off, kn2);
+    else if (idx_dt == LSA_FP8_E4M3FN && d == 128)
+        hipLaunchKernelGGL((k_key_norm2<LSA_FP8_E4M3FN, 128>), grid, dim3(256), 0, s, g, cnt, sel_slot, pg, page_bytes, ikey_off, kn2);
+    else if (idx_dt == LSA_FP8_E4M3FN && d == 64)
+        hipLaunchKernelGGL((k_key_norm2<LSA_FP8_E4M3FN, 64>), grid, dim3(256), 0, s, g, cnt, sel_slot, pg, page_bytes, ikey_off, kn2);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -34,6 +34,7 @@ struct lsa_ctx {
     int32_t* pt[2] = {nullptr, nullptr};
     int32_t* sel_slot = nullptr;  // pages of the running window's selected chunks
     float* sel_scale = nullptr;   // and their index-key scales
+    float* kn2 = nullptr;         // |key|^2 of their tokens
     int32_t* h_sel[2] = {nullptr, nullptr};
     int32_t* h_cnt[2] = {nullptr, nullptr};
     hipEvent_t ev_sel = nullptr, ev_win[2] = {nullptr, nullptr}, ev_fetch[2] = {nullptr, nullptr};
@@ -56,7 +57,7 @@ struct Carve {
 };
 
 // Workspace layout; returns total bytes (0 on invalid description).
-size_t layout(const lsa_ctx_desc* d, GeomDev* g, AttnPlan* plan, size_t offs[14]) {
+size_t layout(const lsa_ctx_desc* d, GeomDev* g, AttnPlan* plan, size_t offs[15]) {
     if (!d) return 0;
     if (geom_derive(&d->geom, g) != LSA_OK) return 0;
     if (attn_plan(*g, &d->kv, d->Hq, d->k, 0, plan) != LSA_OK) return 0;
@@ -78,6 +79,7 @@ size_t layout(const lsa_ctx_desc* d, GeomDev* g, AttnPlan* plan, size_t offs[14]
     offs[11] = c.take((size_t)nh * 4);                  // page table 1
     offs[12] = c.take((size_t)nh * 4);                  // pages of the selected chunks
     offs[13] = c.take((size_t)nh * 4);                  // their scales
+    offs[14] = c.take((size_t)nh * LSA_CHUNK * 4);      // |key|^2 of their tokens
     return c.off;
 }
 
@@ -110,7 +112,7 @@ extern "C" {
 size_t lsa_ctx_ws_bytes(const lsa_ctx_desc* desc) {
     GeomDev g;
     AttnPlan p;
-    size_t offs[14];
+    size_t offs[15];
     return layout(desc, &g, &p, offs);
 }
 
@@ -119,7 +121,7 @@ lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc) {
     *ctx = nullptr;
     GeomDev g;
     AttnPlan plan;
-    size_t offs[14];
+    size_t offs[15];
     lsa_status st = geom_derive(&desc->geom, &g);
     if (st != LSA_OK) return st;
     if (desc->d != 64 && desc->d != 128) return LSA_ERR_UNSUPPORTED;
@@ -165,6 +167,7 @@ lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc) {
     x->pt[1] = (int32_t*)(base + offs[11]);
     x->sel_slot = (int32_t*)(base + offs[12]);
     x->sel_scale = (float*)(base + offs[13]);
+    x->kn2 = (float*)(base + offs[14]);
     const size_t nhb = (size_t)(x->nh > 0 ? x->nh : 1) * 4;
     bool ok = true;
     for (int i = 0; i < 2 && ok; ++i) {
@@ -234,8 +237,11 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
 
     if (hipStreamWaitEvent(ms, x->ev_fetch[cur], 0) != hipSuccess) return LSA_ERR_HIP;
     const bool band = band_supported(d.idx_dt, d.q_dt, d.H, d.d);
-    if (band && launch_resolve_sel(g, x->sel[cur], x->cnt[cur], x->pt[cur], d.ikey_scale,
-                                   x->sel_slot, x->sel_scale, ms) != hipSuccess)
+    if (band && (launch_resolve_sel(g, x->sel[cur], x->cnt[cur], x->pt[cur], d.ikey_scale,
+                                    x->sel_slot, x->sel_scale, ms) != hipSuccess ||
+                 launch_key_norm2(g, x->cnt[cur], x->sel_slot, lsa_pool_slots(d.pool),
+                                  d.kv.page_bytes, d.kv.ikey_off, d.idx_dt, d.d, x->kn2,
+                                  ms) != hipSuccess))
         return LSA_ERR_HIP;
     if (in->next) {
         lsa_status st = score_select(x, in->next, nxt, ms);
@@ -256,8 +262,8 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
             x->band_clean = false;  // until the chain is queued whole
             if (launch_refine_band(g, x->sel[cur], x->cnt[cur], lsa_pool_slots(d.pool),
                                    d.kv.page_bytes, d.kv.ikey_off, x->pt[cur], d.idx_dt,
-                                   d.ikey_scale, x->sel_slot, x->sel_scale, qr, wr, d.H, d.d, d.k,
-                                   tk, tc, x->scores, clean, ms) != hipSuccess)
+                                   d.ikey_scale, x->sel_slot, x->sel_scale, x->kn2, qr, wr, d.H,
+                                   d.d, d.k, tk, tc, x->scores, clean, ms) != hipSuccess)
                 return LSA_ERR_HIP;
             x->band_clean = true;
         } else {
