@@ -53,10 +53,14 @@ def kernel_work(name, cfg, inp, sel_cnt, k, tcnt_total, B):
         flops = n_cand * (2 * cfg.H * cfg.d + 2 * cfg.H + 1)
         return n_cand * per + int(sel_cnt.sum()) * 4 + n_cand * 4, flops
     if name == "k_refine_mfma":
-        # key rows of every candidate, its (L, U) pair out, chunk id + scale
+        # key rows of every candidate, its |key|^2 (formed once per window by
+        # the pipeline), its (L, U) pair out, and the chunk's page + scale
         nsel = int(sel_cnt.sum())
-        per = cfg.d * eb[cfg.idx_dtype] + 8
+        per = cfg.d * eb[cfg.idx_dtype] + 4 + 8
         return n_cand * per + nsel * (8 if cfg.idx_dtype == 2 else 4), n_cand * 2 * cfg.H * cfg.d
+    if name == "k_key_norm2":
+        # key rows of every candidate in, one fp32 norm per candidate out
+        return n_cand * (cfg.d * eb[cfg.idx_dtype] + 4), n_cand * 2 * cfg.d
     if name in ("k_attn_mla", "k_attn_f32"):
         toks = tcnt_total + nrec
         row = cfg.Dk * eb[cfg.kv_dtype]
@@ -82,6 +86,7 @@ def source_hash(names):
 
 KERNEL_SOURCE = {"k_refine": ["refine_topk.hip"], "k_topk": ["refine_topk.hip"],
                  "k_refine_mfma": ["refine_band.hip"], "k_band_fine": ["refine_band.hip"],
+                 "k_key_norm2": ["refine_band.hip"], "k_resolve_sel": ["refine_band.hip"],
                  "k_band_list": ["refine_band.hip"], "k_topk_band": ["refine_band.hip"],
                  "k_attn_mla": ["attn_decode.hip"], "k_attn_f32": ["attn_decode.hip"],
                  "k_attn_merge": ["attn_decode.hip"], "k_score": ["score_select.hip"],

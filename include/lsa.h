@@ -450,7 +450,8 @@ lsa_status lsa_step64(lsa_ctx* ctx, const lsa_window_in* in, lsa_window_out* out
  * k_score, k_select, k_refine, k_topk, k_refine_mfma, k_band_fine,
  * k_band_list, k_topk_band, k_attn_mla, k_attn_f32, k_attn_merge,
  * k_gather, k_stream_read, k_score_sig, k_select_ranked, k_chunk_ml, k_append_kv,
- * k_commit_chunk), the number of timed launches and their summed duration in
+ * k_commit_chunk, k_resolve_sel, k_key_norm2), the number of timed launches and
+ * their summed duration in
  * milliseconds since the last reset.  lsa_timing_only(name) restricts the
  * timing to that one kernel (NULL: all; a name of 64 or more characters is
  * LSA_ERR_INVALID_ARG), so that one kernel can be timed inside a run with

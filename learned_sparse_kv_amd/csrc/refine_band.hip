@@ -1092,8 +1092,10 @@ hipError_t launch_resolve_sel(const GeomDev& g, const int32_t* sel, const int32_
                               int32_t* sel_slot, float* sel_scale, hipStream_t s) {
     const int mh = max_hist(g);
     if (mh == 0) return hipSuccess;
+    timing_begin("k_resolve_sel", s);
     hipLaunchKernelGGL(k_resolve_sel, dim3((mh + 255) / 256, g.B), dim3(256), 0, s, g, sel, cnt,
                        page_table, ikey_scale, sel_slot, sel_scale);
+    timing_end("k_resolve_sel", s);
     return hipGetLastError();
 }
 
@@ -1104,15 +1106,21 @@ hipError_t launch_key_norm2(const GeomDev& g, const int32_t* cnt, const int32_t*
     if (mh == 0) return hipSuccess;
     const dim3 grid((mh + 3) / 4, g.B);
     const uint8_t* pg = (const uint8_t*)pages;
-    if (idx_dt == LSA_BF16 && d == 128)
-        hipLaunchKernelGGL((k_key_norm2<LSA_BF16, 128>), grid, dim3(256), 0, s, g, cnt, sel_slot, pg, page_bytes, ikey_off, kn2);
-    else if (idx_dt == LSA_BF16 && d == 64)
-        hipLaunchKernelGGL((k_key_norm2<LSA_BF16, 64>), grid, dim3(256), 0, s, g, cnt, sel_slot, pg, page_bytes, ikey_off, kn2);
-    else if (idx_dt == LSA_FP8_E4M3FN && d == 128)
-        hipLaunchKernelGGL((k_key_norm2<LSA_FP8_E4M3FN, 128>), grid, dim3(256), 0, s, g, cnt, sel_slot, pg, page_bytes, ikey_off, kn2);
-    else if (idx_dt == LSA_FP8_E4M3FN && d == 64)
-        hipLaunchKernelGGL((k_key_norm2<LSA_FP8_E4M3FN, 64>), grid, dim3(256), 0, s, g, cnt, sel_slot, pg, page_bytes, ikey_off, kn2);
-    else
+    if ((idx_dt != LSA_BF16 && idx_dt != LSA_FP8_E4M3FN) || (d != 64 && d != 128))
         return hipErrorInvalidValue;
+    timing_begin("k_key_norm2", s);
+    if (idx_dt == LSA_BF16 && d == 128)
+        hipLaunchKernelGGL((k_key_norm2<LSA_BF16, 128>), grid, dim3(256), 0, s, g, cnt, sel_slot, pg,
+                           page_bytes, ikey_off, kn2);
+    else if (idx_dt == LSA_BF16 && d == 64)
+        hipLaunchKernelGGL((k_key_norm2<LSA_BF16, 64>), grid, dim3(256), 0, s, g, cnt, sel_slot, pg,
+                           page_bytes, ikey_off, kn2);
+    else if (idx_dt == LSA_FP8_E4M3FN && d == 128)
+        hipLaunchKernelGGL((k_key_norm2<LSA_FP8_E4M3FN, 128>), grid, dim3(256), 0, s, g, cnt, sel_slot, pg,
+                           page_bytes, ikey_off, kn2);
+    else
+        hipLaunchKernelGGL((k_key_norm2<LSA_FP8_E4M3FN, 64>), grid, dim3(256), 0, s, g, cnt, sel_slot, pg,
+                           page_bytes, ikey_off, kn2);
+    timing_end("k_key_norm2", s);
     return hipGetLastError();
 }
