@@ -281,6 +281,53 @@ def test_window_pipeline_matches_oracle(host_cold):
     pipe.close()
 
 
+def test_window_pipeline_full_size_sampled():
+    """lsa_step64 on the 500K-token, batch-8 workload with the pinned-host cold
+    tier, 64 steps per window as the bench times it, over two windows with
+    2 % drift: sampled (request, step) units against the oracle (top-k bit
+    for bit, attention within tolerance) and every window's fetch count
+    against the pool simulation."""
+    R = _runner()
+    cfg = synth.dataclasses.replace(synth.config(4), windows=3)
+    inp = synth.generate(cfg, steps=64, threads=16)
+    dev = R.DeviceInputs(inp)
+    pipe = R.Pipeline(dev)
+    B, S, windows = cfg.batch, 64, 2
+    print(f"[setup] {cfg.name}: n_hist={list(inp['n_hist'])} slots/request={pipe.spr}", flush=True)
+    st0, _ = pipe.prime()
+    fetched = [st0["fetched"]]
+    outs = torch.empty((windows, S, B, cfg.Hq, cfg.Dv), dtype=torch.int16, device="cuda")
+    tks = torch.empty((windows, S, B, cfg.topk), dtype=torch.int32, device="cuda")
+    tcs = torch.empty((windows, S, B), dtype=torch.int32, device="cuda")
+    for m in range(windows):
+        print(f"[window] {m}", flush=True)
+        st, _ = pipe.window(m, 0, S, outs[m], topk=tks[m], tcnt=tcs[m], last=(m == windows - 1))
+        if m < windows - 1:
+            fetched.append(st["fetched"])
+    torch.cuda.synchronize()
+    tol, _ = tol_of(cfg)
+    per_req_sets = [[] for _ in range(B)]
+    samples = [[(0, 0), (B // 2, 31), (B - 1, S - 1)], [(1, 63), (B - 2, 1)]]
+    for m in range(windows):
+        o = oracle.Oracle(inp, kic=inp["kic_windows"][m], kic_scale=inp["kic_scale_windows"][m])
+        _, sel_o, cnt_o = o.score_select()
+        for r in range(B):
+            a = int(inp["chunk_off"][r])
+            per_req_sets[r].append(set(sel_o[a:a + cnt_o[r]].tolist()))
+        tk_o, out_o, _ = o.decode_units(samples[m], sel_o, cnt_o, cfg.topk, cfg.sm_scale)
+        for u, (r, j) in enumerate(samples[m]):
+            print(f"[unit] window={m} request={r} step={j}", flush=True)
+            tc = int(tcs[m, j, r].item())
+            assert tc == len(tk_o[u]), (m, r, j)
+            assert np.array_equal(tks[m, j, r, :tc].cpu().numpy(), tk_o[u]), (m, r, j)
+            got = R.out_to_f32(outs[m, j, r:r + 1], cfg)[0]
+            err = float(rel_err(got, out_o[u]).max())
+            assert err <= tol, (m, r, j, err)
+    sim = [oracle.pool_sim(per_req_sets[r], pipe.spr) for r in range(B)]
+    assert fetched == [sum(sim[r][m] for r in range(B)) for m in range(windows)]
+    pipe.close()
+
+
 def test_topk_all_ties_zero_query():
     """q = 0 makes every refine score +0: the k lowest candidate tokens."""
     inp, dev, o = setup("fp8")
