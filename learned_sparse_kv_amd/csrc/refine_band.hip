@@ -790,7 +790,7 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
     if (in_lds) {
         if (tid == 0) s_u = 0;
         // every entry's loads in flight before any is stored (kGB per thread)
-        constexpr int kGB = 4;
+        constexpr int kGB = 8;
         for (int j0 = 0; j0 < m; j0 += kT * kGB) {
             uint32_t kk[kGB];
             int32_t pp[kGB];
