@@ -468,6 +468,46 @@ void lsa_timing_reset(void);
 lsa_status lsa_timing_read(const char* kernel, int64_t* launches, double* total_ms);
 
 /* ------------------------------------------------------------------------
+ * Diagnostics: launch-shape overrides.  Each knob replaces one launch-shape
+ * choice of the library, process-wide, until set again; a value < 0 restores
+ * the library's own choice.  They exist so that tests reach rarely taken
+ * kernel paths at small sizes, and for measurement sweeps; the results of
+ * every entry point stay as documented under any setting.
+ *   LSA_TUNE_REFINE_BLOCKS    blocks per request of the matrix-core refine
+ *                             pass (>= 1; fewer blocks make each of its waves
+ *                             walk more chunks)
+ *   LSA_TUNE_ATTN_PAIR_POLLS  polls of the bf16 attention kernel's bounded
+ *                             wait for its partner wave (>= 0).  A wait that
+ *                             runs out is reported through lsa_device_status
+ *                             and lsa_step64 (LSA_ERR_HIP) and leaves that
+ *                             launch's output undefined; 0 makes every wait
+ *                             run out at once, which tests that report.
+ * Returns LSA_ERR_INVALID_ARG for an unknown knob or an invalid value.
+ * ---------------------------------------------------------------------- */
+typedef enum {
+    LSA_TUNE_REFINE_BLOCKS = 0,
+    LSA_TUNE_ATTN_PAIR_POLLS = 1,
+    LSA_TUNE_COUNT_ = 2
+} lsa_tune_knob;
+lsa_status lsa_tune_set(lsa_tune_knob knob, int32_t value);
+
+/* ------------------------------------------------------------------------
+ * Device-side error report.  A kernel whose bounded wait runs out (the bf16
+ * attention kernel's wait for its partner wave; see LSA_TUNE_ATTN_PAIR_POLLS)
+ * records that in a word that each GPU holds for the library, instead of
+ * returning a wrong result silently.  lsa_device_status waits for `stream`
+ * (NULL: the default stream), then returns LSA_OK if the current device's
+ * word is clear, or LSA_ERR_HIP if any kernel of the library set it since the
+ * last call, and clears it.  flags (host, nullable) receives the word:
+ *   bit 0  an attention pair wait ran out (that launch's output is undefined)
+ * lsa_step64 takes the word over at the end of each window (reads and clears
+ * it on the main stream) and returns LSA_ERR_HIP from the next call when that
+ * window set it; the window's own outputs are then undefined.  Library calls
+ * running on other streams of the same device meanwhile share the word.
+ * ---------------------------------------------------------------------- */
+lsa_status lsa_device_status(void* stream, uint32_t* flags);
+
+/* ------------------------------------------------------------------------
  * Diagnostics: achievable read bandwidth.  Reads `bytes` of device memory at
  * src (16-byte aligned, a multiple of 16) with a plain streaming kernel
  * (k_stream_read) and writes nothing but, practically never, one word to

@@ -82,6 +82,23 @@ const char* lsa_status_str(lsa_status s) {
     return "unknown status";
 }
 
+lsa_status lsa_device_status(void* stream, uint32_t* flags) {
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t* word = dev_err_word();
+    if (!word) return LSA_ERR_HIP;
+    uint32_t v = 0;
+    LSA_HIP(hipStreamSynchronize(s));
+    LSA_HIP(hipMemcpyAsync(&v, word, sizeof(v), hipMemcpyDeviceToHost, s));
+    LSA_HIP(hipStreamSynchronize(s));
+    if (v) {
+        const uint32_t zero = 0;
+        LSA_HIP(hipMemcpyAsync(word, &zero, sizeof(zero), hipMemcpyHostToDevice, s));
+        LSA_HIP(hipStreamSynchronize(s));
+    }
+    if (flags) *flags = v;
+    return v ? LSA_ERR_HIP : LSA_OK;
+}
+
 size_t lsa_score_ws_bytes(const lsa_geom* g, int32_t d) {
     if (!g || g->batch < 1 || d < 1) return 0;
     return align_up((size_t)g->batch * d * sizeof(float), 256);

@@ -21,6 +21,8 @@
 // k_attn_f32: fp32 rows, VALU, for small head counts (fp32 path).
 #include "lsa_internal.h"
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 namespace {
@@ -168,7 +170,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
                                                         const uint16_t* __restrict__ q, int Hq,
                                                         int n_splits, int per_split, int hgroups,
                                                         float sm_log2e, uint16_t* __restrict__ part_o,
-                                                        float* __restrict__ part_ml) {
+                                                        float* __restrict__ part_ml, int polls,
+                                                        uint32_t* __restrict__ err) {
     constexpr int NB = 2 * kKSteps;                   // operand blocks per tile (36)
     constexpr int NLmax = (NB + NW - 1) / NW;         // tile loads per wave (the first NB % NW waves)
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[kNBuf][kTileB];
@@ -360,13 +363,21 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_mla(GeomDev g, PosMap pm,
         }
         // publish them (the release orders the data writes before the flag)
         // and wait for the partner's: only the pair meets here, not the
-        // block.  The wait is bounded; the partner runs the same tile loop, so
-        // it always publishes.
+        // block.  The partner runs the same tile loop, so it always
+        // publishes; the wait is still bounded (polls), and one that runs
+        // out is recorded in the device's error word, so the output it
+        // spoils is reported instead of returned silently.
         __hip_atomic_store(&pflag[w], it + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        for (int spin = 0; spin < (1 << 20); ++spin) {
-            const int f = __hip_atomic_load(&pflag[w ^ 1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (__builtin_amdgcn_readfirstlane(f) > it) break;
-            __builtin_amdgcn_s_sleep(1);
+        {
+            int seen = -1;
+            for (int spin = 0; spin < polls; ++spin) {
+                seen = __builtin_amdgcn_readfirstlane(
+                    __hip_atomic_load(&pflag[w ^ 1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+                if (seen > it) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (seen <= it && L == 0 && err)
+                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         const float4* other = (const float4*)sx[w ^ 1];
         const int t0 = it * MT;
@@ -633,7 +644,9 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_attn_merge(const PT* __res
     }
     // fixed-order tree over the lanes
     for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
-    const float Lsum = part, inv = 1.0f / part;
+    // an empty attended set (no recent token, no top-k entry) has no
+    // softmax: its output is zero and its lse -inf
+    const float Lsum = part, inv = part > 0.0f ? 1.0f / part : 0.0f;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -689,7 +702,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_attn_merge(const PT* __res
             }
         }
     }
-    if (lse && cb == 0 && L == 0) lse[rh] = (m + __log2f(Lsum)) * kLn2;
+    if (lse && cb == 0 && L == 0) lse[rh] = Lsum > 0.0f ? (m + __log2f(Lsum)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -750,6 +763,29 @@ lsa_status attn_plan(const GeomDev& g, const lsa_kv_layout* kv, int Hq, int k, i
     return LSA_OK;
 }
 
+// Each GPU holds its own copy of the error word; its address is looked up
+// once per device (with that device current) and kept.
+__device__ uint32_t g_lsa_err_word;
+
+uint32_t* dev_err_word() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<uint32_t*> addr[kMaxDev];
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+    uint32_t* a = addr[dev].load(std::memory_order_acquire);
+    if (a) return a;
+    std::lock_guard<std::mutex> lk(mu);
+    a = addr[dev].load(std::memory_order_relaxed);
+    if (!a) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_lsa_err_word)) != hipSuccess || !p) return nullptr;
+        a = (uint32_t*)p;
+        addr[dev].store(a, std::memory_order_release);
+    }
+    return a;
+}
+
 hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, int Hq,
                        const lsa_kv_layout& kv, const void* pages, const int32_t* page_table,
                        const void* recent, const int32_t* topk, const int32_t* tcnt, int k,
@@ -760,17 +796,21 @@ hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, in
     float* part_ml = (float*)((uint8_t*)ws + plan.part_o_bytes);
     const float sm_log2e = sm_scale * 1.44269504088896340736f;
     if (plan.mode == 1) {
+        uint32_t* err = dev_err_word();
+        if (!err) return hipErrorInvalidSymbol;
+        const int tp = tune_get(LSA_TUNE_ATTN_PAIR_POLLS);
+        const int polls = tp >= 0 ? tp : (1 << 20);
         const int units = g.B * plan.n_splits;
         const int grid = (units + 7) / 8 * 8 * plan.head_groups;
         timing_begin("k_attn_mla", s);
         if (plan.waves == 8)
             hipLaunchKernelGGL((k_attn_mla<8, 1>), dim3(grid), dim3(512), 0, s, g, pm, tcnt,
                                (const uint16_t*)q, Hq, plan.n_splits, plan.per_split,
-                               plan.head_groups, sm_log2e, (uint16_t*)part_o, part_ml);
+                               plan.head_groups, sm_log2e, (uint16_t*)part_o, part_ml, polls, err);
         else
             hipLaunchKernelGGL((k_attn_mla<4, 1>), dim3(grid), dim3(256), 0, s, g, pm, tcnt,
                                (const uint16_t*)q, Hq, plan.n_splits, plan.per_split,
-                               plan.head_groups, sm_log2e, (uint16_t*)part_o, part_ml);
+                               plan.head_groups, sm_log2e, (uint16_t*)part_o, part_ml, polls, err);
         timing_end("k_attn_mla", s);
     } else {
         timing_begin("k_attn_f32", s);

@@ -99,6 +99,12 @@ void* lsa_pool_slots(const lsa_pool* p);
 int64_t lsa_pool_page_bytes(const lsa_pool* p);
 int32_t lsa_pool_batch(const lsa_pool* p);
 
+// Launch-shape override of lsa_tune_set (-1: the library's own choice).
+int tune_get(lsa_tune_knob knob);
+// The current device's error word (kernels OR flags into it), or nullptr if
+// its address cannot be had.
+uint32_t* dev_err_word();
+
 // Per-kernel event timing hooks (no-ops unless lsa_timing_enable(1)).
 void timing_begin(const char* name, hipStream_t s);
 void timing_end(const char* name, hipStream_t s);

@@ -207,10 +207,16 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
         // where the registers allow it)
         constexpr int DEPTH = NR * 4 * 4 <= 32 ? 2 : 1;
         uint4 raw[4][NR], raw2[4][NR];
-        auto fetch = [&](int j, uint4 (&dst)[4][NR]) __attribute__((always_inline)) {
+        // each key buffer carries its chunk's scale, taken from the index
+        // window together with the page: the window may move on (to the
+        // chunks 64 further) before the buffer's chunk is computed
+        float sc_a = 1.0f, sc_b = 1.0f;
+        auto fetch = [&](int j, uint4 (&dst)[4][NR], float& dsc) __attribute__((always_inline)) {
             const int src = j & 63;
             const int64_t pgo = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pg_l, src) |
                                 ((int64_t)__builtin_amdgcn_readlane((int)(pg_l >> 32), src) << 32);
+            if constexpr (KDT == LSA_FP8_E4M3FN)
+                dsc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), src));
             const uint8_t* base = pages + pgo * page_bytes + ikey_off;
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
@@ -219,8 +225,8 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
                     dst[tb][n] = *(const uint4*)(base + (tb * 16 + l16) * ROWB + n * 64 + lq * 16);
         };
         if (nj > 0) {
-            fetch(0, raw);
-            if (DEPTH == 2 && nj > 1) fetch(1, raw2);
+            fetch(0, raw, sc_a);
+            if (DEPTH == 2 && nj > 1) fetch(1, raw2, sc_b);
         }
         // Wq = sum_h |w_h| * |q_h|_2 (rounded up), from the operands held:
         // lane (l16, lq) has dims lq*8.. of every k-step of head hb*16 + l16
@@ -253,23 +259,24 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
                     else ka[tb][ks] = (ks & 1) ? fp8x8_to_bf16x8(raw[tb][ks >> 1].z, raw[tb][ks >> 1].w)
                                                : fp8x8_to_bf16x8(raw[tb][ks >> 1].x, raw[tb][ks >> 1].y);
                 }
-            const float scale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), j & 63));
+            const float scale = sc_a;
             if constexpr (DEPTH == 2) {
                 if (j + 1 < nj) {
 #pragma unroll
                     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
                         for (int n = 0; n < NR; ++n) raw[tb][n] = raw2[tb][n];
+                    sc_a = sc_b;
                     if (j + 2 < nj) {
-                        // the index window moves 64 chunks at a time; its scales
-                        // are read for chunk j above, so it may move now
+                        // the index window moves 64 chunks at a time; the
+                        // chunks in flight already hold their pages and scales
                         if (((j + 2) & 63) == 0) load_idx(j + 2, nj);
-                        fetch(j + 2, raw2);
+                        fetch(j + 2, raw2, sc_b);
                     }
                 }
             } else if (j + 1 < nj) {
                 if (((j + 1) & 63) == 0) load_idx(j + 1, nj);
-                fetch(j + 1, raw);
+                fetch(j + 1, raw, sc_a);
             }
             // |key|^2 on the matrix cores (unless given): the diagonal of the
             // 16x16 Gram block of tokens tb*16..; lane (l16, lq) holds rows
@@ -974,6 +981,8 @@ static int max_hist(const GeomDev& g) {
 // K1 blocks per request: about two blocks per CU over the whole batch, no
 // more than the longest history needs.
 static int k1_blocks(const GeomDev& g) {
+    const int forced = tune_get(LSA_TUNE_REFINE_BLOCKS);
+    if (forced >= 1) return forced;
     int x = (512 + g.B - 1) / g.B;
     const int need = (max_hist(g) + kWaves - 1) / kWaves;
     if (x > need) x = need;

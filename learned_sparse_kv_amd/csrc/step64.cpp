@@ -37,6 +37,8 @@ struct lsa_ctx {
     float* kn2 = nullptr;         // |key|^2 of their tokens
     int32_t* h_sel[2] = {nullptr, nullptr};
     int32_t* h_cnt[2] = {nullptr, nullptr};
+    uint32_t* h_err = nullptr;   // pinned [3]: the device error word after each window, 0
+    uint32_t* d_err = nullptr;   // the device error word
     hipEvent_t ev_sel = nullptr, ev_win[2] = {nullptr, nullptr}, ev_fetch[2] = {nullptr, nullptr};
     int cur = 0;
     bool primed = false;
@@ -176,7 +178,10 @@ lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc) {
              hipEventCreateWithFlags(&x->ev_win[i], hipEventDisableTiming) == hipSuccess &&
              hipEventCreateWithFlags(&x->ev_fetch[i], hipEventDisableTiming) == hipSuccess;
     }
-    ok = ok && hipEventCreateWithFlags(&x->ev_sel, hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&x->ev_sel, hipEventDisableTiming) == hipSuccess &&
+         hipHostMalloc((void**)&x->h_err, 3 * sizeof(uint32_t), hipHostMallocDefault) == hipSuccess &&
+         (x->d_err = dev_err_word()) != nullptr;
+    if (ok) x->h_err[0] = x->h_err[1] = x->h_err[2] = 0;
     if (!ok) {
         lsa_ctx_destroy(x);
         return LSA_ERR_HIP;
@@ -198,6 +203,7 @@ void lsa_ctx_destroy(lsa_ctx* x) {
         if (x->ev_fetch[i]) (void)hipEventDestroy(x->ev_fetch[i]);
     }
     if (x->ev_sel) (void)hipEventDestroy(x->ev_sel);
+    if (x->h_err) (void)hipHostFree(x->h_err);
     delete x;
 }
 
@@ -282,9 +288,19 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
                         ms) != hipSuccess)
             return LSA_ERR_HIP;
     }
+    // the device error word as this window leaves it, taken over (and
+    // cleared) so that it reports this window only; the next call reads it
+    // once its wait below has passed this window
+    if (hipMemcpyAsync(&x->h_err[cur], x->d_err, sizeof(uint32_t), hipMemcpyDeviceToHost, ms) !=
+            hipSuccess ||
+        hipMemcpyAsync(x->d_err, &x->h_err[2], sizeof(uint32_t), hipMemcpyHostToDevice, ms) != hipSuccess)
+        return LSA_ERR_HIP;
     if (hipEventRecord(x->ev_win[cur], ms) != hipSuccess) return LSA_ERR_HIP;
+    bool dev_err = false;
     if (in->next) {
         if (hipEventSynchronize(x->ev_sel) != hipSuccess) return LSA_ERR_HIP;
+        // ev_sel follows the previous window on the main stream
+        dev_err = x->h_err[nxt] != 0;
         lsa_gather_stats gs{};
         lsa_status st = lsa_gather_kv(x->d.pool, x->h_sel[nxt], x->h_cnt[nxt], x->h_sel[cur],
                                       x->h_cnt[cur], x->pt[nxt], copy_stream, x->ev_win[nxt],
@@ -297,7 +313,7 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
     } else {
         x->have_next = false;
     }
-    return LSA_OK;
+    return dev_err ? LSA_ERR_HIP : LSA_OK;
 }
 
 }  // extern "C"

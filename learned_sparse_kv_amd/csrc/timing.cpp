@@ -1,9 +1,13 @@
-// Per-kernel timing with HIP events (diagnostics).
+// Diagnostics: per-kernel timing with HIP events, and launch-shape overrides.
 //
 // When enabled, every kernel the library launches is bracketed by two
 // events recorded on the stream it is launched on; lsa_timing_read
 // synchronises them and returns the launch count and summed duration per
 // kernel name.  Disabled (the default), the hooks cost one relaxed load.
+//
+// The overrides (lsa_tune_set) replace a launch-shape choice of the library
+// process-wide, so that tests reach rarely taken kernel paths at small sizes
+// and sweeps can try other shapes; -1 means the library's own choice.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -31,6 +35,7 @@ std::map<std::string, std::vector<Pair>> g_pending;
 std::map<std::string, std::pair<int64_t, double>> g_done;
 std::vector<hipEvent_t> g_free;  // recycled events (created once, reused)
 thread_local hipEvent_t t_start = nullptr;
+std::atomic<int> g_tune[LSA_TUNE_COUNT_] = {-1, -1};
 
 hipEvent_t take_event() {
     {
@@ -90,7 +95,18 @@ static void drain() {
     g_pending.clear();
 }
 
+int tune_get(lsa_tune_knob knob) {
+    return (int)knob >= 0 && (int)knob < LSA_TUNE_COUNT_ ? g_tune[knob].load(std::memory_order_relaxed) : -1;
+}
+
 extern "C" {
+
+lsa_status lsa_tune_set(lsa_tune_knob knob, int32_t value) {
+    if ((int)knob < 0 || (int)knob >= LSA_TUNE_COUNT_) return LSA_ERR_INVALID_ARG;
+    if (knob == LSA_TUNE_REFINE_BLOCKS && value == 0) return LSA_ERR_INVALID_ARG;
+    g_tune[knob].store(value < 0 ? -1 : value, std::memory_order_relaxed);
+    return LSA_OK;
+}
 
 lsa_status lsa_timing_enable(int32_t on) {
     g_on.store(on ? 1 : 0);

@@ -113,6 +113,8 @@ def _load():
         "lsa_timing_reset": ([], None),
         "lsa_timing_read": ([C.c_char_p, C.POINTER(I64), C.POINTER(C.c_double)], I),
         "lsa_stream_read": ([P, SZ, P, P], I),
+        "lsa_tune_set": ([I, I32], I),
+        "lsa_device_status": ([P, C.POINTER(C.c_uint32)], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -383,3 +385,19 @@ def lsa_timing_read(kernel: str):
 
 def lsa_stream_read(src, nbytes: int, sink, stream=None):
     _check("lsa_stream_read", _lib.lsa_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
+
+
+TUNE_REFINE_BLOCKS, TUNE_ATTN_PAIR_POLLS = 0, 1
+
+
+def lsa_tune_set(knob: int, value: int):
+    """Launch-shape override (value < 0: the library's own choice)."""
+    _check("lsa_tune_set", _lib.lsa_tune_set(int(knob), int(value)))
+
+
+def lsa_device_status(stream=None):
+    """(status code, flags) of the device error word; clears it.  Does not
+    raise: a set word returns LSA_ERR_HIP (-5) with its flags."""
+    f = C.c_uint32(0)
+    code = _lib.lsa_device_status(_stream(stream), C.byref(f))
+    return int(code), int(f.value)

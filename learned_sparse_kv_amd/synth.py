@@ -15,6 +15,10 @@ per request, PCG64 streams):
 * coarse query q_h ~ N(0, H/4) per element, w_h = 1/H, b = -1.0.  The fused
   query then has per-element variance 1/4, unplanted logits are ~N(-1, 1/4)
   (about 2.3 % of them exceed 0) and planted logits sit far above 0.
+  With ``signed_weights`` the head weights (coarse and per step) are drawn
+  U(-1, 1) per head and scaled so that sum_h w_h^2 = 1/H as for 1/H (so the
+  fused query keeps its variance), and each request's bias is drawn
+  U(-1.25, -0.75): weights of both signs that are not powers of two.
 * per-token index keys ~ N(0, 1/d); refine queries ~ N(0, 1), w = 1/H.
 * attention queries and KV ~ N(0, 1); separate K and V for the fp32 config,
   a 576-wide latent row (value = first 512) otherwise.
@@ -66,6 +70,7 @@ class LsaConfig:
     drift: float = 0.0
     host_cold: bool = False         # cold tier lives in pinned host memory
     slots_per_req: int = 1024
+    signed_weights: bool = False    # head weights U(-1, 1) (scaled), bias per request
 
     # ---- layout sizes (byte layout of the ABI) ----
     @property
@@ -184,9 +189,10 @@ def seq_lens_of(cfg: LsaConfig):
 # generation
 # ----------------------------------------------------------------------------
 _T_KIC, _T_PLANT, _T_QC, _T_IKEY, _T_KVH, _T_KVR, _T_QR, _T_QA, _T_DRIFT = range(9)
-_T_LAYER = 100  # tensor ids of indexer layer l >= 1: _T_LAYER + 10 l + {0: KIComp, 1: planted, 2: query}
+_T_LAYER = 100  # tensor ids of indexer layer l >= 1: _T_LAYER + 10 l + {0: KIComp, 1: planted, 2: query, 3: weights}
 _T_POLICY = 200  # random-policy keys of window w: _T_POLICY + w
 _T_FOCUS = 300
+_T_WC, _T_WR = 400, 402  # signed coarse weights (and biases), refine weights
 
 
 def _rng(root: np.random.SeedSequence, tensor: int, req: int = 0):
@@ -199,6 +205,27 @@ def _normal(rng, shape, std=1.0):
     if std != 1.0:
         x *= np.float32(std)
     return x
+
+
+def _signed_weights(rng, shape):
+    """Head weights (last axis) of both signs: U(-1, 1), scaled per row so
+    that sum_h w_h^2 = 1/H, as for the uniform weights 1/H."""
+    u = rng.uniform(-1.0, 1.0, size=shape)
+    H = shape[-1]
+    u /= np.sqrt(H * (u * u).sum(axis=-1, keepdims=True))
+    return u.astype(np.float32)
+
+
+def _coarse_weights(cfg, root, tensor, B, H):
+    """Coarse head weights [B, H] and biases [B] of one indexer layer."""
+    if not cfg.signed_weights:
+        return np.full((B, H), 1.0 / H, dtype=np.float32), np.full((B,), -1.0, dtype=np.float32)
+    w, b = np.zeros((B, H), np.float32), np.zeros(B, np.float32)
+    for r in range(B):
+        rng = _rng(root, tensor, r)  # the request's weights, then its bias
+        w[r] = _signed_weights(rng, (H,))
+        b[r] = rng.uniform(-1.25, -0.75)
+    return w, b
 
 
 class Inputs(dict):
@@ -221,8 +248,7 @@ def generate(cfg: LsaConfig, steps: int | None = None, threads: int = 8) -> Inpu
     q_raw = np.stack([_normal(_rng(root, _T_QC, r), (H, d), std=np.sqrt(H / 4.0))
                       for r in range(B)])
     out["q_coarse"] = encode(q_raw, cfg.q_dtype)
-    out["w_coarse"] = np.full((B, H), 1.0 / H, dtype=np.float32)
-    out["bias"] = np.full((B,), -1.0, dtype=np.float32)
+    out["w_coarse"], out["bias"] = _coarse_weights(cfg, root, _T_WC, B, H)
     qv = decode_query_f64(out["q_coarse"], cfg.q_dtype)
     u = np.einsum("bh,bhd->bd", out["w_coarse"].astype(np.float64), qv)
     u /= np.linalg.norm(u, axis=1, keepdims=True)
@@ -301,13 +327,17 @@ def generate(cfg: LsaConfig, steps: int | None = None, threads: int = 8) -> Inpu
     recent = np.empty((NR, cfg.kv_row_bytes), dtype=np.uint8)
     for r in range(B):
         x = _normal(_rng(root, _T_KVR, r), (int(n_rec[r]), cfg.kv_row_elems))
-        recent[rec_off[r]:rec_off[r + 1]] = encode(x, cfg.kv_dtype).reshape(int(n_rec[r]), -1).view(np.uint8)
+        enc = np.ascontiguousarray(encode(x, cfg.kv_dtype)).view(np.uint8)
+        recent[rec_off[r]:rec_off[r + 1]] = enc.reshape(int(n_rec[r]), cfg.kv_row_bytes)
     out["recent"] = recent
 
     # ---- per-step refine and attention queries ----
     qr = _normal(_rng(root, _T_QR), (steps, B, H, d))
     out["q_refine"] = encode(qr, cfg.q_dtype)
-    out["w_refine"] = np.full((steps, B, H), 1.0 / H, dtype=np.float32)
+    if cfg.signed_weights:
+        out["w_refine"] = _signed_weights(_rng(root, _T_WR), (steps, B, H))
+    else:
+        out["w_refine"] = np.full((steps, B, H), 1.0 / H, dtype=np.float32)
     qa = _normal(_rng(root, _T_QA), (steps, B, cfg.Hq, cfg.Dk))
     out["q_attn"] = encode(qa, cfg.kv_dtype)
     return out
@@ -315,12 +345,13 @@ def generate(cfg: LsaConfig, steps: int | None = None, threads: int = 8) -> Inpu
 
 def small_config(name="small_bf16", seed=11, seq_lens=(5000, 3000), window=1024, idx=BF16,
                  topk=256, steps=3, H=8, d=128, Hq=64, Dk=576, Dv=512, kv=BF16,
-                 separate_v=False, planted=0.12, q_dtype=None) -> LsaConfig:
+                 separate_v=False, planted=0.12, q_dtype=None, signed_weights=False) -> LsaConfig:
     """Parity-test shapes: several tiles and a ragged tail, seconds on the CPU."""
     return LsaConfig(name, seed, len(seq_lens), tuple(seq_lens), window=window, H=H, d=d,
                      q_dtype=(F32 if kv == F32 else BF16) if q_dtype is None else q_dtype,
                      idx_dtype=idx, planted=planted, topk=topk, Hq=Hq, Dk=Dk, Dv=Dv,
-                     kv_dtype=kv, separate_v=separate_v, steps=steps)
+                     kv_dtype=kv, separate_v=separate_v, steps=steps,
+                     signed_weights=signed_weights)
 
 
 def attention_focus(inp: Inputs, boost: float = 2.5, window: int = 0) -> Inputs:
@@ -389,7 +420,7 @@ def indexer_layers(inp: Inputs, n_layers: int = 3, window: int = 0):
         t = _T_LAYER + 10 * l
         q_raw = np.stack([_normal(_rng(root, t + 2, r), (H, d), std=np.sqrt(H / 4.0)) for r in range(B)])
         q_enc = encode(q_raw, cfg.q_dtype)
-        w = np.full((B, H), 1.0 / H, dtype=np.float32)
+        w, bias = _coarse_weights(cfg, root, t + 3, B, H)
         qv = decode_query_f64(q_enc, cfg.q_dtype)
         u = np.einsum("bh,bhd->bd", w.astype(np.float64), qv)
         u /= np.linalg.norm(u, axis=1, keepdims=True)
@@ -404,6 +435,5 @@ def indexer_layers(inp: Inputs, n_layers: int = 3, window: int = 0):
             enc, sc = to_fp8_blocks(rows)
         else:
             enc, sc = encode(rows, cfg.idx_dtype), np.ones(NH, np.float32)
-        layers.append(dict(q_coarse=q_enc, w_coarse=w, bias=np.full((B,), -1.0, dtype=np.float32),
-                           kic=enc, kic_scale=sc))
+        layers.append(dict(q_coarse=q_enc, w_coarse=w, bias=bias, kic=enc, kic_scale=sc))
     return layers

@@ -388,7 +388,10 @@ static const void* o_kv_row(const lsao_batch* b, int64_t chunk0, int64_t rec0, i
 /* A = the top-k tokens followed by the recent tokens [rs, L).  For every
  * query head h:  x_i = sm * q_h . K_i,  m = max x,  p_i = exp(x_i - m),
  * l = sum p,  o_h = sum_i p_i V_i / l,  lse_h = m + ln l.  K_i is the first
- * Dk elements of token i's KV row, V_i the Dv elements at v_off. */
+ * Dk elements of token i's KV row, V_i the Dv elements at v_off.
+ * An empty A (no recent token and an empty top-k; the pages never reach it,
+ * their recent window is always attended) has no softmax: the reading taken
+ * is the value of an empty sum, o_h = 0 and lse_h = ln 0 = -inf. */
 int lsao_attend(const lsao_batch* b, int32_t r, const int32_t* topk, int32_t kcnt,
                 const void* q_r, double sm, double* out, double* lse) {
     int64_t chunk0, rec0, g[3];
@@ -400,7 +403,11 @@ int lsao_attend(const lsao_batch* b, int32_t r, const int32_t* topk, int32_t kcn
     if (!rows || !x) return -1;
     for (int32_t i = 0; i < kcnt; i++) rows[i] = o_kv_row(b, chunk0, rec0, rs, topk[i]);
     for (int64_t s = rs; s < L; s++) rows[kcnt + (s - rs)] = o_kv_row(b, chunk0, rec0, rs, s);
-    for (int32_t h = 0; h < b->Hq; h++) {
+    for (int32_t h = 0; h < b->Hq && nA == 0; h++) {
+        for (int32_t e = 0; e < b->Dv; e++) out[(int64_t)h * b->Dv + e] = 0.0;
+        lse[h] = -INFINITY;
+    }
+    for (int32_t h = 0; h < b->Hq && nA > 0; h++) {
         double m = -INFINITY;
         for (int64_t i = 0; i < nA; i++) {
             double acc = 0.0;

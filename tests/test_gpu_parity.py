@@ -31,6 +31,10 @@ def _lsa():
 
 
 def small(kind):
+    """Parity-test configurations; a "_sw" suffix gives the same shapes with
+    signed head weights that are not powers of two and a bias per request."""
+    if kind.endswith("_sw"):
+        return synth.dataclasses.replace(small(kind[:-3]), signed_weights=True, name=kind)
     if kind == "f32":
         return synth.small_config("f32_small", 21, (5000, 2100, 700), window=1024, idx=F32, kv=F32,
                                   H=4, d=64, Hq=8, Dk=128, Dv=128, separate_v=True, topk=256,
@@ -69,22 +73,36 @@ def rel_err(got, ref):
 _cache = {}
 
 
+def config_of(kind):
+    if not kind.startswith("cfg"):
+        return small(kind)
+    cfg = synth.config(int(kind[3]))
+    if kind.endswith("_sw"):
+        cfg = synth.dataclasses.replace(cfg, signed_weights=True, name=cfg.name + "_sw")
+    return cfg
+
+
 def setup(kind):
+    """Inputs, device copies and oracle of a kind.  Small kinds stay cached;
+    a full-size config replaces every other full-size one."""
     if kind not in _cache:
-        cfg = small(kind) if not kind.startswith("cfg") else synth.config(int(kind[3]))
+        cfg = config_of(kind)
         steps = None if not kind.startswith("cfg") else 2
         inp = synth.generate(cfg, steps=steps)
         print(f"[setup] {kind}: lens={list(inp['seq_len'])} n_hist={list(inp['n_hist'])}",
               flush=True)
-        _cache.clear()
+        if kind.startswith("cfg"):
+            for k in [k for k in _cache if k.startswith("cfg")]:
+                del _cache[k]
         _cache[kind] = (inp, _runner().DeviceInputs(inp), oracle.Oracle(inp))
     return _cache[kind]
 
 
 SMALL = ["f32", "bf16", "fp8", "bf16_h128", "bf16_h8"]
+SIGNED = [k + "_sw" for k in SMALL] + ["cfg3_sw"]
 
 
-@pytest.mark.parametrize("kind", SMALL + ["cfg0", "cfg1", "cfg2", "cfg3"])
+@pytest.mark.parametrize("kind", SMALL + ["cfg0", "cfg1", "cfg2", "cfg3"] + SIGNED)
 def test_score_select_bitexact(kind):
     inp, dev, o = setup(kind)
     z, sel, cnt = dev.score_select()
@@ -108,7 +126,7 @@ def _units(inp, full):
     return [(r, j % S) for j, r in enumerate(rs)]
 
 
-@pytest.mark.parametrize("kind", SMALL + ["cfg0", "cfg1", "cfg2", "cfg3"])
+@pytest.mark.parametrize("kind", SMALL + ["cfg0", "cfg1", "cfg2", "cfg3"] + SIGNED)
 def test_refine_topk_and_attention(kind):
     inp, dev, o = setup(kind)
     cfg = inp.cfg
@@ -234,13 +252,19 @@ def test_topk_k1_and_k_exceeding_candidates():
             assert np.array_equal(got, want), (k, r)
 
 
-@pytest.mark.parametrize("host_cold", [False, True])
-def test_window_pipeline_matches_oracle(host_cold):
+@pytest.mark.parametrize("host_cold,variant", [(False, "band"), (True, "band"), (True, "valu")])
+def test_window_pipeline_matches_oracle(host_cold, variant):
     """lsa_step64 over three windows with drift: per-window outputs and
-    per-fetch copy counts against the oracle and the pool simulation."""
+    per-fetch copy counts against the oracle and the pool simulation.  The
+    "valu" variant (8 indexer heads, bf16 keys, signed head weights) takes the
+    pipeline's vector-ALU refine instead of the matrix-core band."""
     R = _runner()
-    cfg = synth.small_config("pipe", 31, (12000, 7000), window=1024, idx=FP8, H=16, topk=256,
-                             steps=6, planted=0.10)
+    if variant == "band":
+        cfg = synth.small_config("pipe", 31, (12000, 7000), window=1024, idx=FP8, H=16, topk=256,
+                                 steps=6, planted=0.10)
+    else:
+        cfg = synth.small_config("pipe_valu", 33, (12000, 7000), window=1024, idx=BF16, H=8, topk=256,
+                                 steps=6, planted=0.10, signed_weights=True)
     cfg = synth.dataclasses.replace(cfg, windows=4, drift=0.10, host_cold=host_cold,
                                     slots_per_req=80)
     inp = synth.generate(cfg)
@@ -349,7 +373,7 @@ def test_topk_all_ties_zero_query():
         assert list(got) == want
 
 
-@pytest.mark.parametrize("kind", ["f32", "bf16", "fp8", "cfg3"])
+@pytest.mark.parametrize("kind", ["f32", "bf16", "fp8", "cfg3", "bf16_sw", "fp8_sw", "cfg3_sw"])
 def test_score_union_bitexact(kind):
     """OR-mode union over three indexer layers: the combined logits bitwise,
     the selected ids and counts exactly."""
@@ -426,8 +450,9 @@ def _check_sigmoid(inp, dev, o, q=None, w=None, bias=None, exact=False):
     return S, S_o, int(near.sum())
 
 
-SIG_EXACT = ["f32", "bf16_qf32", "fp8_qf32"]      # fp32 queries: one lane per chunk
-SIG_MFMA = ["bf16", "fp8", "bf16_h128", "bf16_h8", "cfg1", "cfg3"]
+SIG_EXACT = ["f32", "bf16_qf32", "fp8_qf32", "f32_sw", "fp8_qf32_sw"]  # fp32 queries: one lane per chunk
+SIG_MFMA = ["bf16", "fp8", "bf16_h128", "bf16_h8", "cfg1", "cfg3", "bf16_sw", "fp8_sw", "bf16_h8_sw",
+            "cfg3_sw"]
 
 
 @pytest.mark.parametrize("kind", SIG_EXACT)

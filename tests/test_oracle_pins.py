@@ -308,6 +308,24 @@ def test_attention_closed_forms():
     np.testing.assert_allclose(lse, np.log(len(rows)), rtol=1e-14)
 
 
+def test_attention_empty_set_is_empty_sum():
+    """No recent token (window 0, context a multiple of the chunk) and an
+    empty top-k: the attended set is empty, and the output is the value of an
+    empty sum (0) with lse = ln 0 = -inf; one attended token in the other
+    request still gives that token's V row exactly."""
+    inp = helpers.tiny_inputs(seq_lens=(8, 9), window=0)
+    cfg = inp.cfg
+    assert list(inp["n_rec"]) == [0, 1]
+    o = oracle.Oracle(inp)
+    out, lse = o.attend(0, [], inp["q_attn"][0, 0], cfg.sm_scale)
+    assert out.shape == (cfg.Hq, cfg.Dv) and np.all(out == 0) and np.all(np.isneginf(lse))
+    _, sel, cnt = o.score_select(theta=float("inf"))
+    _, outs, lses = o.decode_units([(0, 0), (1, 1)], sel, cnt, cfg.topk, cfg.sm_scale)
+    assert np.all(outs[0] == 0) and np.all(np.isneginf(lses[0]))
+    K, V = helpers.kv_rows(inp, 1)
+    assert (outs[1] == V[8][None, :]).all()
+
+
 # ---------------------------------------------------------------- PIN-10 pool
 def test_pool_sim_closed_forms():
     s = [set(range(10)), set(range(10)), set(range(10))]
