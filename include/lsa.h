@@ -252,6 +252,27 @@ lsa_status lsa_sparse_decode_attn(const lsa_geom* g, const void* q, int32_t Hq,
                                   void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * a7 without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * it).  Same arguments, results and errors as lsa_sparse_decode_attn, bit for
+ * bit, but the split partials live in a scratch array of
+ * lsa_attn_noalloc_max_bytes() bytes (32 MiB) that the library holds on each
+ * GPU from its load until the process ends.  A call whose partials need more
+ * (lsa_attn_ws_bytes(...) > that size) returns LSA_ERR_WORKSPACE and
+ * enqueues nothing.  The call allocates nothing.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams, or
+ * other threads) race and give undefined outputs; serialise them.  Nothing in
+ * the array needs to start at zero (each call writes every partial it reads).
+ * ---------------------------------------------------------------------- */
+size_t lsa_attn_noalloc_max_bytes(void);
+lsa_status lsa_sparse_decode_attn_noalloc(const lsa_geom* g, const void* q, int32_t Hq,
+                                          const lsa_kv_layout* kv, const void* pages,
+                                          const int32_t* page_table, const void* recent,
+                                          const int32_t* topk_idx, const int32_t* topk_cnt,
+                                          int32_t k, float sm_scale, void* out, float* lse,
+                                          int32_t n_splits, void* stream);
+
+/* ------------------------------------------------------------------------
  * Growing context (geometry with recent_cap > 0 and chunk_cap > 0; see the
  * top of this file).  The pages' indexer fires every 64 decode steps to
  * predict the history the next 64 steps need (cjcn.com.cn explainer,

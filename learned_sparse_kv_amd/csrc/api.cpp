@@ -373,6 +373,23 @@ size_t lsa_attn_ws_bytes(const lsa_geom* g, const lsa_kv_layout* kv, int32_t Hq,
     return p.part_o_bytes + p.part_ml_bytes;
 }
 
+// Argument checks and plan of both attention entry points (ws is checked
+// by the caller).
+static lsa_status attn_args(const lsa_geom* g, const void* q, int32_t Hq, const lsa_kv_layout* kv,
+                            const void* pages, const void* recent, const int32_t* topk_idx,
+                            const int32_t* topk_cnt, int32_t k, float sm_scale, void* out,
+                            int32_t n_splits, GeomDev* gd, AttnPlan* plan) {
+    lsa_status st = geom_derive(g, gd);
+    if (st != LSA_OK) return st;
+    st = check_kv(kv);
+    if (st != LSA_OK) return st;
+    if (!q || !recent || !topk_idx || !topk_cnt || !out || Hq < 1 || k < 1) return LSA_ERR_INVALID_ARG;
+    if (gd->chunk_off[gd->B] > 0 && !pages) return LSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(recent) || (pages && !aligned16(pages))) return LSA_ERR_INVALID_ARG;
+    if (!(sm_scale == sm_scale) || n_splits < 0) return LSA_ERR_INVALID_ARG;
+    return attn_plan(*gd, kv, Hq, k, n_splits, plan);
+}
+
 lsa_status lsa_sparse_decode_attn(const lsa_geom* g, const void* q, int32_t Hq,
                                   const lsa_kv_layout* kv, const void* pages,
                                   const int32_t* page_table, const void* recent,
@@ -380,20 +397,33 @@ lsa_status lsa_sparse_decode_attn(const lsa_geom* g, const void* q, int32_t Hq,
                                   float sm_scale, void* out, float* lse, int32_t n_splits,
                                   void* ws, size_t ws_bytes, void* stream) {
     GeomDev gd;
-    lsa_status st = geom_derive(g, &gd);
-    if (st != LSA_OK) return st;
-    st = check_kv(kv);
-    if (st != LSA_OK) return st;
-    if (!q || !recent || !topk_idx || !topk_cnt || !out || !ws || Hq < 1 || k < 1)
-        return LSA_ERR_INVALID_ARG;
-    if (gd.chunk_off[gd.B] > 0 && !pages) return LSA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(recent) || !aligned16(ws) || (pages && !aligned16(pages)))
-        return LSA_ERR_INVALID_ARG;
-    if (!(sm_scale == sm_scale) || n_splits < 0) return LSA_ERR_INVALID_ARG;
     AttnPlan plan;
-    st = attn_plan(gd, kv, Hq, k, n_splits, &plan);
+    lsa_status st = attn_args(g, q, Hq, kv, pages, recent, topk_idx, topk_cnt, k, sm_scale, out,
+                              n_splits, &gd, &plan);
     if (st != LSA_OK) return st;
+    if (!ws || !aligned16(ws)) return LSA_ERR_INVALID_ARG;
     if (ws_bytes < plan.part_o_bytes + plan.part_ml_bytes) return LSA_ERR_WORKSPACE;
+    LSA_HIP(launch_attn(gd, plan, q, Hq, *kv, pages, page_table, recent, topk_idx, topk_cnt, k,
+                        sm_scale, out, lse, ws, (hipStream_t)stream));
+    return LSA_OK;
+}
+
+size_t lsa_attn_noalloc_max_bytes(void) { return attn_scratch_bytes(); }
+
+lsa_status lsa_sparse_decode_attn_noalloc(const lsa_geom* g, const void* q, int32_t Hq,
+                                          const lsa_kv_layout* kv, const void* pages,
+                                          const int32_t* page_table, const void* recent,
+                                          const int32_t* topk_idx, const int32_t* topk_cnt,
+                                          int32_t k, float sm_scale, void* out, float* lse,
+                                          int32_t n_splits, void* stream) {
+    GeomDev gd;
+    AttnPlan plan;
+    lsa_status st = attn_args(g, q, Hq, kv, pages, recent, topk_idx, topk_cnt, k, sm_scale, out,
+                              n_splits, &gd, &plan);
+    if (st != LSA_OK) return st;
+    if (plan.part_o_bytes + plan.part_ml_bytes > attn_scratch_bytes()) return LSA_ERR_WORKSPACE;
+    void* ws = attn_scratch();  // the device address of this GPU's array
+    if (!ws) return LSA_ERR_HIP;
     LSA_HIP(launch_attn(gd, plan, q, Hq, *kv, pages, page_table, recent, topk_idx, topk_cnt, k,
                         sm_scale, out, lse, ws, (hipStream_t)stream));
     return LSA_OK;

@@ -767,6 +767,35 @@ lsa_status attn_plan(const GeomDev& g, const lsa_kv_layout* kv, int Hq, int k, i
 // once per device (with that device current) and kept.
 __device__ uint32_t g_lsa_err_word;
 
+// The split partials of lsa_sparse_decode_attn_noalloc, for callers that
+// cannot allocate: a device array of fixed size that each GPU holds from the
+// library's load until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in); it uses the device
+// address that attn_scratch() looks up once per device.
+constexpr size_t kAttnScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kAttnScratchBytes];
+
+size_t attn_scratch_bytes() { return kAttnScratchBytes; }
+
+void* attn_scratch() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<void*> addr[kMaxDev];
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+    void* a = addr[dev].load(std::memory_order_acquire);
+    if (a) return a;
+    std::lock_guard<std::mutex> lk(mu);
+    a = addr[dev].load(std::memory_order_relaxed);
+    if (!a) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        a = p;
+        addr[dev].store(a, std::memory_order_release);
+    }
+    return a;
+}
+
 uint32_t* dev_err_word() {
     constexpr int kMaxDev = 64;
     static std::atomic<uint32_t*> addr[kMaxDev];

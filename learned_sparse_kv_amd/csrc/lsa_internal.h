@@ -94,6 +94,11 @@ hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, in
 hipError_t launch_gather(const int32_t* pairs, int n_pairs, const void* src, void* dst,
                          int64_t page_bytes, hipStream_t s);
 
+// Device address of the attention scratch array of the current device
+// (nullptr if it cannot be had) and its size.
+void* attn_scratch();
+size_t attn_scratch_bytes();
+
 // Device slot memory of a pool (pages of the resident chunks).
 void* lsa_pool_slots(const lsa_pool* p);
 int64_t lsa_pool_page_bytes(const lsa_pool* p);

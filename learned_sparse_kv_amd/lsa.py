@@ -114,6 +114,9 @@ def _load():
         "lsa_timing_read": ([C.c_char_p, C.POINTER(I64), C.POINTER(C.c_double)], I),
         "lsa_stream_read": ([P, SZ, P, P], I),
         "lsa_tune_set": ([I, I32], I),
+        "lsa_attn_noalloc_max_bytes": ([], SZ),
+        "lsa_sparse_decode_attn_noalloc": ([G, P, I32, C.POINTER(lsa_kv_layout), P, P, P, P, P, I32, F,
+                                            P, P, I32, P], I),
         "lsa_device_status": ([P, C.POINTER(C.c_uint32)], I),
     }
     for name, (args, res) in sig.items():
@@ -275,6 +278,19 @@ def lsa_sparse_decode_attn(g: Geom, q, Hq, kv: lsa_kv_layout, pages, page_table,
                                        _ptr(topk_cnt), k, float(sm_scale), _ptr(out), _ptr(lse),
                                        n_splits, _ptr(ws), ws.numel() * ws.element_size(),
                                        _stream(stream)))
+
+
+def lsa_attn_noalloc_max_bytes() -> int:
+    return _lib.lsa_attn_noalloc_max_bytes()
+
+
+def lsa_sparse_decode_attn_noalloc(g: Geom, q, Hq, kv: lsa_kv_layout, pages, page_table, recent, topk_idx,
+                                   topk_cnt, k, sm_scale, out, lse, n_splits, stream=None):
+    _check("lsa_sparse_decode_attn_noalloc",
+           _lib.lsa_sparse_decode_attn_noalloc(g.ref, _ptr(q), Hq, C.byref(kv), _ptr(pages),
+                                               _ptr(page_table), _ptr(recent), _ptr(topk_idx),
+                                               _ptr(topk_cnt), k, float(sm_scale), _ptr(out), _ptr(lse),
+                                               n_splits, _stream(stream)))
 
 
 class Pool:
