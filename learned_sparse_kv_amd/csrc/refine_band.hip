@@ -44,6 +44,11 @@ namespace {
 
 using namespace lsa_dev;
 
+// max(x, +0) with +0 for every negative value and for -0: as a signed
+// integer the bit pattern of a negative float is negative (one instruction,
+// where fmaxf also quiets NaNs)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __device__ __forceinline__ uint32_t fkey(float f) {
     const uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -53,13 +58,13 @@ constexpr int kWaves = 4;         // waves per block of K1 and K3
 constexpr int kCoarse = 1024;     // coarse bins: key >> 22
 constexpr int kFine = 2048;       // fine bins inside one coarse bin: (key >> 11) & 2047
 constexpr int kHist = 2 * kCoarse + 2 * kFine;  // per request: coarse L, U, then fine L, U
-constexpr int kRedStride = 33;    // per-token row: 16 + 16 partial sums, |key|^2
 constexpr int kT = 1024, kTW = kT / 64;
 constexpr int kMaxSeg = 1024;     // band list segments (K3 blocks) per request, at most
 constexpr int kListCap = 8192;    // band entries K4 keeps in LDS
 constexpr int kUncCap = 1024;     // uncertain entries K4 ranks directly
 constexpr int kPgCap = 256;       // chunks per K3 block whose pages K3 keeps in LDS
 constexpr int kUclCap = 512;      // uncertain entries per K3 block kept in LDS
+constexpr int kRs = 64;           // uncertain entries K3 re-scores per round
 
 // ---------------------------------------------------------------------------
 template <int NW>
@@ -129,10 +134,15 @@ __device__ __forceinline__ void load_hist(const uint32_t* gh, uint32_t* lds) {
 
 // ---------------------------------------------------------------------------
 // K1.  Grid (X, B): block x of request r takes chunks x*4 + wave, stepping by
-// 4X, and prefetches the next chunk's key rows while the current one is on
-// the matrix cores.  The query operands, weights and the bound's query term
-// are set up once per block.  The block's coarse histograms go to the
-// request's (hist, zero on entry) with one atomic per nonzero bin.
+// 4X.  The query rows are the A operands (rows = heads), a chunk's key rows
+// the B operands (columns = tokens), so D = Q K^T leaves each lane four heads
+// of one token: the weighted head sum runs inside the lane and across the
+// four lane groups by two permlane swaps, with no trip through LDS.  Key rows
+// stay in flight ahead of the chunk being computed: each 16-token part of a
+// key buffer is refilled with the next chunk's part as soon as it has been
+// converted (with fp8 keys two buffers alternate, so two chunks are in
+// flight).  The block's coarse histograms go to the request's (hist, zero on
+// entry) with one atomic per nonzero bin.
 template <int KDT, int D, int H>
 __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_refine_mfma(
     GeomDev g, const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
@@ -147,8 +157,10 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
     constexpr int HB = H / 16;   // head blocks
     constexpr int NR = KDT == LSA_BF16 ? KS : KS / 2;  // 16-byte key loads per token row and lane
     constexpr int QROW = D * 2 + 16;      // bytes per query row in LDS (padded: no bank conflicts)
+    // key buffers in flight: two with fp8 keys (8 registers per 16 tokens),
+    // one with bf16 keys (16 per 16 tokens)
+    constexpr int NBUF = NR * 4 * 4 <= 32 ? 2 : 1;
     __shared__ uint32_t hl[2 * kCoarse];  // coarse L bins, then coarse U bins
-    __shared__ float red[kWaves][64 * kRedStride];
     __shared__ __attribute__((aligned(16))) uint8_t qs[H * QROW];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, lq = lane >> 4;
@@ -180,173 +192,164 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
     const int nj_max = i0 < nhr ? (nhr - i0 + stride - 1) / stride : 0;
     load_idx(0, nj_max);
     const int nc = cnt[r];
-    // the query rows load behind the index loads, once per block into LDS
-    // (each wave takes its operands from there); the first key rows load as
-    // soon as their pages are known, and the query norms are formed while
-    // the key rows are in flight
+    const int nj = i0 < nc ? (nc - i0 + stride - 1) / stride : 0;
+    // key rows: B operands of tokens tb*16 + l16, 16 bytes per load.  Each
+    // buffer carries its chunk's page base and scale, taken from the index
+    // window together: the window may move on (to the chunks 64 further)
+    // before the buffer's chunk is computed.
+    uint4 buf[NBUF][4][NR];
+    const uint8_t* bbase[NBUF];
+    float bsc[NBUF];
+    auto set_chunk = [&](int j, int b) __attribute__((always_inline)) {
+        const int src = j & 63;
+        const int64_t pgo = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pg_l, src) |
+                            ((int64_t)__builtin_amdgcn_readlane((int)(pg_l >> 32), src) << 32);
+        bbase[b] = pages + pgo * page_bytes + ikey_off;
+        bsc[b] = 1.0f;
+        if constexpr (KDT == LSA_FP8_E4M3FN)
+            bsc[b] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), src));
+    };
+    auto load_part = [&](int b, int tb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = 0; n < NR; ++n)
+            buf[b][tb][n] = *(const uint4*)(bbase[b] + (tb * 16 + l16) * ROWB + n * 64 + lq * 16);
+    };
+    // the query rows load once per block into LDS (each wave takes its
+    // operands from there)
     {
         const uint4* qr = (const uint4*)(q + (int64_t)r * H * D);
         for (int e = tid; e < H * D / 8; e += 64 * kWaves)
             *(uint4*)(qs + (e / (D / 8)) * QROW + (e % (D / 8)) * 16) = qr[e];
     }
-    float wl[HB], wa[HB];
+    // weights of the heads this lane's accumulators hold: hb*16 + 4*lq + i;
+    // and of head hb*16 + l16, whose query operands the lane holds (bound)
+    float wl[HB][4], wq_own[HB];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) wl[hb] = w[(int64_t)r * H + hb * 16 + l16];
+    for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wl[hb][e] = w[(int64_t)r * H + hb * 16 + 4 * lq + e];
+        wq_own[hb] = w[(int64_t)r * H + hb * 16 + l16];
+    }
     for (int i = tid; i < 2 * kCoarse; i += 64 * kWaves) hl[i] = 0;
     lds_barrier();
     if ((int)blockIdx.x * kWaves < nc) {  // uniform across the block
-        const int nj = i0 < nc ? (nc - i0 + stride - 1) / stride : 0;
-        uint4 qb[HB][KS];
+        uint4 qa[HB][KS];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                qb[hb][ks] = *(const uint4*)(qs + (hb * 16 + l16) * QROW + kdim<KDT>(ks, lq) * 2);
-        // key rows of chunk j: A operands of tokens tb*16 + l16 (16 bytes per
-        // load); DEPTH chunks are in flight ahead of the one computed (two
-        // where the registers allow it)
-        constexpr int DEPTH = NR * 4 * 4 <= 32 ? 2 : 1;
-        uint4 raw[4][NR], raw2[4][NR];
-        // each key buffer carries its chunk's scale, taken from the index
-        // window together with the page: the window may move on (to the
-        // chunks 64 further) before the buffer's chunk is computed
-        float sc_a = 1.0f, sc_b = 1.0f;
-        auto fetch = [&](int j, uint4 (&dst)[4][NR], float& dsc) __attribute__((always_inline)) {
-            const int src = j & 63;
-            const int64_t pgo = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pg_l, src) |
-                                ((int64_t)__builtin_amdgcn_readlane((int)(pg_l >> 32), src) << 32);
-            if constexpr (KDT == LSA_FP8_E4M3FN)
-                dsc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), src));
-            const uint8_t* base = pages + pgo * page_bytes + ikey_off;
+                qa[hb][ks] = *(const uint4*)(qs + (hb * 16 + l16) * QROW + kdim<KDT>(ks, lq) * 2);
+        // the chunks ahead of j, one per buffer, have their pages known
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
+        for (int b = 0; b < NBUF; ++b) {
+            if (b < nj) {
+                set_chunk(b, b);
 #pragma unroll
-                for (int n = 0; n < NR; ++n)
-                    dst[tb][n] = *(const uint4*)(base + (tb * 16 + l16) * ROWB + n * 64 + lq * 16);
-        };
-        if (nj > 0) {
-            fetch(0, raw, sc_a);
-            if (DEPTH == 2 && nj > 1) fetch(1, raw2, sc_b);
+                for (int tb = 0; tb < 4; ++tb) load_part(b, tb);
+            }
         }
         // Wq = sum_h |w_h| * |q_h|_2 (rounded up), from the operands held:
         // lane (l16, lq) has dims lq*8.. of every k-step of head hb*16 + l16
         float part = 0.0f;
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
-            wa[hb] = fabsf(wl[hb]);
             float ss = 0.0f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) ss += sumsq_bf16x8(qb[hb][ks]);
+            for (int ks = 0; ks < KS; ++ks) ss += sumsq_bf16x8(qa[hb][ks]);
             ss += __shfl_xor(ss, 16);
             ss += __shfl_xor(ss, 32);
-            part += wa[hb] * sqrtf(ss * (1.0f + gam(D + 8))) * (1.0f + 4 * kU2);
+            part += fabsf(wq_own[hb]) * sqrtf(ss * (1.0f + gam(D + 8))) * (1.0f + 4 * kU2);
         }
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) part += __shfl_xor(part, o);
         const float wq = part * (1.0f + gam(H + 8));
 
-        float* pr = red[wv];
-        for (int j = 0; j < nj; ++j) {
+        // one chunk from buffer b: refill each 16-token part with chunk j + NBUF's
+        // as soon as it is converted; lane = token of the chunk at the end
+        auto chunk = [&](int j, int b) __attribute__((always_inline)) {
             const int i = i0 + j * stride;
             // |key|^2 of the lane's token, formed once per window when given
             const float kn2_pre = kn2g ? kn2g[(off + i) * 64 + lane] : 0.0f;
-            uint4 ka[4][KS];
+            const float scale = bsc[b];
+            const bool more = j + NBUF < nj;
+            float mI = 0.0f, mW = 0.0f, mK = 0.0f;
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
+            for (int tb = 0; tb < 4; ++tb) {
+                uint4 ka[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    if constexpr (KDT == LSA_BF16) ka[tb][ks] = raw[tb][ks];
-                    else ka[tb][ks] = (ks & 1) ? fp8x8_to_bf16x8(raw[tb][ks >> 1].z, raw[tb][ks >> 1].w)
-                                               : fp8x8_to_bf16x8(raw[tb][ks >> 1].x, raw[tb][ks >> 1].y);
+                    if constexpr (KDT == LSA_BF16) ka[ks] = buf[b][tb][ks];
+                    else ka[ks] = (ks & 1) ? fp8x8_to_bf16x8(buf[b][tb][ks >> 1].z, buf[b][tb][ks >> 1].w)
+                                           : fp8x8_to_bf16x8(buf[b][tb][ks >> 1].x, buf[b][tb][ks >> 1].y);
                 }
-            const float scale = sc_a;
-            if constexpr (DEPTH == 2) {
-                if (j + 1 < nj) {
-#pragma unroll
-                    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                        for (int n = 0; n < NR; ++n) raw[tb][n] = raw2[tb][n];
-                    sc_a = sc_b;
-                    if (j + 2 < nj) {
-                        // the index window moves 64 chunks at a time; the
-                        // chunks in flight already hold their pages and scales
-                        if (((j + 2) & 63) == 0) load_idx(j + 2, nj);
-                        fetch(j + 2, raw2, sc_b);
+                if (more) {
+                    if (tb == 0) {
+                        // the index window moves 64 chunks at a time; the chunks
+                        // in flight already hold their pages and scales
+                        if (((j + NBUF) & 63) == 0) load_idx(j + NBUF, nj);
+                        set_chunk(j + NBUF, b);
                     }
+                    load_part(b, tb);
                 }
-            } else if (j + 1 < nj) {
-                if (((j + 1) & 63) == 0) load_idx(j + 1, nj);
-                fetch(j + 1, raw, sc_a);
-            }
-            // |key|^2 on the matrix cores (unless given): the diagonal of the
-            // 16x16 Gram block of tokens tb*16..; lane (l16, lq) holds rows
-            // 4lq..4lq+3 of column l16
-            if (!kn2g) {  // uniform
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb) {
+                // |key|^2 on the matrix cores (unless given): the diagonal of the
+                // 16x16 Gram block; lane (l16, lq) holds rows 4lq..4lq+3 of
+                // column l16, so the diagonal of column l16 sits in lane group
+                // l16 / 4, element l16 % 4
+                if (!kn2g) {  // uniform
                     f32x4_t gm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)
-                        gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, ka[tb][ks]),
-                            __builtin_bit_cast(bf16x8_t, ka[tb][ks]), gm, 0, 0, 0);
+                        gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
+                                                                     __builtin_bit_cast(bf16x8_t, ka[ks]), gm, 0, 0, 0);
                     const int e = l16 & 3;
                     const float dv = e == 0 ? gm[0] : (e == 1 ? gm[1] : (e == 2 ? gm[2] : gm[3]));
-                    if ((l16 >> 2) == lq) pr[(tb * 16 + l16) * kRedStride + 32] = dv;
+                    const float dg = __shfl(dv, (l16 >> 2) * 16 + l16);
+                    if (lq == tb) mK = dg;
                 }
-            }
-            // partial head sums per lane (heads hb*16 + l16), then through LDS
-            // to one lane per token: red[token][l16], fixed summation order
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                f32x4_t acc[HB];
+                // a'[head hb*16 + 4lq + e][token tb*16 + l16]; weighted ReLU sums
+                // over the lane's heads, then over the four lane groups
+                float sI = 0.0f, sW = 0.0f;
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) {
                     f32x4_t c4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)
-                        c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, ka[tb][ks]),
-                            __builtin_bit_cast(bf16x8_t, qb[hb][ks]), c4, 0, 0, 0);
-                    acc[hb] = c4;  // a'[token tb*16 + 4*lq + e][head hb*16 + l16]
-                }
+                        c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[hb][ks]),
+                                                                     __builtin_bit_cast(bf16x8_t, ka[ks]), c4, 0, 0, 0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float sI = 0.0f, sW = 0.0f;
-#pragma unroll
-                    for (int hb = 0; hb < HB; ++hb) {
-                        const float rr = fmaxf(acc[hb][e], 0.0f);
-                        sI = __builtin_fmaf(wl[hb], rr, sI);
-                        sW = __builtin_fmaf(wa[hb], rr, sW);
+                    for (int e = 0; e < 4; ++e) {
+                        const float rr = relu(c4[e]);
+                        sI = __builtin_fmaf(wl[hb][e], rr, sI);
+                        sW = __builtin_fmaf(fabsf(wl[hb][e]), rr, sW);
                     }
-                    const int t = tb * 16 + 4 * lq + e;
-                    pr[t * kRedStride + l16] = sI;
-                    pr[t * kRedStride + 16 + l16] = sW;
+                }
+                sI = add_xor32(add_xor16(sI));
+                sW = add_xor32(add_xor16(sW));
+                if (lq == tb) {  // lane lq * 16 + l16 keeps token tb * 16 + l16
+                    mI = sI;
+                    mW = sW;
                 }
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // lane = token of the chunk
-            float sI = 0.0f, sW = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                sI += pr[lane * kRedStride + j];
-                sW += pr[lane * kRedStride + 16 + j];
-            }
-            const float kn2 = kn2g ? kn2_pre : pr[lane * kRedStride + 32];
+            const float kn2 = kn2g ? kn2_pre : mK;
             const float kn = sqrtf(kn2 * (1.0f + gam(D + 8))) * (1.0f + 4 * kU2);
             const float ek = gam(D) * 2.0f * kn * wq;  // sum_h |w_h| eps_h
-            float E = ek + 2.0f * gam(H + 24) * (sW + ek);
-            const float Is = sI * scale;
+            float E = ek + 2.0f * gam(H + 24) * (mW + ek);
+            const float Is = mI * scale;
             E = (E * scale + 4 * kU2 * (fabsf(Is) + E * scale)) * (1.0f + 16 * kU2) + 1e-30f;
             const uint32_t kL = fkey(Is - E), kU = fkey(Is + E);
             lu[(off + i) * 64 + lane] = make_uint2(kL, kU);
             atomicAdd(&hl[kL >> 22], 1u);
             atomicAdd(&hl[kCoarse + (kU >> 22)], 1u);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();  // red[] is rewritten by the next chunk
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        };
+        if constexpr (NBUF == 2) {
+            int j = 0;
+            for (; j + 1 < nj; j += 2) {
+                chunk(j, 0);
+                chunk(j + 1, 1);
+            }
+            if (j < nj) chunk(j, 0);
+        } else {
+            for (int j = 0; j < nj; ++j) chunk(j, 0);
         }
     }
     lds_barrier();
@@ -354,7 +357,6 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
     for (int i = tid; i < 2 * kCoarse; i += 64 * kWaves)
         if (hl[i]) atomicAdd(&gh[i], hl[i]);
 }
-
 // Pages (slots) and index-key scales of the selected chunks, in selection
 // order: sel_slot[off + i] for i below the request's count, -1 from there to
 // the request's chunk count.  The window pipeline forms them once per window
@@ -544,8 +546,15 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
     constexpr int TPW = 64 / TPT;         // tokens per wave
     constexpr int EB = KDT == LSA_BF16 ? 2 : 1;
     constexpr int ROWB = D * EB;
-    __shared__ __attribute__((aligned(16))) float kf[kWaves][TPW][D];
-    __shared__ float rel[kWaves][TPW][H];
+    constexpr int G = 4;                  // tokens a lane scores at once (independent chains)
+    constexpr int PPR = ROWB / 16;        // 16-byte pieces per key row
+    constexpr int NPT = kRs * PPR / (64 * kWaves);  // row pieces per thread per round
+    static_assert(NPT * 64 * kWaves == kRs * PPR, "key rows must split evenly");
+    __shared__ __attribute__((aligned(16))) uint8_t krow[kRs][ROWB];  // key rows of a round
+    __shared__ uint64_t rrow[kRs];        // their addresses
+    __shared__ float rsc[kRs];            // their chunk scales
+    __shared__ int rent[kRs];             // their band list slots
+    __shared__ float rel[kWaves][TPW][G][H];
     __shared__ float wf[H];
     __shared__ __attribute__((aligned(16))) uint32_t hf[2 * kFine];
     __shared__ int wsum[kWaves], s_out[4];
@@ -641,19 +650,18 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
         psc[tid] = sc_v;
     }
     if (tid < H) wf[tid] = w_v;
-    // canonical scores of this block's uncertain entries
-    // the lists in global memory written above are read by other threads
-    // below (past the LDS copies): a full block barrier
+    // canonical scores of this block's uncertain entries, kRs at a time:
+    // every entry's key row comes into LDS in one round of loads, then each
+    // lane runs the element-order chains of its heads for G tokens at once
+    // (independent accumulators), and one lane per token the head sum.
+    // The lists in global memory written above are read by other threads
+    // below (past the LDS copies): a full block barrier.
     __threadfence_block();
     __syncthreads();
-    float* kr = kf[wv][ts];
-    float* rr = rel[wv][ts];
-    for (int u0 = wv * TPW; u0 < nu; u0 += kWaves * TPW) {
-        const int u = u0 + ts;
-        const bool valid = u < nu;
-        int64_t e = 0;
-        float scale = 1.0f;
-        if (valid) {
+    for (int u0 = 0; u0 < nu; u0 += kRs) {  // uniform
+        const int n = min(kRs, nu - u0);
+        if (tid < n) {
+            const int u = u0 + tid;
             int p, j;
             if (u < kUclCap) {
                 p = ucp[u];
@@ -662,8 +670,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
                 j = ul[seg + u];
                 p = bl[seg + j];
             }
-            e = seg + j;
             int64_t pg;
+            float scale = 1.0f;
             if (pg_lds) {
                 pg = pgb[(p >> 6) - c0];
                 scale = psc[(p >> 6) - c0];
@@ -677,54 +685,91 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_list(
                     if constexpr (KDT == LSA_FP8_E4M3FN) scale = ikey_scale[off + c];
                 }
             }
-            const uint8_t* row = pages + pg * page_bytes + ikey_off + (int64_t)(p & 63) * ROWB;
-            for (int e4 = lt2; e4 < D / 4; e4 += TPT) {
-                float4 x;
-                if constexpr (KDT == LSA_BF16) {
-                    const uint2 b = *(const uint2*)(row + 8 * e4);
-                    x = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
-                                    __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u));
-                } else {
-                    const uint32_t b = *(const uint32_t*)(row + 4 * e4);
-                    const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, false);
-                    const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, true);
-                    x = make_float4(lo2[0], lo2[1], hi2[0], hi2[1]);
-                }
-                *(float4*)&kr[4 * e4] = x;
+            rrow[tid] = (uint64_t)(pages + pg * page_bytes + ikey_off + (int64_t)(p & 63) * ROWB);
+            rsc[tid] = scale;
+            rent[tid] = (int)(seg + j - off * 64);
+        }
+        lds_barrier();
+        {
+            // every thread loads (rows past the round's count repeat row 0)
+            typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+            typedef const __attribute__((address_space(1))) u32x4v gu32x4;
+            uint4 v[NPT];
+#pragma unroll
+            for (int m = 0; m < NPT; ++m) {
+                const int e = tid + 64 * kWaves * m, x = e / PPR;
+                v[m] = __builtin_bit_cast(uint4, *(gu32x4*)(rrow[x < n ? x : 0] + (e % PPR) * 16));
+            }
+#pragma unroll
+            for (int m = 0; m < NPT; ++m) {
+                const int e = tid + 64 * kWaves * m, x = e / PPR;
+                if (x < n) *(uint4*)&krow[x][(e % PPR) * 16] = v[m];
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (valid) {
+        lds_barrier();
+        for (int x0 = 0; x0 < n; x0 += kWaves * TPW * G) {  // uniform
+            // token of group g: x0 + (wv * TPW + ts) + kWaves * TPW * g
+            float a[G][HPT];
 #pragma unroll
-            for (int j = 0; j < HPT; ++j) {
-                float a = 0.0f;
+            for (int gg = 0; gg < G; ++gg)
 #pragma unroll
-                for (int i = 0; i < D; i += 4) {
-                    const float4 x = *(const float4*)&kr[i];
-                    const uint32_t q01 = qp[j][i / 2], q23 = qp[j][i / 2 + 1];
-                    a = __builtin_fmaf(__uint_as_float(q01 << 16), x.x, a);
-                    a = __builtin_fmaf(__uint_as_float(q01 & 0xffff0000u), x.y, a);
-                    a = __builtin_fmaf(__uint_as_float(q23 << 16), x.z, a);
-                    a = __builtin_fmaf(__uint_as_float(q23 & 0xffff0000u), x.w, a);
+                for (int jh = 0; jh < HPT; ++jh) a[gg][jh] = 0.0f;
+            int xs[G];
+#pragma unroll
+            for (int gg = 0; gg < G; ++gg) xs[gg] = min(x0 + wv * TPW + ts + kWaves * TPW * gg, kRs - 1);
+#pragma unroll
+            for (int i = 0; i < D; i += 4) {
+#pragma unroll
+                for (int gg = 0; gg < G; ++gg) {
+                    float k4[4];
+                    if constexpr (KDT == LSA_BF16) {
+                        const uint2 bb = *(const uint2*)&krow[xs[gg]][2 * i];
+                        k4[0] = __uint_as_float(bb.x << 16);
+                        k4[1] = __uint_as_float(bb.x & 0xffff0000u);
+                        k4[2] = __uint_as_float(bb.y << 16);
+                        k4[3] = __uint_as_float(bb.y & 0xffff0000u);
+                    } else {
+                        const uint32_t bb = *(const uint32_t*)&krow[xs[gg]][i];
+                        const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)bb, false);
+                        const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)bb, true);
+                        k4[0] = lo2[0];
+                        k4[1] = lo2[1];
+                        k4[2] = hi2[0];
+                        k4[3] = hi2[1];
+                    }
+#pragma unroll
+                    for (int jh = 0; jh < HPT; ++jh) {
+                        const uint32_t q01 = qp[jh][i / 2], q23 = qp[jh][i / 2 + 1];
+                        a[gg][jh] = __builtin_fmaf(__uint_as_float(q01 << 16), k4[0], a[gg][jh]);
+                        a[gg][jh] = __builtin_fmaf(__uint_as_float(q01 & 0xffff0000u), k4[1], a[gg][jh]);
+                        a[gg][jh] = __builtin_fmaf(__uint_as_float(q23 << 16), k4[2], a[gg][jh]);
+                        a[gg][jh] = __builtin_fmaf(__uint_as_float(q23 & 0xffff0000u), k4[3], a[gg][jh]);
+                    }
                 }
-                rr[lt2 + TPT * j] = a > 0.0f ? a : 0.0f;
             }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (valid && lt2 == 0) {
-            float I = 0.0f;
+#pragma unroll
+            for (int gg = 0; gg < G; ++gg)
+#pragma unroll
+                for (int jh = 0; jh < HPT; ++jh) rel[wv][ts][gg][lt2 + TPT * jh] = a[gg][jh] > 0.0f ? a[gg][jh] : 0.0f;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // head sums, in head order: lane lt2 = g of the slot takes token g
+            if (lt2 < G) {
+                const int x = x0 + wv * TPW + ts + kWaves * TPW * lt2;
+                if (x < n) {
+                    float I = 0.0f;
 #pragma unroll 8
-            for (int h = 0; h < H; ++h) I = __builtin_fmaf(wf[h], rr[h], I);
-            if constexpr (KDT == LSA_FP8_E4M3FN) I = I * scale;
-            bk[e] = fkey(I);
+                    for (int h = 0; h < H; ++h) I = __builtin_fmaf(wf[h], rel[wv][ts][lt2][h], I);
+                    if constexpr (KDT == LSA_FP8_E4M3FN) I = I * rsc[x];
+                    bk[off * 64 + rent[x]] = fkey(I);
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();  // rel is rewritten by the next tokens
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();  // kf / rel are rewritten next round
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        lds_barrier();  // krow and the entry arrays are rewritten by the next round
     }
 }
 
