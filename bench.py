@@ -297,8 +297,15 @@ def policy_comparison(inp, n_time=8, mass_steps=64, boost=2.5):
     lsa.lsa_timing_enable(False)
     n_ml, ms_ml = lsa.lsa_timing_read("k_chunk_ml")
     lsa.lsa_timing_reset()
-    ml_bytes = mass_steps * int(np.sum(f["seq_len"])) * 1152  # key bytes of every row, per step
-    ml_gbs = ml_bytes / (ms_ml * 1e-3) / 1e9
+    # the pass scores every row of the context against every step's 64 query
+    # heads: 2 * Hq * Dk flop per (row, step) on the matrix cores, and it reads
+    # each row once per step (the rows of one request fit the caches between
+    # steps, so these are not HBM bytes: the distinct bytes are one pass)
+    tokens = int(np.sum(f["seq_len"]))
+    ml_flops = 2.0 * cfg.Hq * cfg.Dk * tokens * mass_steps
+    ml_stream = mass_steps * tokens * cfg.Dk * 2
+    ml_unique = tokens * cfg.kv_row_bytes
+    ml_tflops = ml_flops / (ms_ml * 1e-3) / 1e12
     share = lambda n, pct: (n * pct + 99) // 100
     pols = {}
     _, sel, cnt = dev.score_select(theta=0.0, window=0)
@@ -316,8 +323,11 @@ def policy_comparison(inp, n_time=8, mass_steps=64, boost=2.5):
            "attention_focus_boost": boost, "mass_steps": mass_steps,
            "history_mass_share": round(hist_mass / (hist_mass + rec_total), 4),
            "chunk_mass_pass": {"k_chunk_ml_ms": round(ms_ml / max(n_ml, 1), 3), "launches": n_ml,
-                               "alg_bytes": ml_bytes, "gbs": round(ml_gbs, 1),
-                               "pct_peak": round(100 * ml_gbs / HBM_PEAK_GBS, 1)},
+                               "bound": "mfma", "tflop": round(ml_flops / 1e12, 2),
+                               "tflops": round(ml_tflops, 1),
+                               "pct_mfma_bf16_peak": round(100 * ml_tflops / MFMA_BF16_PEAK_TFLOPS, 1),
+                               "unique_bytes": ml_unique, "unique_gbs": round(ml_unique / (ms_ml * 1e-3) / 1e9, 1),
+                               "row_bytes_streamed": ml_stream},
            "policies": {}}
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for name, (sel, cnt) in pols.items():
@@ -351,6 +361,50 @@ def policy_comparison(inp, n_time=8, mass_steps=64, boost=2.5):
     torch.cuda.empty_cache()
     out["seconds"] = round(time.perf_counter() - t0, 1)
     return out
+
+
+def window_rate(cfg, n_layers=1, warmup=3, windows=6, steps=64):
+    """Decode steps per second of lsa_step64 windows on one workload (inputs
+    generated here, cold tier as the config says), with n_layers indexer
+    layers selecting their OR union at every trigger.  Wall clock over the
+    timed windows, bracketed by device synchronisation."""
+    import numpy as np
+    import torch
+    from learned_sparse_kv_amd import runner, synth
+    t0 = time.perf_counter()
+    cfg = synth.dataclasses.replace(cfg, windows=warmup + windows + 2, drift=0.02 if cfg.drift == 0 else cfg.drift)
+    inp = synth.generate(cfg, steps=steps, threads=16)
+    gen_s = time.perf_counter() - t0
+    dev = runner.DeviceInputs(inp)
+    pipe = runner.Pipeline(dev, n_layers=n_layers)
+    B = cfg.batch
+    out = torch.empty((steps, B, cfg.Hq, cfg.Dv), dtype=torch.int16, device="cuda")
+    _, cnt = pipe.prime()
+    m = 0
+    for _ in range(warmup):
+        pipe.window(m, 0, steps, out)
+        m += 1
+    torch.cuda.synchronize()
+    cnts = []
+    t1 = time.perf_counter()
+    for _ in range(windows):
+        _, c = pipe.window(m, 0, steps, out)
+        cnts.append(c)
+        m += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+    pipe.close()
+    res = {"workload": cfg.name, "batch": B, "contexts": [int(x) for x in inp["seq_len"]],
+           "index_keys": {0: "f32", 1: "bf16", 2: "fp8_e4m3fn"}[cfg.idx_dtype], "indexer_layers": n_layers,
+           "cold_tier": "pinned host" if cfg.host_cold else "HBM", "windows_timed": windows,
+           "decode_steps_per_s": round(steps * windows / wall, 1),
+           "tokens_per_s": round(B * steps * windows / wall, 1),
+           "ms_per_window": round(wall * 1e3 / windows, 3),
+           "selected_chunks_per_request": round(float(np.mean(cnts)), 1),
+           "generate_s": round(gen_s, 1)}
+    del pipe, dev, inp
+    torch.cuda.empty_cache()
+    return res
 
 
 def growing_decode(inp, n_windows=4):
@@ -485,6 +539,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sustained", action="store_true",
                     help="skip the cold-cache scoring / attention GB/s points at 128K and 500K")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the decode steps/s of the 128K workloads and of the three-layer union")
     ap.add_argument("--no-growing", action="store_true",
                     help="skip the growing-context decode (append per step, chunk commit per window)")
     ap.add_argument("--no-policies", action="store_true",
@@ -679,6 +735,16 @@ def main():
         log(f"[bench] sustained points in {time.perf_counter() - t0:.1f}s: "
             + json.dumps({"scoring": result["scoring_sustained"],
                           "attention": result["attention_sustained"]}))
+    if not args.no_workloads:
+        # decode steps/s at 128K (the ragged 32K-128K batch of 16 and the same
+        # batch at 131,072 tokens each) and the pages' three-layer union at 500K
+        t0 = time.perf_counter()
+        result["decode_steps_128k"] = [window_rate(synth.config(2)), window_rate(synth.config_2u())]
+        # the union of three layers selects about 1 - 0.9^3 = 27 % of the
+        # chunks: a pool with room for two windows' selections
+        result["union3_window"] = window_rate(synth.dataclasses.replace(cfg, slots_per_req=3072), n_layers=3)
+        log(f"[bench] other workloads in {time.perf_counter() - t0:.1f}s: "
+            + json.dumps({"128k": result["decode_steps_128k"], "union3": result["union3_window"]}))
     if not args.no_policies:
         result["policy_comparison"] = policy_comparison(inp)
         log("[bench] policies: " + json.dumps(result["policy_comparison"]))

@@ -411,7 +411,11 @@ lsa_status lsa_gather_kv(lsa_pool* pool, const int32_t* sel_ids, const int32_t* 
  * (refine + top-k + attention per step) on main_stream while it scores the
  * next window (if given), fetches its missing chunks on copy_stream, and
  * builds its page table.  One window ahead, so a window's refill overlaps
- * the previous window's steps.
+ * the previous window's steps.  With n_layers > 1 each trigger scores every
+ * layer's KIComp against that layer's query (one lsa_trigger_in per layer)
+ * and selects the OR union of their selections, as lsa_score_chunks_union
+ * followed by lsa_select_threshold does (cjcn.com.cn explainer, section 四;
+ * gist.science summary, section 2.4).
  * ---------------------------------------------------------------------- */
 typedef struct lsa_ctx lsa_ctx;
 
@@ -427,6 +431,9 @@ typedef struct {
     lsa_pool* pool;           /* slot pool (its cold tier holds the pages)    */
     void* ws;                 /* (device) >= lsa_ctx_ws_bytes(desc) bytes     */
     size_t ws_bytes;
+    int32_t n_layers;         /* indexer layers whose OR union each trigger
+                                 selects (the pages' inference configuration
+                                 runs three), 1..LSA_MAX_LAYERS; 0 means 1    */
 } lsa_ctx_desc;
 
 typedef struct {
@@ -442,7 +449,8 @@ typedef struct {
     const void* q_refine;     /* (device) [steps, B, H, d] q_dt               */
     const float* w_refine;    /* (device) [steps, B, H]                        */
     const void* q_attn;       /* (device) [steps, B, Hq, Dk] kv dtype          */
-    const lsa_trigger_in* next; /* next window's trigger, or NULL (last window) */
+    const lsa_trigger_in* next; /* (host) next window's trigger, one per indexer
+                                   layer (n_layers of them), or NULL (last window) */
 } lsa_window_in;
 
 typedef struct {
@@ -457,7 +465,8 @@ typedef struct {
 size_t lsa_ctx_ws_bytes(const lsa_ctx_desc* desc);
 lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc);
 void lsa_ctx_destroy(lsa_ctx* ctx);
-/* Score, select and fetch the first window (synchronous on the host). */
+/* Score, select and fetch the first window (synchronous on the host);
+ * first points to one lsa_trigger_in per indexer layer. */
 lsa_status lsa_ctx_prime(lsa_ctx* ctx, const lsa_trigger_in* first, void* main_stream,
                          void* copy_stream, lsa_window_out* out);
 lsa_status lsa_step64(lsa_ctx* ctx, const lsa_window_in* in, lsa_window_out* out,

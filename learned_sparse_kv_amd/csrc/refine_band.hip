@@ -65,6 +65,7 @@ constexpr int kUncCap = 1024;     // uncertain entries K4 ranks directly
 constexpr int kPgCap = 256;       // chunks per K3 block whose pages K3 keeps in LDS
 constexpr int kUclCap = 512;      // uncertain entries per K3 block kept in LDS
 constexpr int kRs = 64;           // uncertain entries K3 re-scores per round
+constexpr int kSelCap = 8192;     // selected chunk ids K4 keeps in LDS
 
 // ---------------------------------------------------------------------------
 template <int NW>
@@ -795,14 +796,18 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
     __shared__ __attribute__((aligned(16))) uint64_t uval[kUncCap];  // (key, ~position): larger ranks first
     __shared__ int32_t uj[kUncCap];
     __shared__ int boff[kMaxSeg + 1];
+    __shared__ int32_t ssel[kSelCap];  // the request's selected chunk ids
     __shared__ int wsum[kTW];
     __shared__ uint32_t s_prefix;
     __shared__ int s_remaining, s_eq, s_u;
     const int r = blockIdx.x, tid = threadIdx.x;
     const int64_t off = g.chunk_off[r];
-    // the count and the K3 block counts load at once
+    // the count, the K3 block counts and the selected chunk ids (all the
+    // request's chunk slots, before the count is known) load at once
     const int nc = cnt[r];
     const int v_scnt = tid < X ? scnt[(int64_t)r * X + tid] : 0;
+    const int nsl = min(g.nhist[r], kSelCap);
+    for (int i = tid; i < nsl; i += kT) ssel[i] = sel[g.chunk_off[r] + i];
     // the request's histograms were last read by the previous kernel: clear
     // them for the next launch
     for (int i = tid; i < kHist; i += kT) bhist[(int64_t)r * kHist + i] = 0;
@@ -838,6 +843,7 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
         pos = bl[e];
     };
     const int32_t* sl = sel + off;
+    auto sel_of = [&](int i) -> int32_t { return i < kSelCap ? ssel[i] : sl[i]; };
     int32_t* out = topk + (int64_t)r * k;
     if (in_lds) {
         if (tid == 0) s_u = 0;
@@ -918,7 +924,7 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
             for (int j = j0; j < j1; ++j) tc += lkey[j] == 0xffffffffu;
             int o = block_scan<kTW>(tc, wsum, tot);
             for (int j = j0; j < j1; ++j)
-                if (lkey[j] == 0xffffffffu) out[o++] = sl[lpos[j] >> 6] * 64 + (lpos[j] & 63);
+                if (lkey[j] == 0xffffffffu) out[o++] = sel_of(lpos[j] >> 6) * 64 + (lpos[j] & 63);
             if (tid == 0) tcnt[r] = tot;
             return;
         }
@@ -1000,7 +1006,7 @@ __global__ __launch_bounds__(kT) void k_topk_band(GeomDev g, const int32_t* __re
         int o = base + block_scan<kTW>(tc, wsum, tot);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (take[j]) out[o++] = sl[pos[j] >> 6] * 64 + (pos[j] & 63);
+            if (take[j]) out[o++] = sel_of(pos[j] >> 6) * 64 + (pos[j] & 63);
         base += tot;
     }
     if (tid == 0) tcnt[r] = base;

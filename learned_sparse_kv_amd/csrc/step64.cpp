@@ -85,16 +85,26 @@ size_t layout(const lsa_ctx_desc* d, GeomDev* g, AttnPlan* plan, size_t offs[15]
     return c.off;
 }
 
+int n_layers_of(const lsa_ctx_desc& d) { return d.n_layers > 1 ? d.n_layers : 1; }
+
+// Scores every indexer layer into z (later layers keep the per-chunk maximum,
+// so z > theta exactly when some layer's logit is), then selects.
 lsa_status score_select(lsa_ctx* x, const lsa_trigger_in* t, int buf, hipStream_t s) {
     const lsa_ctx_desc& d = x->d;
-    if (!t || !t->q || !t->w || !t->bias) return LSA_ERR_INVALID_ARG;
-    if (x->nh > 0 && !t->kic) return LSA_ERR_INVALID_ARG;
-    if (x->nh > 0 && d.idx_dt == LSA_FP8_E4M3FN && !t->kic_scale) return LSA_ERR_INVALID_ARG;
-    if (launch_fuse_query(x->g, t->q, d.q_dt, t->w, d.H, d.d, x->qbar, s) != hipSuccess)
-        return LSA_ERR_HIP;
-    if (launch_score(x->g, t->kic, d.idx_dt, t->kic_scale, x->qbar, t->bias, d.d, x->z, s) !=
-        hipSuccess)
-        return LSA_ERR_HIP;
+    const int nl = n_layers_of(d);
+    if (!t) return LSA_ERR_INVALID_ARG;
+    for (int l = 0; l < nl; ++l) {
+        if (!t[l].q || !t[l].w || !t[l].bias) return LSA_ERR_INVALID_ARG;
+        if (x->nh > 0 && !t[l].kic) return LSA_ERR_INVALID_ARG;
+        if (x->nh > 0 && d.idx_dt == LSA_FP8_E4M3FN && !t[l].kic_scale) return LSA_ERR_INVALID_ARG;
+    }
+    for (int l = 0; l < nl; ++l) {
+        if (launch_fuse_query(x->g, t[l].q, d.q_dt, t[l].w, d.H, d.d, x->qbar, s) != hipSuccess)
+            return LSA_ERR_HIP;
+        if (launch_score(x->g, t[l].kic, d.idx_dt, t[l].kic_scale, x->qbar, t[l].bias, d.d, x->z, s,
+                         l > 0) != hipSuccess)
+            return LSA_ERR_HIP;
+    }
     if (launch_select(x->g, x->z, d.theta, x->sel[buf], x->cnt[buf], s) != hipSuccess)
         return LSA_ERR_HIP;
     if (x->nh > 0 && hipMemcpyAsync(x->h_sel[buf], x->sel[buf], (size_t)x->nh * 4,
@@ -128,6 +138,7 @@ lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc) {
     if (st != LSA_OK) return st;
     if (desc->d != 64 && desc->d != 128) return LSA_ERR_UNSUPPORTED;
     if (desc->H < 1 || desc->H > 128 || desc->k < 1 || desc->Hq < 1) return LSA_ERR_INVALID_ARG;
+    if (desc->n_layers < 0 || desc->n_layers > LSA_MAX_LAYERS) return LSA_ERR_INVALID_ARG;
     if (desc->q_dt != LSA_F32 && desc->q_dt != LSA_BF16) return LSA_ERR_UNSUPPORTED;
     if (!desc->pool || !desc->recent || !desc->ws || ((uintptr_t)desc->ws & 15u))
         return LSA_ERR_INVALID_ARG;

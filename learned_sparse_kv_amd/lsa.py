@@ -54,7 +54,7 @@ class lsa_ctx_desc(C.Structure):
                 ("idx_dt", C.c_int), ("Hq", C.c_int32), ("k", C.c_int32),
                 ("kv", lsa_kv_layout), ("sm_scale", C.c_float), ("theta", C.c_float),
                 ("recent", C.c_void_p), ("ikey_scale", C.c_void_p), ("pool", C.c_void_p),
-                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t)]
+                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t), ("n_layers", C.c_int32)]
 
 
 class lsa_trigger_in(C.Structure):
@@ -333,6 +333,15 @@ def _event(e):
     return int(e)
 
 
+def trigger_ptr(trig):
+    """Pointer to the first lsa_trigger_in of a struct or of an array of them."""
+    if trig is None:
+        return None
+    if isinstance(trig, lsa_trigger_in):
+        return C.pointer(trig)
+    return C.cast(trig, C.POINTER(lsa_trigger_in))
+
+
 class Ctx:
     """lsa_ctx_create / lsa_ctx_prime / lsa_step64 / lsa_ctx_destroy."""
 
@@ -342,10 +351,11 @@ class Ctx:
         _check("lsa_ctx_create", _lib.lsa_ctx_create(C.byref(h), C.byref(desc)))
         self.h = h
 
-    def prime(self, trig: lsa_trigger_in, main=None, copy=None, sel_cnt=None):
+    def prime(self, trig, main=None, copy=None, sel_cnt=None):
+        """trig: one lsa_trigger_in, or a ctypes array of one per indexer layer."""
         out = lsa_window_out()
         out.sel_cnt = _ptr(sel_cnt)
-        _check("lsa_ctx_prime", _lib.lsa_ctx_prime(self.h, C.byref(trig), _stream(main),
+        _check("lsa_ctx_prime", _lib.lsa_ctx_prime(self.h, trigger_ptr(trig), _stream(main),
                                                    _stream(copy), C.byref(out)))
         return out.stats.as_dict()
 

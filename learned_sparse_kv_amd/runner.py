@@ -164,9 +164,16 @@ def out_to_f32(out: torch.Tensor, cfg) -> np.ndarray:
 class Pipeline:
     """The window pipeline (lsa_ctx_* / lsa_step64) over DeviceInputs."""
 
-    def __init__(self, dev: DeviceInputs, k=None, slots_per_req=None, theta=0.0):
+    def __init__(self, dev: DeviceInputs, k=None, slots_per_req=None, theta=0.0, n_layers=1):
         cfg = dev.cfg
         self.dev, self.cfg = dev, cfg
+        self.n_layers = n_layers
+        # indexer layers beyond the inputs' own (the same for every window)
+        self.extra_layers = []
+        if n_layers > 1:
+            for lay in synth.indexer_layers(dev.inp, n_layers)[1:]:
+                self.extra_layers.append({key: _dev(np.ascontiguousarray(v), dev.device)
+                                          for key, v in lay.items()})
         self.k = cfg.topk if k is None else k
         spr = cfg.slots_per_req if slots_per_req is None else slots_per_req
         spr = max(1, min(spr, max(int(dev.inp["n_hist"].max()), 1)))
@@ -184,6 +191,7 @@ class Pipeline:
         desc.recent = dev.recent.data_ptr()
         desc.ikey_scale = dev.ikey_scale.data_ptr()
         desc.pool = self.pool.h.value
+        desc.n_layers = n_layers
         nbytes = lsa.lsa_ctx_ws_bytes(desc)
         if nbytes == 0:
             raise lsa.LsaError("lsa_ctx_ws_bytes", -1)
@@ -193,11 +201,19 @@ class Pipeline:
         self.copy_stream = torch.cuda.Stream(device=dev.device)
         self.sel_cnt = np.zeros(cfg.batch, dtype=np.int32)
 
-    def trigger(self, window: int) -> lsa.lsa_trigger_in:
+    def trigger(self, window: int):
+        """The window's trigger: one lsa_trigger_in per indexer layer (the
+        inputs' own indexer first, with that window's KIComp)."""
         d = self.dev
         w = window % len(d.kic)
-        return lsa.lsa_trigger_in(d.kic[w].data_ptr(), d.kic_scale[w].data_ptr(),
-                                  d.q_coarse.data_ptr(), d.w_coarse.data_ptr(), d.bias.data_ptr())
+        trig = (lsa.lsa_trigger_in * self.n_layers)()
+        trig[0] = lsa.lsa_trigger_in(d.kic[w].data_ptr(), d.kic_scale[w].data_ptr(),
+                                     d.q_coarse.data_ptr(), d.w_coarse.data_ptr(), d.bias.data_ptr())
+        for l, lay in enumerate(self.extra_layers, start=1):
+            trig[l] = lsa.lsa_trigger_in(lay["kic"].data_ptr(), lay["kic_scale"].data_ptr(),
+                                         lay["q_coarse"].data_ptr(), lay["w_coarse"].data_ptr(),
+                                         lay["bias"].data_ptr())
+        return trig
 
     def prime(self, main=None):
         self._trig0 = self.trigger(0)
@@ -213,8 +229,7 @@ class Pipeline:
         qr = d.q_refine[step0:step0 + steps]
         wr = d.w_refine[step0:step0 + steps]
         qa = d.q_attn[step0:step0 + steps]
-        win = lsa.lsa_window_in(steps, qr.data_ptr(), wr.data_ptr(), qa.data_ptr(),
-                                C.pointer(nxt) if nxt is not None else None)
+        win = lsa.lsa_window_in(steps, qr.data_ptr(), wr.data_ptr(), qa.data_ptr(), lsa.trigger_ptr(nxt))
         wo = lsa.lsa_window_out()
         wo.out = out.data_ptr()
         wo.lse = lse.data_ptr() if lse is not None else None

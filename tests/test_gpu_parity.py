@@ -252,14 +252,17 @@ def test_topk_k1_and_k_exceeding_candidates():
             assert np.array_equal(got, want), (k, r)
 
 
-@pytest.mark.parametrize("host_cold,variant", [(False, "band"), (True, "band"), (True, "valu")])
+@pytest.mark.parametrize("host_cold,variant", [(False, "band"), (True, "band"), (True, "valu"),
+                                               (True, "union3")])
 def test_window_pipeline_matches_oracle(host_cold, variant):
     """lsa_step64 over three windows with drift: per-window outputs and
     per-fetch copy counts against the oracle and the pool simulation.  The
     "valu" variant (8 indexer heads, bf16 keys, signed head weights) takes the
-    pipeline's vector-ALU refine instead of the matrix-core band."""
+    pipeline's vector-ALU refine instead of the matrix-core band; "union3"
+    selects, at every trigger, the OR union over three indexer layers."""
     R = _runner()
-    if variant == "band":
+    n_layers = 3 if variant == "union3" else 1
+    if variant in ("band", "union3"):
         cfg = synth.small_config("pipe", 31, (12000, 7000), window=1024, idx=FP8, H=16, topk=256,
                                  steps=6, planted=0.10)
     else:
@@ -269,7 +272,7 @@ def test_window_pipeline_matches_oracle(host_cold, variant):
                                     slots_per_req=80)
     inp = synth.generate(cfg)
     dev = R.DeviceInputs(inp)
-    pipe = R.Pipeline(dev)
+    pipe = R.Pipeline(dev, n_layers=n_layers)
     B, S = cfg.batch, 2  # two steps per window
     st0, cnt0 = pipe.prime()
     sels, fetched = [], [st0["fetched"]]
@@ -287,7 +290,10 @@ def test_window_pipeline_matches_oracle(host_cold, variant):
     tol, _ = tol_of(cfg)
     for m in range(windows):
         o = oracle.Oracle(inp, kic=inp["kic_windows"][m], kic_scale=inp["kic_scale_windows"][m])
-        _, sel_o, cnt_o = o.score_select()
+        if n_layers > 1:
+            _, sel_o, cnt_o = o.score_select_union(synth.indexer_layers(inp, n_layers, window=m))
+        else:
+            _, sel_o, cnt_o = o.score_select()
         for r in range(B):
             a = int(inp["chunk_off"][r])
             per_req_sets[r].append(set(sel_o[a:a + cnt_o[r]].tolist()))
