@@ -19,7 +19,6 @@ Prints one JSON line:
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -76,23 +75,6 @@ def kernel_work(name, cfg, inp, sel_cnt, k, tcnt_total, B):
     return 0, 0
 
 
-def source_hash(names):
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "learned_sparse_kv_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-KERNEL_SOURCE = {"k_refine": ["refine_topk.hip"], "k_topk": ["refine_topk.hip"],
-                 "k_refine_mfma": ["refine_band.hip"], "k_band_fine": ["refine_band.hip"],
-                 "k_key_norm2": ["refine_band.hip"], "k_resolve_sel": ["refine_band.hip"],
-                 "k_band_list": ["refine_band.hip"], "k_topk_band": ["refine_band.hip"],
-                 "k_attn_mla": ["attn_decode.hip"], "k_attn_f32": ["attn_decode.hip"],
-                 "k_attn_merge": ["attn_decode.hip"], "k_score": ["score_select.hip"],
-                 "k_select": ["score_select.hip"], "k_gather": ["gather.hip"]}
-
-
 def traffic_for(kernel, workload, launches_per_window):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source (else None)."""
@@ -102,7 +84,8 @@ def traffic_for(kernel, workload, launches_per_window):
     with open(path) as f:
         t = json.load(f)
     e = t.get(workload, {}).get(kernel)
-    if not e or e.get("source_hash") != source_hash(KERNEL_SOURCE.get(kernel, [])):
+    from learned_sparse_kv_amd.profsum import KERNEL_SOURCE, source_hash
+    if not e or kernel not in KERNEL_SOURCE or e.get("source_hash") != source_hash(KERNEL_SOURCE[kernel]):
         return None
     return e.get("bytes_per_launch")
 
@@ -547,6 +530,8 @@ def main():
                     help="skip the comparison policies (recency-only, random 10 %%, attention-mass top shares)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
+    ap.add_argument("--mfma-calibration", action="store_true",
+                    help="also run a bf16 8192^3 GEMM (what matrix-core-bound reads on the counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -712,6 +697,21 @@ def main():
             bb.copy_(a)
         torch.cuda.synchronize()
         del a, bb
+    if args.mfma_calibration:
+        n = 8192
+        a = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+        bb = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+        cc = torch.mm(a, bb)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            torch.mm(a, bb, out=cc)
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / 3
+        result["mfma_calibration"] = {"gemm": f"bf16 {n}x{n}x{n}", "avg_us": round(sec * 1e6, 1),
+                                      "tflops": round(2 * n ** 3 / sec / 1e12, 1)}
+        del a, bb, cc
     pipe.close()
     del pipe, dev
     torch.cuda.empty_cache()

@@ -416,6 +416,33 @@ lsa_status lsa_gather_kv(lsa_pool* pool, const int32_t* sel_ids, const int32_t* 
  * and selects the OR union of their selections, as lsa_score_chunks_union
  * followed by lsa_select_threshold does (cjcn.com.cn explainer, section 四;
  * gist.science summary, section 2.4).
+ *
+ * Growing context (growing != 0).  Decode adds one token per step and, as
+ * the context grows, the recent region's oldest full chunk joins the history
+ * at each trigger (cjcn.com.cn explainer, section 二).  The geometry then
+ * needs chunk_cap > 0 and recent_cap >= 2 * Rmax, where
+ *     Rmax = max(W + 63, max_r R_r) + 64
+ * bounds the recent rows of a request during any window (R_r as given).
+ * For window m (steps s, L_r and rs_r as lsa_ctx_state reports at the call):
+ *   - request r commits chunk N_r = rs_r / C iff R_r + s >= W + C; its
+ *     KV rows are recent tokens [rs_r, rs_r + C), already present;
+ *   - the next trigger (in->next) scores the history with the chunks
+ *     committed in this window included, so the pages of those chunks are
+ *     written at the start of the call: KV rows from the recent region,
+ *     in->commit_ikeys[r] at kv.ikey_off, in->commit_ikey_scale[r] into
+ *     desc->ikey_scale (fp8) -- the library writes the pool's cold tier
+ *     and desc->ikey_scale, which the caller keeps writable;
+ *   - the caller writes each committing chunk's KIComp row (and fp8 scale)
+ *     into the next trigger's kic arrays, row chunk_off[r] + N_r of every
+ *     layer, before the call (on main_stream or earlier);
+ *   - step j appends in->new_rows[j][r] as token L_r + j of request r and
+ *     attends over the grown recent region (desc->recent is written too);
+ *   - at the window's end a committing request's history boundary moves to
+ *     rs_r + C: those rows leave the recent region and are attended from
+ *     then on only when a later trigger selects their chunk.
+ * The recent rows of request r slide inside its recent_cap rows (the row
+ * of token t is r * recent_cap + recent_first_r + t - rs_r); when a window
+ * would run past the end they move back to the start, in one copy.
  * ---------------------------------------------------------------------- */
 typedef struct lsa_ctx lsa_ctx;
 
@@ -434,6 +461,7 @@ typedef struct {
     int32_t n_layers;         /* indexer layers whose OR union each trigger
                                  selects (the pages' inference configuration
                                  runs three), 1..LSA_MAX_LAYERS; 0 means 1    */
+    int32_t growing;          /* nonzero: growing context (see above)          */
 } lsa_ctx_desc;
 
 typedef struct {
@@ -451,6 +479,12 @@ typedef struct {
     const void* q_attn;       /* (device) [steps, B, Hq, Dk] kv dtype          */
     const lsa_trigger_in* next; /* (host) next window's trigger, one per indexer
                                    layer (n_layers of them), or NULL (last window) */
+    /* growing context only (else ignored):                                    */
+    const void* new_rows;     /* (device) [steps, B, row_bytes] appended tokens */
+    const void* commit_ikeys; /* (device) [B, C, d] idx_dt: index keys of the
+                                 chunk each committing request moves to its
+                                 history (rows of other requests unread)     */
+    const float* commit_ikey_scale; /* (device) [B] fp8 index keys, else NULL */
 } lsa_window_in;
 
 typedef struct {
@@ -471,6 +505,13 @@ lsa_status lsa_ctx_prime(lsa_ctx* ctx, const lsa_trigger_in* first, void* main_s
                          void* copy_stream, lsa_window_out* out);
 lsa_status lsa_step64(lsa_ctx* ctx, const lsa_window_in* in, lsa_window_out* out,
                       void* main_stream, void* copy_stream);
+/* The context's lengths as of now (host arrays [B], each may be NULL):
+ * seq_len L_r, hist_tokens rs_r and recent_first_r (the recent region's
+ * first row within request r's recent_cap rows; 0 without growing).  A
+ * growing window that would take a history past chunk_cap returns
+ * LSA_ERR_CAPACITY from lsa_step64 before it launches anything. */
+lsa_status lsa_ctx_state(const lsa_ctx* ctx, int32_t* seq_len, int32_t* hist_tokens,
+                         int32_t* recent_first);
 
 /* ------------------------------------------------------------------------
  * Diagnostics: per-kernel timing.  While enabled, every kernel the library
@@ -480,7 +521,8 @@ lsa_status lsa_step64(lsa_ctx* ctx, const lsa_window_in* in, lsa_window_out* out
  * k_score, k_select, k_refine, k_topk, k_refine_mfma, k_band_fine,
  * k_band_list, k_topk_band, k_attn_mla, k_attn_f32, k_attn_merge,
  * k_gather, k_stream_read, k_score_sig, k_select_ranked, k_chunk_ml, k_append_kv,
- * k_commit_chunk, k_resolve_sel, k_key_norm2), the number of timed launches and
+ * k_commit_chunk, k_commit_page, k_compact_recent, k_resolve_sel, k_key_norm2), the
+ * number of timed launches and
  * their summed duration in
  * milliseconds since the last reset.  lsa_timing_only(name) restricts the
  * timing to that one kernel (NULL: all; a name of 64 or more characters is

@@ -68,6 +68,15 @@ lsa_status geom_derive(const lsa_geom* g, GeomDev* d) {
     return LSA_OK;
 }
 
+void geom_retile(GeomDev* d) {
+    int32_t to = 0;
+    for (int r = 0; r < d->B; ++r) {
+        d->tile_off[r] = to;
+        to += (d->nhist[r] + 63) / 64;
+    }
+    d->tile_off[d->B] = to;
+}
+
 extern "C" {
 
 const char* lsa_status_str(lsa_status s) {

@@ -57,7 +57,64 @@ __global__ void k_commit_chunk(GeomDev g, int64_t row_bytes, int64_t page_bytes,
     }
 }
 
+// Grid (X, B).  The window pipeline's commit (growing context): request r
+// with f.on[r] moves chunk nhist[r] into its history ahead of the window's
+// end, so that the next trigger can score it: recent rows [0, 64) (rows
+// rec_off[r] ..) to the KV part of cold page chunk_off[r] + nhist[r], the
+// chunk's index keys (ikeys[r]) to that page at ikey_off, its scale to
+// ikey_scale.  The recent rows stay where they are until the window ends.
+__global__ void k_commit_page(GeomDev g, CommitSet f, int64_t row_bytes, int64_t page_bytes,
+                              int64_t ikey_off, const uint8_t* __restrict__ recent,
+                              uint8_t* __restrict__ cold, int64_t key_row_bytes,
+                              const uint8_t* __restrict__ ikeys, const float* __restrict__ iks,
+                              float* __restrict__ ikey_scale) {
+    const int r = blockIdx.y;
+    if (!f.on[r]) return;
+    const int64_t c = g.chunk_off[r] + g.nhist[r];
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const uint4* src = (const uint4*)(recent + g.rec_off[r] * row_bytes);
+    uint4* pg = (uint4*)(cold + c * page_bytes);
+    for (int64_t u = tid; u < 64 * row_bytes / 16; u += stride) pg[u] = src[u];
+    const uint4* sk = (const uint4*)(ikeys + (int64_t)r * 64 * key_row_bytes);
+    uint4* pk = (uint4*)(cold + c * page_bytes + ikey_off);
+    for (int64_t u = tid; u < 64 * key_row_bytes / 16; u += stride) pk[u] = sk[u];
+    if (iks && tid == 0) ikey_scale[c] = iks[r];
+}
+
+// Grid (X, B).  Request r with m.n[r] > 0 moves its recent rows
+// [src[r], src[r] + n[r]) to [dst[r], ..); the ranges do not overlap.
+__global__ void k_compact_recent(RecentMoves m, int64_t row_bytes, uint8_t* __restrict__ recent) {
+    const int r = blockIdx.y;
+    if (m.n[r] <= 0) return;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const uint4* src = (const uint4*)(recent + m.src[r] * row_bytes);
+    uint4* dst = (uint4*)(recent + m.dst[r] * row_bytes);
+    for (int64_t u = tid; u < (int64_t)m.n[r] * row_bytes / 16; u += stride) dst[u] = src[u];
+}
+
 }  // namespace
+
+hipError_t launch_commit_page(const GeomDev& g, const CommitSet& f, int64_t row_bytes,
+                              int64_t page_bytes, int64_t ikey_off, const void* recent, void* cold,
+                              int64_t key_row_bytes, const void* ikeys, const float* iks,
+                              float* ikey_scale, hipStream_t s) {
+    timing_begin("k_commit_page", s);
+    hipLaunchKernelGGL(k_commit_page, dim3(16, g.B), dim3(256), 0, s, g, f, row_bytes, page_bytes,
+                       ikey_off, (const uint8_t*)recent, (uint8_t*)cold, key_row_bytes,
+                       (const uint8_t*)ikeys, iks, ikey_scale);
+    timing_end("k_commit_page", s);
+    return hipGetLastError();
+}
+
+hipError_t launch_compact_recent(int B, const RecentMoves& m, int64_t row_bytes, void* recent,
+                                 hipStream_t s) {
+    timing_begin("k_compact_recent", s);
+    hipLaunchKernelGGL(k_compact_recent, dim3(64, B), dim3(256), 0, s, m, row_bytes, (uint8_t*)recent);
+    timing_end("k_compact_recent", s);
+    return hipGetLastError();
+}
 
 hipError_t launch_append_kv(const GeomDev& g, const void* rows, int64_t row_bytes, void* recent,
                             hipStream_t s) {

@@ -52,6 +52,21 @@ hipError_t launch_commit_chunk(const GeomDev& g, int64_t row_bytes, int64_t page
                                const void* new_ikeys, const float* new_iks, float* ikey_scale,
                                const void* new_kic, const float* new_kcs, void* kic, float* kic_scale,
                                bool fp8, hipStream_t s);
+// The window pipeline's growing context: which requests commit a chunk in
+// the window, and the recent rows moved back to the start of their area.
+struct CommitSet {
+    int32_t on[LSA_MAX_BATCH];
+};
+struct RecentMoves {
+    int64_t src[LSA_MAX_BATCH], dst[LSA_MAX_BATCH];  // first rows
+    int32_t n[LSA_MAX_BATCH];                        // rows (0: none)
+};
+hipError_t launch_commit_page(const GeomDev& g, const CommitSet& f, int64_t row_bytes,
+                              int64_t page_bytes, int64_t ikey_off, const void* recent, void* cold,
+                              int64_t key_row_bytes, const void* ikeys, const float* iks,
+                              float* ikey_scale, hipStream_t s);
+hipError_t launch_compact_recent(int B, const RecentMoves& m, int64_t row_bytes, void* recent,
+                                 hipStream_t s);
 
 // Per-request keep counts of lsa_select_ranked (by value).
 struct RankCounts {
@@ -103,6 +118,12 @@ size_t attn_scratch_bytes();
 void* lsa_pool_slots(const lsa_pool* p);
 int64_t lsa_pool_page_bytes(const lsa_pool* p);
 int32_t lsa_pool_batch(const lsa_pool* p);
+void* lsa_pool_cold(const lsa_pool* p);
+// A grown history: the pool takes the new chunk counts (nhist) of g; chunks
+// beyond the old counts start not resident.  Host only.
+lsa_status pool_grow(lsa_pool* p, const GeomDev& g);
+// tile_off of g from its nhist (after the history counts change)
+void geom_retile(GeomDev* g);
 
 // Launch-shape override of lsa_tune_set (-1: the library's own choice).
 int tune_get(lsa_tune_knob knob);

@@ -76,6 +76,23 @@ void pack_chunks(uint8_t* dst, const uint8_t* src, const int32_t* pairs, int n, 
 void* lsa_pool_slots(const lsa_pool* p) { return p ? p->slots : nullptr; }
 int64_t lsa_pool_page_bytes(const lsa_pool* p) { return p ? p->page_bytes : 0; }
 int32_t lsa_pool_batch(const lsa_pool* p) { return p ? p->g.B : 0; }
+void* lsa_pool_cold(const lsa_pool* p) { return p ? (void*)p->cold : nullptr; }
+
+lsa_status pool_grow(lsa_pool* p, const GeomDev& g) {
+    if (!p || g.B != p->g.B) return LSA_ERR_INVALID_ARG;
+    for (int r = 0; r < g.B; ++r) {
+        if (g.chunk_off[r] != p->g.chunk_off[r] || g.nhist[r] < p->g.nhist[r]) return LSA_ERR_INVALID_ARG;
+        if (g.nhist[r] > p->g.chunk_off[r + 1] - p->g.chunk_off[r]) return LSA_ERR_INVALID_ARG;
+    }
+    for (int r = 0; r < g.B; ++r) {
+        p->chunk_slot[r].resize(g.nhist[r], -1);
+        p->mark[r].resize(g.nhist[r], 0);
+        p->g.nhist[r] = g.nhist[r];
+        p->g.L[r] = g.L[r];
+        p->g.rs[r] = g.rs[r];
+    }
+    return LSA_OK;
+}
 
 extern "C" {
 

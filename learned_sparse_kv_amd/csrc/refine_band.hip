@@ -177,17 +177,21 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
     // selected chunks come resolved (one load instead of two).
     int64_t pg_l = 0;
     float sc_l = 1.0f;
+    // the scales sit beside the resolved pages, or by chunk (one array for
+    // both cases: a choice of array per load puts the pointers in scratch)
+    const float* __restrict__ scl = sel_slot ? sel_scale : ikey_scale;
     auto load_idx = [&](int j0, int nlim) __attribute__((always_inline)) {
         if (j0 + lane < nlim) {
             const int i = i0 + (j0 + lane) * stride;
+            int64_t e;  // the chunk's entry in the page and scale arrays
             if (sel_slot) {
-                pg_l = (int64_t)sel_slot[off + i];
-                if constexpr (KDT == LSA_FP8_E4M3FN) sc_l = sel_scale[off + i];
+                e = off + i;
+                pg_l = (int64_t)sel_slot[e];
             } else {
-                const int c = min(max(sel[off + i], 0), nhr - 1);
-                pg_l = page_table ? (int64_t)page_table[off + c] : off + c;
-                if constexpr (KDT == LSA_FP8_E4M3FN) sc_l = ikey_scale[off + c];
+                e = off + min(max(sel[off + i], 0), nhr - 1);
+                pg_l = page_table ? (int64_t)page_table[e] : e;
             }
+            if constexpr (KDT == LSA_FP8_E4M3FN) sc_l = scl[e];
         }
     };
     const int nj_max = i0 < nhr ? (nhr - i0 + stride - 1) / stride : 0;

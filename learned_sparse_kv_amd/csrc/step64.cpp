@@ -43,6 +43,12 @@ struct lsa_ctx {
     int cur = 0;
     bool primed = false;
     bool have_next = false;
+    // growing context: request r's recent rows start at row rec_first[r] of
+    // its recent_cap rows; no window holds more than rmax of them
+    bool growing = false;
+    int64_t recent_cap = 0;
+    int32_t rmax = 0;
+    int32_t rec_first[LSA_MAX_BATCH] = {};
 };
 
 namespace {
@@ -58,11 +64,29 @@ struct Carve {
     }
 };
 
+// Growing context: the most recent rows a request holds during a window.
+// A window starts with at most max(W + 63, R_r) rows (a request at or past
+// W + 64 at a window's end commits a chunk) and adds at most 64.
+int32_t grow_rmax(const GeomDev& g) {
+    int32_t a = g.W + 63;
+    for (int r = 0; r < g.B; ++r) a = g.nrec[r] > a ? g.nrec[r] : a;
+    return a + 64;
+}
+
+// The attention plan covers every recent length the context reaches.
+lsa_status ctx_plan(const lsa_ctx_desc* d, const GeomDev& g, AttnPlan* plan) {
+    if (!d->growing) return attn_plan(g, &d->kv, d->Hq, d->k, 0, plan);
+    GeomDev gp = g;
+    const int32_t rm = grow_rmax(g);
+    for (int r = 0; r < g.B; ++r) gp.nrec[r] = rm;
+    return attn_plan(gp, &d->kv, d->Hq, d->k, 0, plan);
+}
+
 // Workspace layout; returns total bytes (0 on invalid description).
 size_t layout(const lsa_ctx_desc* d, GeomDev* g, AttnPlan* plan, size_t offs[15]) {
     if (!d) return 0;
     if (geom_derive(&d->geom, g) != LSA_OK) return 0;
-    if (attn_plan(*g, &d->kv, d->Hq, d->k, 0, plan) != LSA_OK) return 0;
+    if (ctx_plan(d, *g, plan) != LSA_OK) return 0;
     const int64_t nh = g->chunk_off[g->B];
     const int B = g->B;
     Carve c;
@@ -89,7 +113,8 @@ int n_layers_of(const lsa_ctx_desc& d) { return d.n_layers > 1 ? d.n_layers : 1;
 
 // Scores every indexer layer into z (later layers keep the per-chunk maximum,
 // so z > theta exactly when some layer's logit is), then selects.
-lsa_status score_select(lsa_ctx* x, const lsa_trigger_in* t, int buf, hipStream_t s) {
+lsa_status score_select(lsa_ctx* x, const GeomDev& g, const lsa_trigger_in* t, int buf,
+                        hipStream_t s) {
     const lsa_ctx_desc& d = x->d;
     const int nl = n_layers_of(d);
     if (!t) return LSA_ERR_INVALID_ARG;
@@ -99,18 +124,18 @@ lsa_status score_select(lsa_ctx* x, const lsa_trigger_in* t, int buf, hipStream_
         if (x->nh > 0 && d.idx_dt == LSA_FP8_E4M3FN && !t[l].kic_scale) return LSA_ERR_INVALID_ARG;
     }
     for (int l = 0; l < nl; ++l) {
-        if (launch_fuse_query(x->g, t[l].q, d.q_dt, t[l].w, d.H, d.d, x->qbar, s) != hipSuccess)
+        if (launch_fuse_query(g, t[l].q, d.q_dt, t[l].w, d.H, d.d, x->qbar, s) != hipSuccess)
             return LSA_ERR_HIP;
-        if (launch_score(x->g, t[l].kic, d.idx_dt, t[l].kic_scale, x->qbar, t[l].bias, d.d, x->z, s,
+        if (launch_score(g, t[l].kic, d.idx_dt, t[l].kic_scale, x->qbar, t[l].bias, d.d, x->z, s,
                          l > 0) != hipSuccess)
             return LSA_ERR_HIP;
     }
-    if (launch_select(x->g, x->z, d.theta, x->sel[buf], x->cnt[buf], s) != hipSuccess)
+    if (launch_select(g, x->z, d.theta, x->sel[buf], x->cnt[buf], s) != hipSuccess)
         return LSA_ERR_HIP;
     if (x->nh > 0 && hipMemcpyAsync(x->h_sel[buf], x->sel[buf], (size_t)x->nh * 4,
                                     hipMemcpyDeviceToHost, s) != hipSuccess)
         return LSA_ERR_HIP;
-    if (hipMemcpyAsync(x->h_cnt[buf], x->cnt[buf], (size_t)x->g.B * 4, hipMemcpyDeviceToHost, s) !=
+    if (hipMemcpyAsync(x->h_cnt[buf], x->cnt[buf], (size_t)g.B * 4, hipMemcpyDeviceToHost, s) !=
         hipSuccess)
         return LSA_ERR_HIP;
     if (hipEventRecord(x->ev_sel, s) != hipSuccess) return LSA_ERR_HIP;
@@ -154,7 +179,15 @@ lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc) {
     if (lsa_pool_page_bytes(desc->pool) != desc->kv.page_bytes ||
         lsa_pool_batch(desc->pool) != g.B)
         return LSA_ERR_INVALID_ARG;
-    st = attn_plan(g, &desc->kv, desc->Hq, desc->k, 0, &plan);
+    int32_t rmax = 0;
+    if (desc->growing) {
+        // fixed capacities per request, and room for the recent rows to
+        // slide a whole window's length before they move back
+        if (desc->geom.chunk_cap <= 0 || desc->geom.recent_cap <= 0) return LSA_ERR_INVALID_ARG;
+        rmax = grow_rmax(g);
+        if ((int64_t)desc->geom.recent_cap < 2 * (int64_t)rmax) return LSA_ERR_INVALID_ARG;
+    }
+    st = ctx_plan(desc, g, &plan);
     if (st != LSA_OK) return st;
     const size_t need = layout(desc, &g, &plan, offs);
     if (need == 0) return LSA_ERR_INVALID_ARG;
@@ -165,6 +198,9 @@ lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc) {
     x->g = g;
     x->plan = plan;
     x->nh = g.chunk_off[g.B];
+    x->growing = desc->growing != 0;
+    x->recent_cap = desc->geom.recent_cap;
+    x->rmax = rmax;
     uint8_t* base = (uint8_t*)desc->ws;
     x->qbar = (float*)(base + offs[0]);
     x->z = (float*)(base + offs[1]);
@@ -223,7 +259,7 @@ lsa_status lsa_ctx_prime(lsa_ctx* x, const lsa_trigger_in* first, void* main_str
     if (!x || !first) return LSA_ERR_INVALID_ARG;
     hipStream_t ms = (hipStream_t)main_stream;
     x->cur = 0;
-    lsa_status st = score_select(x, first, 0, ms);
+    lsa_status st = score_select(x, x->g, first, 0, ms);
     if (st != LSA_OK) return st;
     if (hipEventRecord(x->ev_win[0], ms) != hipSuccess || hipEventRecord(x->ev_win[1], ms) != hipSuccess)
         return LSA_ERR_HIP;
@@ -248,11 +284,57 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
     if (in->steps < 1 || in->steps > 64 || !in->q_refine || !in->w_refine || !in->q_attn)
         return LSA_ERR_INVALID_ARG;
     const lsa_ctx_desc& d = x->d;
-    const GeomDev& g = x->g;
+    GeomDev& g = x->g;
     hipStream_t ms = (hipStream_t)main_stream;
     const int cur = x->cur, nxt = cur ^ 1;
+    const bool fp8 = d.idx_dt == LSA_FP8_E4M3FN;
+    const int64_t key_row_bytes = (int64_t)d.d * esz(d.idx_dt);
+
+    // growing context: who commits a chunk in this window (checked before
+    // anything is launched), and the history the next trigger scores
+    CommitSet commit{};
+    GeomDev gs = g;
+    if (x->growing) {
+        if (!in->new_rows || !in->commit_ikeys || (fp8 && !in->commit_ikey_scale))
+            return LSA_ERR_INVALID_ARG;
+        for (int r = 0; r < g.B; ++r) {
+            if (g.nrec[r] + in->steps > x->rmax) return LSA_ERR_INVALID_ARG;  // cannot happen
+            commit.on[r] = g.nrec[r] + in->steps >= g.W + LSA_CHUNK;
+            if (commit.on[r] && g.chunk_off[r] + g.nhist[r] + 1 > g.chunk_off[r + 1])
+                return LSA_ERR_CAPACITY;
+            gs.nhist[r] += commit.on[r];
+        }
+        geom_retile(&gs);
+    }
 
     if (hipStreamWaitEvent(ms, x->ev_fetch[cur], 0) != hipSuccess) return LSA_ERR_HIP;
+    if (x->growing) {
+        // a window that would run past the end of a request's recent area
+        // starts with its rows moved back to the area's start (the ranges do
+        // not overlap: the area holds two windows' worth of rows)
+        RecentMoves mv{};
+        bool any_move = false, any_commit = false;
+        for (int r = 0; r < g.B; ++r) {
+            any_commit |= commit.on[r] != 0;
+            if (x->rec_first[r] + g.nrec[r] + in->steps > x->recent_cap) {
+                mv.src[r] = g.rec_off[r];
+                mv.dst[r] = (int64_t)r * x->recent_cap;
+                mv.n[r] = g.nrec[r];
+                x->rec_first[r] = 0;
+                g.rec_off[r] = mv.dst[r];
+                any_move = true;
+            }
+        }
+        if (any_move &&
+            launch_compact_recent(g.B, mv, d.kv.row_bytes, (void*)d.recent, ms) != hipSuccess)
+            return LSA_ERR_HIP;
+        if (any_commit &&
+            launch_commit_page(g, commit, d.kv.row_bytes, d.kv.page_bytes, d.kv.ikey_off, d.recent,
+                               lsa_pool_cold(d.pool), key_row_bytes, in->commit_ikeys,
+                               fp8 ? in->commit_ikey_scale : nullptr, (float*)d.ikey_scale,
+                               ms) != hipSuccess)
+            return LSA_ERR_HIP;
+    }
     const bool band = band_supported(d.idx_dt, d.q_dt, d.H, d.d);
     if (band && (launch_resolve_sel(g, x->sel[cur], x->cnt[cur], x->pt[cur], d.ikey_scale,
                                     x->sel_slot, x->sel_scale, ms) != hipSuccess ||
@@ -261,7 +343,7 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
                                   ms) != hipSuccess))
         return LSA_ERR_HIP;
     if (in->next) {
-        lsa_status st = score_select(x, in->next, nxt, ms);
+        lsa_status st = score_select(x, gs, in->next, nxt, ms);
         if (st != LSA_OK) return st;
     }
     int groups = 0;
@@ -274,6 +356,15 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
         int32_t* tc = out->topk_cnt ? out->topk_cnt + (size_t)j * g.B : x->tcnt_tmp;
         const uint8_t* qr = (const uint8_t*)in->q_refine + j * qr_step;
         const float* wr = in->w_refine + (size_t)j * g.B * d.H;
+        if (x->growing) {  // the step's token joins the recent region first
+            for (int r = 0; r < g.B; ++r) {
+                ++g.L[r];
+                ++g.nrec[r];
+            }
+            if (launch_append_kv(g, (const uint8_t*)in->new_rows + (size_t)j * g.B * d.kv.row_bytes,
+                                 d.kv.row_bytes, (void*)d.recent, ms) != hipSuccess)
+                return LSA_ERR_HIP;
+        }
         if (groups > 0 && band) {
             const bool clean = x->band_clean;
             x->band_clean = false;  // until the chain is queued whole
@@ -307,17 +398,34 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
         hipMemcpyAsync(x->d_err, &x->h_err[2], sizeof(uint32_t), hipMemcpyHostToDevice, ms) != hipSuccess)
         return LSA_ERR_HIP;
     if (hipEventRecord(x->ev_win[cur], ms) != hipSuccess) return LSA_ERR_HIP;
+    if (x->growing) {
+        // the committed chunks leave the recent region: from the next window
+        // on they are history, attended when a trigger selects them
+        for (int r = 0; r < g.B; ++r) {
+            if (!commit.on[r]) continue;
+            g.rs[r] += LSA_CHUNK;
+            g.nhist[r] += 1;
+            g.nrec[r] -= LSA_CHUNK;
+            g.rec_off[r] += LSA_CHUNK;
+            x->rec_first[r] += LSA_CHUNK;
+        }
+        geom_retile(&g);
+    }
     bool dev_err = false;
     if (in->next) {
         if (hipEventSynchronize(x->ev_sel) != hipSuccess) return LSA_ERR_HIP;
         // ev_sel follows the previous window on the main stream
         dev_err = x->h_err[nxt] != 0;
-        lsa_gather_stats gs{};
+        if (x->growing) {
+            lsa_status st = pool_grow(x->d.pool, gs);
+            if (st != LSA_OK) return st;
+        }
+        lsa_gather_stats fs{};
         lsa_status st = lsa_gather_kv(x->d.pool, x->h_sel[nxt], x->h_cnt[nxt], x->h_sel[cur],
                                       x->h_cnt[cur], x->pt[nxt], copy_stream, x->ev_win[nxt],
-                                      x->ev_fetch[nxt], &gs);
+                                      x->ev_fetch[nxt], &fs);
         if (st != LSA_OK) return st;
-        out->stats = gs;
+        out->stats = fs;
         if (out->sel_cnt) std::memcpy(out->sel_cnt, x->h_cnt[nxt], (size_t)g.B * 4);
         x->cur = nxt;
         x->have_next = true;
@@ -325,6 +433,17 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
         x->have_next = false;
     }
     return dev_err ? LSA_ERR_HIP : LSA_OK;
+}
+
+lsa_status lsa_ctx_state(const lsa_ctx* x, int32_t* seq_len, int32_t* hist_tokens,
+                         int32_t* recent_first) {
+    if (!x) return LSA_ERR_INVALID_ARG;
+    for (int r = 0; r < x->g.B; ++r) {
+        if (seq_len) seq_len[r] = x->g.L[r];
+        if (hist_tokens) hist_tokens[r] = x->g.rs[r];
+        if (recent_first) recent_first[r] = x->rec_first[r];
+    }
+    return LSA_OK;
 }
 
 }  // extern "C"

@@ -54,7 +54,8 @@ class lsa_ctx_desc(C.Structure):
                 ("idx_dt", C.c_int), ("Hq", C.c_int32), ("k", C.c_int32),
                 ("kv", lsa_kv_layout), ("sm_scale", C.c_float), ("theta", C.c_float),
                 ("recent", C.c_void_p), ("ikey_scale", C.c_void_p), ("pool", C.c_void_p),
-                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t), ("n_layers", C.c_int32)]
+                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t), ("n_layers", C.c_int32),
+                ("growing", C.c_int32)]
 
 
 class lsa_trigger_in(C.Structure):
@@ -64,7 +65,9 @@ class lsa_trigger_in(C.Structure):
 
 class lsa_window_in(C.Structure):
     _fields_ = [("steps", C.c_int32), ("q_refine", C.c_void_p), ("w_refine", C.c_void_p),
-                ("q_attn", C.c_void_p), ("next", C.POINTER(lsa_trigger_in))]
+                ("q_attn", C.c_void_p), ("next", C.POINTER(lsa_trigger_in)),
+                ("new_rows", C.c_void_p), ("commit_ikeys", C.c_void_p),
+                ("commit_ikey_scale", C.c_void_p)]
 
 
 class lsa_window_out(C.Structure):
@@ -107,6 +110,7 @@ def _load():
         "lsa_ctx_destroy": ([P], None),
         "lsa_ctx_prime": ([P, C.POINTER(lsa_trigger_in), P, P, C.POINTER(lsa_window_out)], I),
         "lsa_step64": ([P, C.POINTER(lsa_window_in), C.POINTER(lsa_window_out), P, P], I),
+        "lsa_ctx_state": ([P, P, P, P], I),
         "lsa_timing_enable": ([I32], I),
         "lsa_timing_only": ([C.c_char_p], I),
         "lsa_timing_every": ([I32], I),
@@ -364,6 +368,13 @@ class Ctx:
                                              _stream(copy)))
         return out.stats.as_dict()
 
+    def state(self):
+        """(seq_len, hist_tokens, recent_first) as host int32 arrays [B]."""
+        B = self.desc.geom.batch
+        L, rs, rf = (np.zeros(B, np.int32) for _ in range(3))
+        _check("lsa_ctx_state", _lib.lsa_ctx_state(self.h, _ptr(L), _ptr(rs), _ptr(rf)))
+        return L, rs, rf
+
     def close(self):
         if getattr(self, "h", None):
             _lib.lsa_ctx_destroy(self.h)
@@ -384,7 +395,8 @@ def lsa_step64(ctx: Ctx, win, out, main=None, copy=None):
 KERNELS = ("k_fuse_query", "k_score", "k_select", "k_refine", "k_topk", "k_refine_mfma",
            "k_band_fine", "k_band_list", "k_topk_band", "k_attn_mla", "k_attn_f32", "k_attn_merge",
            "k_gather", "k_stream_read", "k_score_sig", "k_select_ranked", "k_chunk_ml",
-           "k_append_kv", "k_commit_chunk", "k_resolve_sel", "k_key_norm2")
+           "k_append_kv", "k_commit_chunk", "k_commit_page", "k_compact_recent", "k_resolve_sel",
+           "k_key_norm2")
 
 
 def lsa_timing_enable(on: bool):

@@ -256,76 +256,99 @@ def token_row(inp, r: int, s: int) -> np.ndarray:
     return inp["recent"][int(inp["rec_off"][r]) + s - rs]
 
 
+def growing_state(full, L0, n_windows: int, recent_cap: int):
+    """Host arrays of a growing-context run over the tokens of `full` (inputs
+    generated at the final context lengths L0 + 64 * n_windows), in the
+    fixed-capacity layout (chunk_cap chunks, recent_cap recent rows per
+    request): the cold-tier pages, KIComp rows and scales of the history at
+    L0, the recent rows, each step's appended row, and per window the index
+    keys, KIComp row and scales of the chunk each request commits then (the
+    recent region's oldest full chunk, once it holds W + 64 rows)."""
+    cfg = full.cfg
+    C, W, B = cfg.chunk, cfg.window, cfg.batch
+    L = np.asarray(L0, np.int64).copy()
+    if not np.array_equal(L + C * n_windows, np.asarray(full["seq_len"], np.int64)):
+        raise ValueError("full must hold the contexts L0 + 64 * n_windows")
+    rs0 = C * (np.maximum(L - W, 0) // C)
+    chunk_cap = max(int(np.max(full["n_hist"])), 1)
+    rb, pb = cfg.kv_row_bytes, cfg.page_bytes
+    kb = cfg.d * synth.ELEM_BYTES[cfg.idx_dtype]
+    pages = np.zeros((B * chunk_cap, pb), np.uint8)
+    kic = np.zeros((B * chunk_cap, kb), np.uint8)
+    ksc = np.ones(B * chunk_cap, np.float32)
+    isc = np.ones(B * chunk_cap, np.float32)
+    rec = np.zeros((B * recent_cap, rb), np.uint8)
+    fk = full["kic_windows"][0].reshape(int(full["chunk_off"][-1]), -1).view(np.uint8)
+    for r in range(B):
+        f0, n0, o = int(full["chunk_off"][r]), int(rs0[r]) // C, r * chunk_cap
+        pages[o:o + n0] = full["pages"][f0:f0 + n0]
+        kic[o:o + n0] = fk[f0:f0 + n0]
+        ksc[o:o + n0] = full["kic_scale_windows"][0][f0:f0 + n0]
+        isc[o:o + n0] = full["ikey_scale"][f0:f0 + n0]
+        for i, t in enumerate(range(int(rs0[r]), int(L[r]))):
+            rec[r * recent_cap + i] = token_row(full, r, t)
+    T = C * n_windows
+    app = np.zeros((T, B, rb), np.uint8)
+    for t in range(T):
+        for r in range(B):
+            app[t, r] = token_row(full, r, int(L[r]) + t)
+    nik = np.zeros((n_windows, B, C * kb), np.uint8)
+    nkc = np.zeros((n_windows, B, kb), np.uint8)
+    nis = np.ones((n_windows, B), np.float32)
+    nks = np.ones((n_windows, B), np.float32)
+    commits = np.zeros((n_windows, B), bool)
+    rs = rs0.copy()
+    for m in range(n_windows):
+        Lm = L + C * (m + 1)
+        for r in range(B):
+            if Lm[r] - rs[r] >= W + C:
+                c = int(full["chunk_off"][r]) + int(rs[r]) // C
+                nik[m, r] = full["pages"][c, cfg.ikey_off:cfg.ikey_off + C * kb]
+                nkc[m, r] = fk[c]
+                nis[m, r] = full["ikey_scale"][c]
+                nks[m, r] = full["kic_scale_windows"][0][c]
+                commits[m, r] = True
+                rs[r] += C
+    return dict(L0=L, rs0=rs0, chunk_cap=chunk_cap, pages=pages, kic=kic, kic_scale=ksc,
+                ikey_scale=isc, recent=rec, app=app, nik=nik, nkc=nkc, nis=nis, nks=nks,
+                commits=commits)
+
+
 class Growing:
     """Growing-context decode over the tokens of `full` (inputs generated at
-    the final context lengths).  The run starts at contexts L0 and adds one
-    token per step; every 64 steps (a window) it scores and selects the
-    current history, and at the end of each window it commits the recent
-    region's oldest full chunk into the history.  Device state uses fixed
-    capacities per request (chunk_cap chunks, recent_cap recent rows): a
-    cold tier of pages, KIComp rows and scales, and two recent buffers used
-    in turn.  The rows each step appends and each committed chunk's index
-    keys and KIComp row come from `full`."""
+    the final context lengths), one entry point per step.  The run starts at
+    contexts L0 and adds one token per step; every 64 steps (a window) it
+    scores and selects the current history, and at the end of each window it
+    commits the recent region's oldest full chunk into the history.  Device
+    state uses fixed capacities per request (chunk_cap chunks, recent_cap
+    recent rows): a cold tier of pages, KIComp rows and scales, and two recent
+    buffers used in turn."""
 
     def __init__(self, full, L0, n_windows: int, device="cuda"):
         cfg = full.cfg
         C, W = cfg.chunk, cfg.window
         self.full, self.cfg, self.device, self.B = full, cfg, device, cfg.batch
-        self.L = np.asarray(L0, np.int64).copy()
-        if not np.array_equal(self.L + C * n_windows, np.asarray(full["seq_len"], np.int64)):
-            raise ValueError("full must hold the contexts L0 + 64 * n_windows")
-        self.rs = C * (np.maximum(self.L - W, 0) // C)
-        self.n_windows = n_windows
-        self.chunk_cap = max(int(np.max(full["n_hist"])), 1)
         self.recent_cap = W + 2 * C
-        B, rb, pb = self.B, cfg.kv_row_bytes, cfg.page_bytes
-        kb = cfg.d * synth.ELEM_BYTES[cfg.idx_dtype]
-        pages = np.zeros((B * self.chunk_cap, pb), np.uint8)
-        kic = np.zeros((B * self.chunk_cap, kb), np.uint8)
-        ksc = np.ones(B * self.chunk_cap, np.float32)
-        isc = np.ones(B * self.chunk_cap, np.float32)
-        rec = np.zeros((B * self.recent_cap, rb), np.uint8)
-        fk = full["kic_windows"][0].reshape(int(full["chunk_off"][-1]), -1).view(np.uint8)
-        for r in range(B):
-            f0, n0, o = int(full["chunk_off"][r]), int(self.rs[r]) // C, r * self.chunk_cap
-            pages[o:o + n0] = full["pages"][f0:f0 + n0]
-            kic[o:o + n0] = fk[f0:f0 + n0]
-            ksc[o:o + n0] = full["kic_scale_windows"][0][f0:f0 + n0]
-            isc[o:o + n0] = full["ikey_scale"][f0:f0 + n0]
-            for i, s in enumerate(range(int(self.rs[r]), int(self.L[r]))):
-                rec[r * self.recent_cap + i] = token_row(full, r, s)
-        T = C * n_windows
-        app = np.zeros((T, B, rb), np.uint8)
-        for t in range(T):
-            for r in range(B):
-                app[t, r] = token_row(full, r, int(self.L[r]) + t)
-        # per window: the chunk each request would commit at its end
-        nik = np.zeros((n_windows, B, C * kb), np.uint8)
-        nkc = np.zeros((n_windows, B, kb), np.uint8)
-        nis = np.ones((n_windows, B), np.float32)
-        nks = np.ones((n_windows, B), np.float32)
-        rs = self.rs.copy()
-        for m in range(n_windows):
-            Lm = self.L + C * (m + 1)
-            for r in range(B):
-                if Lm[r] - rs[r] >= W + C:
-                    c = int(full["chunk_off"][r]) + int(rs[r]) // C
-                    nik[m, r] = full["pages"][c, cfg.ikey_off:cfg.ikey_off + C * kb]
-                    nkc[m, r] = fk[c]
-                    nis[m, r] = full["ikey_scale"][c]
-                    nks[m, r] = full["kic_scale_windows"][0][c]
-                    rs[r] += C
+        st = growing_state(full, L0, n_windows, self.recent_cap)
+        self.L, self.rs = st["L0"].copy(), st["rs0"].copy()
+        self.n_windows = n_windows
+        self.chunk_cap = st["chunk_cap"]
+        B = self.B
         d = device
-        self.pages = _dev(pages.reshape(-1), d)
-        self.kic, self.kic_scale, self.ikey_scale = _dev(kic.reshape(-1), d), _dev(ksc, d), _dev(isc, d)
+        self.pages = _dev(st["pages"].reshape(-1), d)
+        self.kic, self.kic_scale = _dev(st["kic"].reshape(-1), d), _dev(st["kic_scale"], d)
+        self.ikey_scale = _dev(st["ikey_scale"], d)
+        rec = st["recent"]
         self.recent = [_dev(rec.reshape(-1), d), torch.zeros(rec.size, dtype=torch.uint8, device=d)]
-        self.app = _dev(app, d)
-        self.nik, self.nkc, self.nis, self.nks = _dev(nik, d), _dev(nkc, d), _dev(nis, d), _dev(nks, d)
+        self.app = _dev(st["app"], d)
+        self.nik, self.nkc = _dev(st["nik"], d), _dev(st["nkc"], d)
+        self.nis, self.nks = _dev(st["nis"], d), _dev(st["nks"], d)
         self.q_coarse, self.w_coarse = _dev(full["q_coarse"], d), _dev(full["w_coarse"], d)
         self.bias = _dev(full["bias"], d)
         self.q_refine, self.w_refine = _dev(full["q_refine"], d), _dev(full["w_refine"], d)
         self.q_attn = _dev(full["q_attn"], d)
-        self.kv = lsa.kv_layout(cfg.kv_dtype, cfg.Dk, cfg.Dv, cfg.v_off, rb, pb, cfg.ikey_off)
+        self.kv = lsa.kv_layout(cfg.kv_dtype, cfg.Dk, cfg.Dv, cfg.v_off, cfg.kv_row_bytes,
+                                cfg.page_bytes, cfg.ikey_off)
         self.cur = 0
         self.t = 0
         self.n_q = int(full["q_attn"].shape[0])  # per-step queries are reused cyclically past this
@@ -395,3 +418,112 @@ class Growing:
                                        self.kic_scale, stream).astype(np.int64)
         self.cur = 1 - self.cur
         return self.rs
+
+
+class GrowingPipeline:
+    """Growing-context decode through the window pipeline (lsa_step64 with
+    growing set) over the tokens of `full`, from contexts L0, n_windows
+    windows of 64 steps.  Every trigger uses the request's own coarse query
+    and the KIComp rows of the history it scores; before window m's call the
+    KIComp rows (and scales) of the chunks committed in window m go into the
+    trigger's arrays, since the next trigger scores them."""
+
+    def __init__(self, full, L0, n_windows: int, host_cold=True, k=None, slots_per_req=None,
+                 theta=0.0, device="cuda"):
+        cfg = full.cfg
+        self.full, self.cfg, self.B, self.device = full, cfg, cfg.batch, device
+        C, W = cfg.chunk, cfg.window
+        L0 = np.asarray(L0, np.int64)
+        rs0 = C * (np.maximum(L0 - W, 0) // C)
+        rmax = max(W + 63, int((L0 - rs0).max())) + 64
+        self.recent_cap = 2 * rmax
+        st = growing_state(full, L0, n_windows, self.recent_cap)
+        self.st, self.n_windows, self.chunk_cap = st, n_windows, st["chunk_cap"]
+        d = device
+        self.geom = lsa.Geom(st["L0"], W, C, hist_tokens=st["rs0"], chunk_cap=self.chunk_cap,
+                             recent_cap=self.recent_cap)
+        self.pages = _pinned(st["pages"].reshape(-1)) if host_cold else _dev(st["pages"].reshape(-1), d)
+        self.kic, self.kic_scale = _dev(st["kic"].reshape(-1), d), _dev(st["kic_scale"], d)
+        self.ikey_scale = _dev(st["ikey_scale"], d)
+        self.recent = _dev(st["recent"].reshape(-1), d)
+        self.app = _dev(st["app"], d)
+        self.nik, self.nis = _dev(st["nik"], d), _dev(st["nis"], d)
+        self.nkc, self.nks = _dev(st["nkc"], d), _dev(st["nks"], d)
+        # KIComp rows each window commits: (row in kic, window, request)
+        self.kic_rows = []
+        n = (st["rs0"] // C).astype(np.int64)
+        for m in range(n_windows):
+            rows = [(r * self.chunk_cap + int(n[r]), r) for r in range(self.B) if st["commits"][m, r]]
+            n = n + st["commits"][m]
+            self.kic_rows.append((torch.tensor([x[0] for x in rows], dtype=torch.int64, device=d),
+                                  torch.tensor([x[1] for x in rows], dtype=torch.int64, device=d)))
+        self.q_coarse, self.w_coarse = _dev(full["q_coarse"], d), _dev(full["w_coarse"], d)
+        self.bias = _dev(full["bias"], d)
+        self.q_refine, self.w_refine = _dev(full["q_refine"], d), _dev(full["w_refine"], d)
+        self.q_attn = _dev(full["q_attn"], d)
+        self.n_q = int(full["q_attn"].shape[0])
+        self.kv = lsa.kv_layout(cfg.kv_dtype, cfg.Dk, cfg.Dv, cfg.v_off, cfg.kv_row_bytes,
+                                cfg.page_bytes, cfg.ikey_off)
+        self.k = cfg.topk if k is None else k
+        spr = cfg.slots_per_req if slots_per_req is None else slots_per_req
+        self.spr = max(1, min(spr, self.chunk_cap))
+        self.slots = torch.empty(self.B * self.spr * cfg.page_bytes, dtype=torch.uint8, device=d)
+        self.pool = lsa.Pool(self.geom, self.slots, self.spr, cfg.page_bytes, self.pages, host_cold)
+        desc = lsa.lsa_ctx_desc()
+        desc.geom = self.geom.s
+        desc.H, desc.d, desc.q_dt, desc.idx_dt = cfg.H, cfg.d, cfg.q_dtype, cfg.idx_dtype
+        desc.Hq, desc.k = cfg.Hq, self.k
+        desc.kv = self.kv
+        desc.sm_scale, desc.theta = cfg.sm_scale, theta
+        desc.recent = self.recent.data_ptr()
+        desc.ikey_scale = self.ikey_scale.data_ptr()
+        desc.pool = self.pool.h.value
+        desc.n_layers = 1
+        desc.growing = 1
+        nbytes = lsa.lsa_ctx_ws_bytes(desc)
+        if nbytes == 0:
+            raise lsa.LsaError("lsa_ctx_ws_bytes", -1)
+        self.ws = _ws(nbytes, d)
+        desc.ws, desc.ws_bytes = self.ws.data_ptr(), self.ws.numel()
+        self.ctx = lsa.Ctx(desc, keep=(self,))
+        self.copy_stream = torch.cuda.Stream(device=d)
+        self.sel_cnt = np.zeros(self.B, dtype=np.int32)
+        self.trig = lsa.lsa_trigger_in(self.kic.data_ptr(), self.kic_scale.data_ptr(),
+                                       self.q_coarse.data_ptr(), self.w_coarse.data_ptr(),
+                                       self.bias.data_ptr())
+
+    def prime(self, main=None):
+        st = self.ctx.prime(self.trig, main, self.copy_stream, self.sel_cnt)
+        return st, self.sel_cnt.copy()
+
+    def window(self, m: int, out, lse=None, topk=None, tcnt=None, last=False, main=None):
+        """Window m: 64 steps (queries of steps 64 m .. 64 m + 63, cyclic past
+        the inputs' own), appending app[64 m + j] at step j."""
+        rows, reqs = self.kic_rows[m]
+        if len(rows):  # the next trigger scores the chunks this window commits
+            kb = self.kic.numel() // (self.B * self.chunk_cap)
+            self.kic.view(-1, kb).index_copy_(0, rows, self.nkc[m].index_select(0, reqs))
+            self.kic_scale.index_copy_(0, rows, self.nks[m].index_select(0, reqs))
+        t0 = (64 * m) % self.n_q
+        if t0 + 64 > self.n_q:
+            raise ValueError("the inputs hold too few steps of queries for a whole window")
+        win = lsa.lsa_window_in(64, self.q_refine[t0].data_ptr(), self.w_refine[t0].data_ptr(),
+                                self.q_attn[t0].data_ptr(), None if last else lsa.trigger_ptr(self.trig),
+                                self.app[64 * m].data_ptr(), self.nik[m].data_ptr(),
+                                self.nis[m].data_ptr())
+        wo = lsa.lsa_window_out()
+        wo.out = out.data_ptr()
+        wo.lse = lse.data_ptr() if lse is not None else None
+        wo.topk_idx = topk.data_ptr() if topk is not None else None
+        wo.topk_cnt = tcnt.data_ptr() if tcnt is not None else None
+        wo.sel_cnt = self.sel_cnt.ctypes.data
+        st = self.ctx.step64(win, wo, main, self.copy_stream)
+        return st, self.sel_cnt.copy()
+
+    def state(self):
+        return self.ctx.state()
+
+    def close(self):
+        torch.cuda.synchronize()
+        self.ctx.close()
+        self.pool.close()

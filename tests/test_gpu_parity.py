@@ -569,6 +569,102 @@ def test_chunk_mass_parity(kind):
 
 
 # ------------------------------------------------- growing context
+def _check_growing_pipeline(cfg, full, L0, nw, k, host_cold, spr, att_steps=(0, 1, 40, 63)):
+    """Run nw windows of lsa_step64 with a growing context and check, per
+    window, the selection counts, every step's top-k (bit-exact) and sampled
+    steps' attention against the oracle on the packed state of that step,
+    the fetch counts against the pool simulation, and the end state (lengths,
+    committed pages and scales, recent rows) against the generated data.
+    Window m's selection is the trigger over the history at window m's start
+    (with the chunks window m - 1 committed), scored one window ahead."""
+    from tests import helpers
+    R = _runner()
+    B = cfg.batch
+    gp = R.GrowingPipeline(full, L0, nw, host_cold=host_cold, k=k, slots_per_req=spr)
+    outs = torch.empty((nw, 64, B, cfg.Hq, cfg.Dv), dtype=torch.int16, device="cuda")
+    lses = torch.empty((nw, 64, B, cfg.Hq), dtype=torch.float32, device="cuda")
+    tks = torch.empty((nw, 64, B, k), dtype=torch.int32, device="cuda")
+    tcs = torch.empty((nw, 64, B), dtype=torch.int32, device="cuda")
+    st0, cnt0 = gp.prime()
+    fetched, cnts, starts = [st0["fetched"]], [cnt0], []
+    for m in range(nw):
+        L, rs, rf = gp.state()
+        starts.append((L.copy(), rs.copy(), rf.copy()))
+        print(f"[pgrow] {cfg.name} window {m}: L={list(L)} rs={list(rs)} recent_first={list(rf)}", flush=True)
+        st, cnt = gp.window(m, outs[m], lse=lses[m], topk=tks[m], tcnt=tcs[m], last=(m == nw - 1))
+        if m < nw - 1:
+            fetched.append(st["fetched"])
+            cnts.append(cnt)
+    torch.cuda.synchronize()
+    tol, lse_tol = tol_of(cfg)
+    sets = [[] for _ in range(B)]
+    tk_all, tc_all = tks.cpu().numpy(), tcs.cpu().numpy()
+    lse_all = lses.cpu().numpy()
+    for m in range(nw):
+        L_m, rs_m, _ = starts[m]
+        got_att = {j: R.out_to_f32(outs[m, j], cfg) for j in att_steps}
+        for r in range(B):
+            snap = helpers.growing_snapshot(full, r, int(L_m[r]), int(rs_m[r]))
+            _, sel_o, cnt_o = oracle.Oracle(snap).score_select()
+            assert cnts[m][r] == cnt_o[0], (m, r)
+            sel_r = np.ascontiguousarray(sel_o[:cnt_o[0]])
+            sets[r].append(set(sel_r.tolist()))
+            for j in range(64):
+                t = 64 * m + j
+                sj = helpers.growing_snapshot(full, r, int(L_m[r]) + j + 1, int(rs_m[r]))
+                o = oracle.Oracle(sj)
+                want = o.refine_topk(0, sel_r, sj["q_refine"][t, 0], sj["w_refine"][t, 0], k)
+                assert tc_all[m, j, r] == len(want), (m, j, r)
+                assert np.array_equal(tk_all[m, j, r, :len(want)], want), (m, j, r)
+                if j in got_att:
+                    ref, lse_ref = o.attend(0, want, sj["q_attn"][t, 0], cfg.sm_scale)
+                    assert rel_err(got_att[j][r], ref).max() <= tol, (m, j, r)
+                    assert np.abs(lse_all[m, j, r] - lse_ref).max() <= lse_tol * max(1.0, np.abs(lse_ref).max())
+    sim = [oracle.pool_sim(sets[r], gp.spr) for r in range(B)]
+    assert fetched == [sum(sim[r][m] for r in range(B)) for m in range(nw)]
+    L, rs, rf = gp.state()
+    assert np.array_equal(L, full["seq_len"]) and np.array_equal(rs, full["rs"])
+    pages = gp.pages.cpu().numpy().reshape(B * gp.chunk_cap, -1)
+    isc = gp.ikey_scale.cpu().numpy()
+    rec = gp.recent.cpu().numpy().reshape(B * gp.recent_cap, -1)
+    for r in range(B):
+        c0, n, a = int(full["chunk_off"][r]), int(full["n_hist"][r]), r * gp.chunk_cap
+        assert np.array_equal(pages[a:a + n], full["pages"][c0:c0 + n]), r
+        assert np.array_equal(isc[a:a + n], full["ikey_scale"][c0:c0 + n]), r
+        q0, nr, b = int(full["rec_off"][r]), int(full["n_rec"][r]), r * gp.recent_cap + int(rf[r])
+        assert np.array_equal(rec[b:b + nr], full["recent"][q0:q0 + nr]), r
+    gp.close()
+    return starts
+
+
+@pytest.mark.parametrize("idx,host_cold", [("bf16", True), ("fp8", True), ("fp8", False)])
+def test_window_pipeline_growing_matches_oracle(idx, host_cold):
+    """lsa_step64 with a growing context: three windows of 64 steps on
+    ragged requests (two commit a chunk in every window, one only in the
+    last), the pinned-host or HBM cold tier."""
+    W, k, nw = 1024, 256, 3
+    L0 = [5000, 3100, 900]
+    dt = BF16 if idx == "bf16" else FP8
+    cfg = synth.small_config("pgrow_" + idx, 41 if idx == "bf16" else 42, tuple(L + 64 * nw for L in L0),
+                             window=W, idx=dt, H=16, topk=k, steps=64 * nw)
+    full = synth.generate(cfg)
+    _check_growing_pipeline(cfg, full, L0, nw, k, host_cold, spr=64)
+
+
+def test_window_pipeline_growing_moves_recent_rows():
+    """A growing context run long enough that the recent rows reach the end
+    of their area and move back to its start (a short window: 128 tokens)."""
+    W, k, nw = 128, 64, 7
+    L0 = [2000, 1100, 100]
+    cfg = synth.small_config("pgrow_move", 43, tuple(L + 64 * nw for L in L0), window=W, idx=FP8,
+                             H=16, topk=k, steps=64 * nw)
+    full = synth.generate(cfg)
+    starts = _check_growing_pipeline(cfg, full, L0, nw, k, True, spr=32, att_steps=(0, 63))
+    rf = np.array([s[2] for s in starts])  # recent_first at each window's start
+    assert (np.diff(rf, axis=0) < 0).any(), rf  # some request's rows moved back
+
+
+# ------------------------------------------------- growing context
 @pytest.mark.parametrize("idx", ["bf16", "fp8"])
 def test_growing_context_matches_oracle(idx):
     """Two windows of growing-context decode (one token appended per step,
