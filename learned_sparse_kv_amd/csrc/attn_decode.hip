@@ -588,17 +588,19 @@ __global__ __launch_bounds__(256) void k_attn_f32(GeomDev g, PosMap pm, const in
 }
 
 // ----------------------------------------------------------------------------
-// merge of the splits: one wave per (request, head, 64 * VPL value columns),
+// merge of the splits: one block per (request, head, 64 * VPL value columns),
 // VPL = 16 bytes of a partial row per lane (8 bf16 columns on the bf16 latent
-// path, 4 fp32 columns on the f32 path), so a wave reads a whole 1 KB
-// partial row per load and has up to kMergeBatch splits' rows in flight.
-// The split weights 2^(m_s - m) and the total sum are formed by the wave in
-// a fixed order; each lane then combines its columns over all splits in
-// split order.
+// path, 4 fp32 columns on the f32 path), so a load reads a whole 1 KB
+// partial row.  The block's kMergeWaves waves take contiguous ranges of the
+// splits and have all their rows in flight at once (the merge is bound by
+// the load latency, not the bytes).  Every wave forms the split weights
+// 2^(m_s - m) and the total sum in the same fixed order; each lane combines
+// its columns over its range in split order, and the ranges are added in
+// wave order.
 // ----------------------------------------------------------------------------
 constexpr int kMergeMaxSplits = 1024;
-constexpr int kMergeWaves = 4;   // waves per block
-constexpr int kMergeBatch = 16;  // partial rows in flight per lane
+constexpr int kMergeWaves = 4;   // waves per block (split ranges)
+constexpr int kMergeBatch = 8;   // partial rows in flight per lane
 
 template <typename PT>
 __host__ __device__ inline int merge_col_blocks(int Dv) {
@@ -613,25 +615,27 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_attn_merge(const PT* __res
                                                                void* __restrict__ out,
                                                                float* __restrict__ lse) {
     constexpr int VPL = 16 / (int)sizeof(PT);
-    __shared__ float fac_s[kMergeWaves][kMergeMaxSplits];
+    __shared__ float fac[kMergeMaxSplits];
+    __shared__ float red[kMergeWaves][VPL][64];
     const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
     const int ncb = merge_col_blocks<PT>(Dv);
-    const int unit = blockIdx.x * kMergeWaves + w;  // (r * Hq + h) * ncb + cb
-    if (unit >= B * Hq * ncb) return;               // uniform per wave
+    const int unit = blockIdx.x;  // (r * Hq + h) * ncb + cb
+    if (unit >= B * Hq * ncb) return;  // uniform per block
     const int rh = unit / ncb, cb = unit % ncb;
     const int r = rh / Hq, h = rh % Hq;
-    float* fac = fac_s[w];
     const int64_t b0 = (int64_t)r * n_splits * Hq + h;  // split s: (b0 + s*Hq)
     const int v = (cb * 64 + L) * VPL;                  // first column of the lane
     const bool col = v < Dv;                            // Dv is a multiple of VPL
     const PT* src = part_o + b0 * Dv + v;
     const int64_t stride = (int64_t)Hq * Dv;
+    const int per = (n_splits + kMergeWaves - 1) / kMergeWaves;
+    const int s_lo = min(w * per, n_splits), s_hi = min(s_lo + per, n_splits);
     // the first batch of partial rows is requested before the split weights
     // are formed, so both latencies overlap
     uint4 x[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u)
-        if (col && u < n_splits) x[u] = *(const uint4*)(src + (int64_t)u * stride);
+        if (col && s_lo + u < s_hi) x[u] = *(const uint4*)(src + (int64_t)(s_lo + u) * stride);
     float m = -INFINITY;
     for (int s = L; s < n_splits; s += 64) m = fmaxf(m, part_ml[(b0 + (int64_t)s * Hq) * 2]);
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
@@ -639,7 +643,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_attn_merge(const PT* __res
     for (int s = L; s < n_splits; s += 64) {
         const float ms = part_ml[(b0 + (int64_t)s * Hq) * 2];
         const float f = (ms == -INFINITY) ? 0.0f : exp2f(ms - m);
-        fac[s] = f;
+        if (w == 0) fac[s] = f;
         part += part_ml[(b0 + (int64_t)s * Hq) * 2 + 1] * f;
     }
     // fixed-order tree over the lanes
@@ -647,22 +651,20 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_attn_merge(const PT* __res
     // an empty attended set (no recent token, no top-k entry) has no
     // softmax: its output is zero and its lse -inf
     const float Lsum = part, inv = part > 0.0f ? 1.0f / part : 0.0f;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (col) {
-        float o[VPL];
+    __syncthreads();  // fac complete
+    float o[VPL];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) o[i] = 0.0f;
-        for (int s0 = 0; s0 < n_splits; s0 += kMergeBatch) {
-            if (s0 > 0) {
+    for (int i = 0; i < VPL; ++i) o[i] = 0.0f;
+    if (col) {
+        for (int s0 = s_lo; s0 < s_hi; s0 += kMergeBatch) {
+            if (s0 > s_lo) {
 #pragma unroll
                 for (int u = 0; u < kMergeBatch; ++u)
-                    if (s0 + u < n_splits) x[u] = *(const uint4*)(src + (int64_t)(s0 + u) * stride);
+                    if (s0 + u < s_hi) x[u] = *(const uint4*)(src + (int64_t)(s0 + u) * stride);
             }
 #pragma unroll
             for (int u = 0; u < kMergeBatch; ++u) {
-                if (s0 + u < n_splits) {
+                if (s0 + u < s_hi) {
                     const float f = fac[s0 + u];
                     if (f != 0.0f) {
                         const uint32_t wd[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
@@ -676,6 +678,18 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_attn_merge(const PT* __res
                     }
                 }
             }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) red[w][i][L] = o[i];
+    __syncthreads();
+    if (w == 0 && col) {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            float t = red[0][i][L];
+#pragma unroll
+            for (int k = 1; k < kMergeWaves; ++k) t += red[k][i][L];
+            o[i] = t;
         }
         const int64_t ob = (int64_t)rh * Dv + v;
         if constexpr (ODT == LSA_F32) {
@@ -702,7 +716,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_attn_merge(const PT* __res
             }
         }
     }
-    if (lse && cb == 0 && L == 0) lse[rh] = Lsum > 0.0f ? (m + __log2f(Lsum)) * kLn2 : -INFINITY;
+    if (lse && cb == 0 && w == 0 && L == 0) lse[rh] = Lsum > 0.0f ? (m + __log2f(Lsum)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -850,9 +864,8 @@ hipError_t launch_attn(const GeomDev& g, const AttnPlan& plan, const void* q, in
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int units = g.B * Hq * (plan.mode == 1 ? merge_col_blocks<uint16_t>(kv.Dv)
-                                                 : merge_col_blocks<float>(kv.Dv));
-    const int mblocks = (units + kMergeWaves - 1) / kMergeWaves;
+    const int mblocks = g.B * Hq * (plan.mode == 1 ? merge_col_blocks<uint16_t>(kv.Dv)
+                                                   : merge_col_blocks<float>(kv.Dv));
     timing_begin("k_attn_merge", s);
     if (plan.mode != 1)
         hipLaunchKernelGGL((k_attn_merge<LSA_F32, float>), dim3(mblocks), dim3(64 * kMergeWaves), 0,

@@ -245,14 +245,16 @@ def test_pool_capacity_error_leaves_pool_unchanged(host_cold):
 
 # --------------------------------------------------------- bounded wait report
 def test_attention_wait_expiry_is_reported():
-    """The bf16 attention kernel's wait for its partner wave is bounded; with
-    the bound forced to zero polls every wait runs out at once (the kernel
-    still finishes), and lsa_device_status reports it (LSA_ERR_HIP, bit 0) and
-    clears it.  With the default bound the same launch is clean and gives the
-    reference output bit for bit."""
+    """The bf16 attention kernel that splits the dims over wave pairs (head
+    counts that are multiples of 32 but not of 64) bounds each wait for the
+    partner wave; with the bound forced to zero polls every wait runs out at
+    once (the kernel still finishes), and lsa_device_status reports it
+    (LSA_ERR_HIP, bit 0) and clears it.  With the default bound the same
+    launch is clean and gives the reference output bit for bit."""
     lsa = _lsa()
     R = _runner()
-    cfg = synth.small_config("expiry", 56, (9000, 4100), window=1024, idx=BF16, H=16, topk=256, steps=1)
+    cfg = synth.small_config("expiry", 56, (9000, 4100), window=1024, idx=BF16, H=16, topk=256, steps=1,
+                             Hq=32)
     inp = synth.generate(cfg)
     dev = R.DeviceInputs(inp)
     assert lsa.lsa_device_status() == (0, 0)
@@ -280,7 +282,7 @@ def test_window_pipeline_reports_wait_expiry():
     lsa = _lsa()
     R = _runner()
     cfg = synth.small_config("pipe_expiry", 57, (9000, 7000), window=1024, idx=FP8, H=16, topk=256, steps=2,
-                             planted=0.10)
+                             planted=0.10, Hq=96)
     cfg = synth.dataclasses.replace(cfg, windows=4, slots_per_req=80)
     inp = synth.generate(cfg)
     pipe = R.Pipeline(R.DeviceInputs(inp))

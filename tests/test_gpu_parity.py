@@ -54,6 +54,9 @@ def small(kind):
     if kind == "fp8_qf32":
         return synth.small_config("fp8_qf32", 27, (6000, 4000), window=1024, idx=FP8, H=16,
                                   topk=256, steps=1, q_dtype=F32)
+    if kind == "bf16_hq32":  # 32 attention heads: the wave-pair attention kernel
+        return synth.small_config("bf16_hq32", 28, (6000, 2600, 500), window=1024, idx=BF16, H=16,
+                                  Hq=32, topk=256, steps=2)
     if kind == "bf16_h128":
         return synth.small_config("bf16_h128", 24, (4000,), window=512, idx=BF16, H=16, Hq=128,
                                   topk=128, steps=1)
@@ -126,7 +129,7 @@ def _units(inp, full):
     return [(r, j % S) for j, r in enumerate(rs)]
 
 
-@pytest.mark.parametrize("kind", SMALL + ["cfg0", "cfg1", "cfg2", "cfg3"] + SIGNED)
+@pytest.mark.parametrize("kind", SMALL + ["bf16_hq32", "cfg0", "cfg1", "cfg2", "cfg3"] + SIGNED)
 def test_refine_topk_and_attention(kind):
     inp, dev, o = setup(kind)
     cfg = inp.cfg
