@@ -517,8 +517,8 @@ lsa_status lsa_ctx_state(const lsa_ctx* ctx, int32_t* seq_len, int32_t* hist_tok
  * Diagnostics: per-kernel timing.  While enabled, every kernel the library
  * launches is bracketed by two hipEvents recorded on the stream it is
  * launched on (adds a little launch overhead).  lsa_timing_read waits for
- * the recorded events and returns, for one kernel name (k_fuse_query,
- * k_score, k_select, k_refine, k_topk, k_refine_mfma, k_band_fine,
+ * the recorded events and returns, for one kernel name (k_score,
+ * k_select, k_select_tiles, k_refine, k_topk, k_refine_mfma, k_band_fine,
  * k_band_list, k_topk_band, k_attn_mla, k_attn_f32, k_attn_merge,
  * k_gather, k_stream_read, k_score_sig, k_select_ranked, k_chunk_ml, k_append_kv,
  * k_commit_chunk, k_commit_page, k_compact_recent, k_resolve_sel, k_key_norm2), the

@@ -28,9 +28,15 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // ---- launchers (each returns the launch error) ----
 hipError_t launch_fuse_query(const GeomDev& g, const void* q, lsa_dtype q_dt, const float* w,
                              int H, int d, float* qbar, hipStream_t s);
+// Chunk logits; with tmask the kernel also records, per tile of 64 chunks
+// (tile_off order), the mask of z > theta and its count, for
+// launch_select_tiles.
 hipError_t launch_score(const GeomDev& g, const void* kic, lsa_dtype kdt, const float* kscale,
                         const float* qbar, const float* bias, int d, float* z, hipStream_t s,
-                        bool combine = false);
+                        bool combine = false, float theta = 0.0f, uint64_t* tmask = nullptr,
+                        int32_t* tcount = nullptr);
+hipError_t launch_select_tiles(const GeomDev& g, const uint64_t* tmask, const int32_t* tcount,
+                               int32_t* sel, int32_t* cnt, hipStream_t s);
 hipError_t launch_score_sig(const GeomDev& g, const void* kic, lsa_dtype kdt, const float* kscale,
                             const void* q, lsa_dtype q_dt, const float* w, int H, const float* bias,
                             float theta, int d, float* S, hipStream_t s);

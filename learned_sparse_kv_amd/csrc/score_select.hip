@@ -23,7 +23,9 @@
 // chunks of one request; rows come in with coalesced 16-byte loads (the next
 // tile in flight while the current one is scored), go through a wave-private
 // LDS tile, and are read back one row per lane.  1 (bf16) to 2 (fp8) flop
-// per byte: HBM-bound.
+// per byte: HBM-bound.  The window pipeline has it record, per tile of 64
+// chunks, the mask of chunks with z > theta and its count, from which
+// k_select_tiles writes the ordered selection with one wave per tile.
 #include "lsa_internal.h"
 
 namespace {
@@ -114,7 +116,7 @@ template <int KDT, int D>
 __global__ __launch_bounds__((64 * score_waves<KDT, D>())) void k_score(
     GeomDev g, const uint8_t* __restrict__ kic, const float* __restrict__ kscale,
     const float* __restrict__ qbar, const float* __restrict__ bias, float* __restrict__ z,
-    int combine) {
+    int combine, float theta, uint64_t* __restrict__ tmask, int32_t* __restrict__ tcount) {
     constexpr int kScoreWaves = score_waves<KDT, D>();
     constexpr int EB = KDT == LSA_F32 ? 4 : (KDT == LSA_BF16 ? 2 : 1);
     constexpr int ROWB = D * EB;          // bytes per KIComp row
@@ -166,15 +168,24 @@ __global__ __launch_bounds__((64 * score_waves<KDT, D>())) void k_score(
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int c = t * 64 + lane;
         const float acc = row_dot<KDT, D>((const uint4*)(lt + lane * STRIDE), (const float4*)qs);
+        float zf = -INFINITY;
         if (c < nh) {
             const float zl = __builtin_fmaf(s, acc, br);
             // union over indexer layers: keep the earlier logit unless this one
             // is strictly larger (the per-chunk max, first of equals)
             if (combine) {
                 const float zo = z[off + c];
-                z[off + c] = zl > zo ? zl : zo;
+                zf = zl > zo ? zl : zo;
             } else {
-                z[off + c] = zl;
+                zf = zl;
+            }
+            z[off + c] = zf;
+        }
+        if (tmask) {  // uniform
+            const uint64_t m = __ballot(c < nh && zf > theta);
+            if (lane == 0) {
+                tmask[g.tile_off[r] + t] = m;
+                tcount[g.tile_off[r] + t] = __popcll(m);
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -230,6 +241,31 @@ __global__ __launch_bounds__(1024) void k_select(GeomDev g, const float* __restr
     if (threadIdx.x == 0) cnt[r] = base;
 }
 
+// Ordered compaction from the tile masks: one wave per tile of 64 chunks.
+// The wave adds the counts of its request's earlier tiles (a fixed-order
+// lane tree), then writes the chunk ids of its mask at their ranks; the wave
+// of a request's last tile writes the request's count.  Requests without
+// history chunks get their zero count from block 0.
+__global__ __launch_bounds__(256) void k_select_tiles(GeomDev g, const uint64_t* __restrict__ tmask,
+                                                     const int32_t* __restrict__ tcount,
+                                                     int32_t* __restrict__ sel,
+                                                     int32_t* __restrict__ cnt) {
+    const int lane = threadIdx.x & 63;
+    const int gt = blockIdx.x * 4 + (threadIdx.x >> 6);  // tile over all requests
+    if (blockIdx.x == 0 && threadIdx.x < g.B && g.nhist[threadIdx.x] == 0) cnt[threadIdx.x] = 0;
+    if (gt >= g.tile_off[g.B]) return;  // whole wave
+    int r = 0;
+    while (g.tile_off[r + 1] <= gt) ++r;  // uniform
+    const int t0 = g.tile_off[r], t = gt - t0;
+    const uint64_t m = tmask[gt];
+    int pre = 0;
+    for (int i = lane; i < t; i += 64) pre += tcount[t0 + i];
+    for (int o = 32; o > 0; o >>= 1) pre += __shfl_xor(pre, o);
+    const int64_t off = g.chunk_off[r];
+    if ((m >> lane) & 1ull) sel[off + pre + __popcll(m & ((1ull << lane) - 1ull))] = t * 64 + lane;
+    if (t == g.tile_off[r + 1] - t0 - 1 && lane == 0) cnt[r] = pre + __popcll(m);
+}
+
 }  // namespace
 
 hipError_t launch_fuse_query(const GeomDev& g, const void* q, lsa_dtype q_dt, const float* w,
@@ -245,7 +281,7 @@ hipError_t launch_fuse_query(const GeomDev& g, const void* q, lsa_dtype q_dt, co
 
 hipError_t launch_score(const GeomDev& g, const void* kic, lsa_dtype kdt, const float* kscale,
                         const float* qbar, const float* bias, int d, float* z, hipStream_t s,
-                        bool combine) {
+                        bool combine, float theta, uint64_t* tmask, int32_t* tcount) {
     const int tiles = g.tile_off[g.B];
     if (tiles == 0) return hipSuccess;
     int mt = 0;  // tiles of the longest request
@@ -257,7 +293,7 @@ hipError_t launch_score(const GeomDev& g, const void* kic, lsa_dtype kdt, const 
         timing_begin("k_score", s);                                                             \
         hipLaunchKernelGGL((k_score<KDT, D>), dim3((mt + 2 * nw - 1) / (2 * nw), g.B),           \
                            dim3(64 * nw), 0, s,                                                 \
-                           g, k, kscale, qbar, bias, z, combine ? 1 : 0);                       \
+                           g, k, kscale, qbar, bias, z, combine ? 1 : 0, theta, tmask, tcount); \
         timing_end("k_score", s);                                                               \
         return hipGetLastError();                                                               \
     }
@@ -276,5 +312,15 @@ hipError_t launch_select(const GeomDev& g, const float* z, float theta, int32_t*
     timing_begin("k_select", s);
     hipLaunchKernelGGL(k_select, dim3(g.B), dim3(1024), 0, s, g, z, theta, sel, cnt);
     timing_end("k_select", s);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_tiles(const GeomDev& g, const uint64_t* tmask, const int32_t* tcount,
+                               int32_t* sel, int32_t* cnt, hipStream_t s) {
+    const int tiles = g.tile_off[g.B];
+    timing_begin("k_select_tiles", s);
+    hipLaunchKernelGGL(k_select_tiles, dim3(tiles > 0 ? (tiles + 3) / 4 : 1), dim3(256), 0, s, g,
+                       tmask, tcount, sel, cnt);
+    timing_end("k_select_tiles", s);
     return hipGetLastError();
 }

@@ -23,6 +23,8 @@ struct lsa_ctx {
     AttnPlan plan;
     int64_t nh = 0;
     float* qbar = nullptr;
+    uint64_t* tmask = nullptr;   // per tile of 64 chunks: the mask of z > theta
+    int32_t* tcount = nullptr;   // and its count
     float* z = nullptr;
     int32_t* sel[2] = {nullptr, nullptr};
     int32_t* cnt[2] = {nullptr, nullptr};
@@ -82,15 +84,22 @@ lsa_status ctx_plan(const lsa_ctx_desc* d, const GeomDev& g, AttnPlan* plan) {
     return attn_plan(gp, &d->kv, d->Hq, d->k, 0, plan);
 }
 
+// Tiles of 64 history chunks the scoring may cover: the requests' chunk
+// capacities when the history grows, else their chunk counts.
+size_t tile_cap(const GeomDev& g, const lsa_ctx_desc* d) {
+    if (d->geom.chunk_cap > 0) return (size_t)g.B * ((d->geom.chunk_cap + 63) / 64);
+    return (size_t)g.tile_off[g.B];
+}
+
 // Workspace layout; returns total bytes (0 on invalid description).
-size_t layout(const lsa_ctx_desc* d, GeomDev* g, AttnPlan* plan, size_t offs[15]) {
+size_t layout(const lsa_ctx_desc* d, GeomDev* g, AttnPlan* plan, size_t offs[16]) {
     if (!d) return 0;
     if (geom_derive(&d->geom, g) != LSA_OK) return 0;
     if (ctx_plan(d, *g, plan) != LSA_OK) return 0;
     const int64_t nh = g->chunk_off[g->B];
     const int B = g->B;
     Carve c;
-    offs[0] = c.take((size_t)B * d->d * 4);             // qbar
+    offs[0] = c.take((tile_cap(*g, d) + 1) * 12);      // tile masks, then tile counts
     offs[1] = c.take((size_t)nh * 4);                   // z
     offs[2] = c.take((size_t)nh * 4);                   // sel[0]
     offs[3] = c.take((size_t)nh * 4);                   // sel[1]
@@ -106,6 +115,7 @@ size_t layout(const lsa_ctx_desc* d, GeomDev* g, AttnPlan* plan, size_t offs[15]
     offs[12] = c.take((size_t)nh * 4);                  // pages of the selected chunks
     offs[13] = c.take((size_t)nh * 4);                  // their scales
     offs[14] = c.take((size_t)nh * LSA_CHUNK * 4);      // |key|^2 of their tokens
+    offs[15] = c.take((size_t)B * d->d * 4);            // fused queries
     return c.off;
 }
 
@@ -123,14 +133,17 @@ lsa_status score_select(lsa_ctx* x, const GeomDev& g, const lsa_trigger_in* t, i
         if (x->nh > 0 && !t[l].kic) return LSA_ERR_INVALID_ARG;
         if (x->nh > 0 && d.idx_dt == LSA_FP8_E4M3FN && !t[l].kic_scale) return LSA_ERR_INVALID_ARG;
     }
+    // the last layer's launch records the tile masks of the union's logits
     for (int l = 0; l < nl; ++l) {
+        const bool last = l == nl - 1;
         if (launch_fuse_query(g, t[l].q, d.q_dt, t[l].w, d.H, d.d, x->qbar, s) != hipSuccess)
             return LSA_ERR_HIP;
         if (launch_score(g, t[l].kic, d.idx_dt, t[l].kic_scale, x->qbar, t[l].bias, d.d, x->z, s,
-                         l > 0) != hipSuccess)
+                         l > 0, d.theta, last ? x->tmask : nullptr,
+                         last ? x->tcount : nullptr) != hipSuccess)
             return LSA_ERR_HIP;
     }
-    if (launch_select(g, x->z, d.theta, x->sel[buf], x->cnt[buf], s) != hipSuccess)
+    if (launch_select_tiles(g, x->tmask, x->tcount, x->sel[buf], x->cnt[buf], s) != hipSuccess)
         return LSA_ERR_HIP;
     if (x->nh > 0 && hipMemcpyAsync(x->h_sel[buf], x->sel[buf], (size_t)x->nh * 4,
                                     hipMemcpyDeviceToHost, s) != hipSuccess)
@@ -149,7 +162,7 @@ extern "C" {
 size_t lsa_ctx_ws_bytes(const lsa_ctx_desc* desc) {
     GeomDev g;
     AttnPlan p;
-    size_t offs[15];
+    size_t offs[16];
     return layout(desc, &g, &p, offs);
 }
 
@@ -158,7 +171,7 @@ lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc) {
     *ctx = nullptr;
     GeomDev g;
     AttnPlan plan;
-    size_t offs[15];
+    size_t offs[16];
     lsa_status st = geom_derive(&desc->geom, &g);
     if (st != LSA_OK) return st;
     if (desc->d != 64 && desc->d != 128) return LSA_ERR_UNSUPPORTED;
@@ -202,7 +215,9 @@ lsa_status lsa_ctx_create(lsa_ctx** ctx, const lsa_ctx_desc* desc) {
     x->recent_cap = desc->geom.recent_cap;
     x->rmax = rmax;
     uint8_t* base = (uint8_t*)desc->ws;
-    x->qbar = (float*)(base + offs[0]);
+    x->qbar = (float*)(base + offs[15]);
+    x->tmask = (uint64_t*)(base + offs[0]);
+    x->tcount = (int32_t*)(base + offs[0] + (tile_cap(g, desc) + 1) * 8);
     x->z = (float*)(base + offs[1]);
     x->sel[0] = (int32_t*)(base + offs[2]);
     x->sel[1] = (int32_t*)(base + offs[3]);

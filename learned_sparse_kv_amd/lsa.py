@@ -392,7 +392,7 @@ def lsa_step64(ctx: Ctx, win, out, main=None, copy=None):
 
 
 # ---------------------------------------------------------------- diagnostics
-KERNELS = ("k_fuse_query", "k_score", "k_select", "k_refine", "k_topk", "k_refine_mfma",
+KERNELS = ("k_fuse_query", "k_score", "k_select", "k_select_tiles", "k_refine", "k_topk", "k_refine_mfma",
            "k_band_fine", "k_band_list", "k_topk_band", "k_attn_mla", "k_attn_f32", "k_attn_merge",
            "k_gather", "k_stream_read", "k_score_sig", "k_select_ranked", "k_chunk_ml",
            "k_append_kv", "k_commit_chunk", "k_commit_page", "k_compact_recent", "k_resolve_sel",
