@@ -158,9 +158,10 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
     constexpr int HB = H / 16;   // head blocks
     constexpr int NR = KDT == LSA_BF16 ? KS : KS / 2;  // 16-byte key loads per token row and lane
     constexpr int QROW = D * 2 + 16;      // bytes per query row in LDS (padded: no bank conflicts)
-    // key buffers in flight: two with fp8 keys (8 registers per 16 tokens),
-    // one with bf16 keys (16 per 16 tokens)
-    constexpr int NBUF = NR * 4 * 4 <= 32 ? 2 : 1;
+    // key buffers in flight ahead of the chunk computed: one.  A second with
+    // fp8 keys (8 registers per 16 tokens) kept the same occupancy (2 waves
+    // per SIMD) and was slower: 20.5 against 19.4 us per step at 500K batch 8.
+    constexpr int NBUF = 1;
     __shared__ uint32_t hl[2 * kCoarse];  // coarse L bins, then coarse U bins
     __shared__ __attribute__((aligned(16))) uint8_t qs[H * QROW];
 
