@@ -134,15 +134,15 @@ __device__ __forceinline__ void load_hist(const uint32_t* gh, uint32_t* lds) {
 }
 
 // ---------------------------------------------------------------------------
-// K1.  Grid (X, B): block x of request r takes chunks x*4 + wave, stepping by
-// 4X.  The query rows are the A operands (rows = heads), a chunk's key rows
+// K1.  Grid (X, B): wave x*4 + v of request r takes the whole chunks
+// x*4 + v + j*4X below 4X * floor(n / 4X), n the request's selection count,
+// and a run of at most four 16-token parts of the remaining chunks.  The query rows are the A operands (rows = heads), a chunk's key rows
 // the B operands (columns = tokens), so D = Q K^T leaves each lane four heads
 // of one token: the weighted head sum runs inside the lane and across the
 // four lane groups by two permlane swaps, with no trip through LDS.  Key rows
 // stay in flight ahead of the chunk being computed: each 16-token part of a
-// key buffer is refilled with the next chunk's part as soon as it has been
-// converted (with fp8 keys two buffers alternate, so two chunks are in
-// flight).  The block's coarse histograms go to the request's (hist, zero on
+// key buffer is refilled with the next chunk's part (or the wave's remainder
+// part) as soon as it has been converted.  The block's coarse histograms go to the request's (hist, zero on
 // entry) with one atomic per nonzero bin.
 template <int KDT, int D, int H>
 __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_refine_mfma(
@@ -158,14 +158,14 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
     constexpr int HB = H / 16;   // head blocks
     constexpr int NR = KDT == LSA_BF16 ? KS : KS / 2;  // 16-byte key loads per token row and lane
     constexpr int QROW = D * 2 + 16;      // bytes per query row in LDS (padded: no bank conflicts)
-    // key buffers in flight ahead of the chunk computed: one.  A second with
+    // One key buffer is in flight ahead of the chunk computed.  A second with
     // fp8 keys (8 registers per 16 tokens) kept the same occupancy (2 waves
     // per SIMD) and was slower: 20.5 against 19.4 us per step at 500K batch 8.
-    constexpr int NBUF = 1;
     __shared__ uint32_t hl[2 * kCoarse];  // coarse L bins, then coarse U bins
     __shared__ __attribute__((aligned(16))) uint8_t qs[H * QROW];
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, lq = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = blockIdx.y, X = gridDim.x;
     const int64_t off = g.chunk_off[r];
     const int nhr = g.nhist[r];
@@ -198,27 +198,46 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
     const int nj_max = i0 < nhr ? (nhr - i0 + stride - 1) / stride : 0;
     load_idx(0, nj_max);
     const int nc = cnt[r];
-    const int nj = i0 < nc ? (nc - i0 + stride - 1) / stride : 0;
-    // key rows: B operands of tokens tb*16 + l16, 16 bytes per load.  Each
-    // buffer carries its chunk's page base and scale, taken from the index
-    // window together: the window may move on (to the chunks 64 further)
-    // before the buffer's chunk is computed.
-    uint4 buf[NBUF][4][NR];
-    const uint8_t* bbase[NBUF];
-    float bsc[NBUF];
-    auto set_chunk = [&](int j, int b) __attribute__((always_inline)) {
+    // Work: every wave takes nj = nc / stride whole chunks (i0 + j * stride);
+    // the 16-token parts of the remaining chunks (selection indices
+    // nj * stride ..) are spread over all the request's waves, at most four
+    // consecutive parts a wave, so that no wave does a whole chunk more than
+    // another.
+    const int nj = nc / stride;
+    const int rem = nc - nj * stride;
+    const int pr0 = (int)((4LL * rem * i0) / stride), pr1 = (int)((4LL * rem * (i0 + 1)) / stride);
+    // key rows: B operands of tokens tb*16 + l16, 16 bytes per load; slot tb
+    // holds part tb of the chunk computed next (or a remainder part)
+    uint4 buf[4][NR];
+    auto load_part = [&](const uint8_t* base, int tb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = 0; n < NR; ++n)
+            buf[tb][n] = *(const uint4*)(base + (tb * 16 + l16) * ROWB + n * 64 + lq * 16);
+    };
+    // page base and scale of the chunk with selection index j (of this
+    // wave's whole chunks), from the index window
+    auto win_chunk = [&](int j, const uint8_t*& base, float& scale) __attribute__((always_inline)) {
         const int src = j & 63;
         const int64_t pgo = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pg_l, src) |
                             ((int64_t)__builtin_amdgcn_readlane((int)(pg_l >> 32), src) << 32);
-        bbase[b] = pages + pgo * page_bytes + ikey_off;
-        bsc[b] = 1.0f;
+        base = pages + pgo * page_bytes + ikey_off;
+        scale = 1.0f;
         if constexpr (KDT == LSA_FP8_E4M3FN)
-            bsc[b] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), src));
+            scale = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_l), src));
     };
-    auto load_part = [&](int b, int tb) __attribute__((always_inline)) {
-#pragma unroll
-        for (int n = 0; n < NR; ++n)
-            buf[b][tb][n] = *(const uint4*)(bbase[b] + (tb * 16 + l16) * ROWB + n * 64 + lq * 16);
+    // the same for a remainder chunk (selection index i), loaded directly
+    auto rem_chunk = [&](int i, const uint8_t*& base, float& scale) __attribute__((always_inline)) {
+        int64_t e, pg;
+        if (sel_slot) {
+            e = off + i;
+            pg = (int64_t)sel_slot[e];
+        } else {
+            e = off + min(max(sel[off + i], 0), nhr - 1);
+            pg = page_table ? (int64_t)page_table[e] : e;
+        }
+        base = pages + pg * page_bytes + ikey_off;
+        scale = 1.0f;
+        if constexpr (KDT == LSA_FP8_E4M3FN) scale = scl[e];
     };
     // the query rows load once per block into LDS (each wave takes its
     // operands from there)
@@ -238,21 +257,39 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
     }
     for (int i = tid; i < 2 * kCoarse; i += 64 * kWaves) hl[i] = 0;
     lds_barrier();
-    if ((int)blockIdx.x * kWaves < nc) {  // uniform across the block
+    if (nj > 0 || pr1 > pr0) {  // uniform per wave
         uint4 qa[HB][KS];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 qa[hb][ks] = *(const uint4*)(qs + (hb * 16 + l16) * QROW + kdim<KDT>(ks, lq) * 2);
-        // the chunks ahead of j, one per buffer, have their pages known
+        // The remainder parts [pr0, pr1) lie in at most two chunks, rc0 and
+        // rc0 + 1, and each has a slot of its own (part p sits in slot p % 4):
+        // all of them load together, after the wave's last whole chunk.
+        const int rc0 = nj * stride + (pr0 >> 2);
+        const uint8_t *rb0 = nullptr, *rb1 = nullptr;
+        float rs0 = 1.0f, rs1 = 1.0f;
+        if (pr1 > pr0) rem_chunk(rc0, rb0, rs0);
+        if (pr1 > pr0 && ((pr1 - 1) >> 2) != (pr0 >> 2)) rem_chunk(rc0 + 1, rb1, rs1);
+        // the remainder part of slot tb, or -1
+        auto rem_part = [&](int tb) __attribute__((always_inline)) {
+            const int p = pr0 + ((tb - pr0) & 3);
+            return p < pr1 ? p : -1;
+        };
+        auto load_rem = [&](int tb) __attribute__((always_inline)) {
+            const int p = rem_part(tb);
+            if (p >= 0) load_part((p >> 2) != (pr0 >> 2) ? rb1 : rb0, tb);
+        };
+        const uint8_t* cbase = nullptr;  // the whole chunk in the slots
+        float cscale = 1.0f;
+        if (nj > 0) {
+            win_chunk(0, cbase, cscale);
 #pragma unroll
-        for (int b = 0; b < NBUF; ++b) {
-            if (b < nj) {
-                set_chunk(b, b);
+            for (int tb = 0; tb < 4; ++tb) load_part(cbase, tb);
+        } else {
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb) load_part(b, tb);
-            }
+            for (int tb = 0; tb < 4; ++tb) load_rem(tb);
         }
         // Wq = sum_h |w_h| * |q_h|_2 (rounded up), from the operands held:
         // lane (l16, lq) has dims lq*8.. of every k-step of head hb*16 + l16
@@ -270,73 +307,62 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
         for (int o = 1; o < 16; o <<= 1) part += __shfl_xor(part, o);
         const float wq = part * (1.0f + gam(H + 8));
 
-        // one chunk from buffer b: refill each 16-token part with chunk j + NBUF's
-        // as soon as it is converted; lane = token of the chunk at the end
-        auto chunk = [&](int j, int b) __attribute__((always_inline)) {
-            const int i = i0 + j * stride;
-            // |key|^2 of the lane's token, formed once per window when given
-            const float kn2_pre = kn2g ? kn2g[(off + i) * 64 + lane] : 0.0f;
-            const float scale = bsc[b];
-            const bool more = j + NBUF < nj;
-            float mI = 0.0f, mW = 0.0f, mK = 0.0f;
+        // slot tb's key rows as bf16 operands
+        auto operands = [&](int tb, uint4 (&ka)[KS]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                uint4 ka[KS];
+            for (int ks = 0; ks < KS; ++ks) {
+                if constexpr (KDT == LSA_BF16) ka[ks] = buf[tb][ks];
+                else ka[ks] = (ks & 1) ? fp8x8_to_bf16x8(buf[tb][ks >> 1].z, buf[tb][ks >> 1].w)
+                                       : fp8x8_to_bf16x8(buf[tb][ks >> 1].x, buf[tb][ks >> 1].y);
+            }
+        };
+        // the weighted ReLU sums and (unless given) |key|^2 of tokens
+        // tb*16 + l16, kept by the lanes of group lq == tb
+        auto sums = [&](int tb, const uint4 (&ka)[KS], float& mI, float& mW, float& mK)
+            __attribute__((always_inline)) {
+            // |key|^2 on the matrix cores (unless given): the diagonal of the
+            // 16x16 Gram block; lane (l16, lq) holds rows 4lq..4lq+3 of
+            // column l16, so the diagonal of column l16 sits in lane group
+            // l16 / 4, element l16 % 4
+            if (!kn2g) {  // uniform
+                f32x4_t gm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    if constexpr (KDT == LSA_BF16) ka[ks] = buf[b][tb][ks];
-                    else ka[ks] = (ks & 1) ? fp8x8_to_bf16x8(buf[b][tb][ks >> 1].z, buf[b][tb][ks >> 1].w)
-                                           : fp8x8_to_bf16x8(buf[b][tb][ks >> 1].x, buf[b][tb][ks >> 1].y);
-                }
-                if (more) {
-                    if (tb == 0) {
-                        // the index window moves 64 chunks at a time; the chunks
-                        // in flight already hold their pages and scales
-                        if (((j + NBUF) & 63) == 0) load_idx(j + NBUF, nj);
-                        set_chunk(j + NBUF, b);
-                    }
-                    load_part(b, tb);
-                }
-                // |key|^2 on the matrix cores (unless given): the diagonal of the
-                // 16x16 Gram block; lane (l16, lq) holds rows 4lq..4lq+3 of
-                // column l16, so the diagonal of column l16 sits in lane group
-                // l16 / 4, element l16 % 4
-                if (!kn2g) {  // uniform
-                    f32x4_t gm = {0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks < KS; ++ks)
+                    gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
+                                                                 __builtin_bit_cast(bf16x8_t, ka[ks]), gm, 0, 0, 0);
+                const int e = l16 & 3;
+                const float dv = e == 0 ? gm[0] : (e == 1 ? gm[1] : (e == 2 ? gm[2] : gm[3]));
+                const float dg = __shfl(dv, (l16 >> 2) * 16 + l16);
+                if (lq == tb) mK = dg;
+            }
+            // a'[head hb*16 + 4lq + e][token tb*16 + l16]; weighted ReLU sums
+            // over the lane's heads, then over the four lane groups
+            float sI = 0.0f, sW = 0.0f;
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
-                                                                     __builtin_bit_cast(bf16x8_t, ka[ks]), gm, 0, 0, 0);
-                    const int e = l16 & 3;
-                    const float dv = e == 0 ? gm[0] : (e == 1 ? gm[1] : (e == 2 ? gm[2] : gm[3]));
-                    const float dg = __shfl(dv, (l16 >> 2) * 16 + l16);
-                    if (lq == tb) mK = dg;
-                }
-                // a'[head hb*16 + 4lq + e][token tb*16 + l16]; weighted ReLU sums
-                // over the lane's heads, then over the four lane groups
-                float sI = 0.0f, sW = 0.0f;
+            for (int hb = 0; hb < HB; ++hb) {
+                f32x4_t c4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb) {
-                    f32x4_t c4 = {0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks < KS; ++ks)
+                    c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[hb][ks]),
+                                                                 __builtin_bit_cast(bf16x8_t, ka[ks]), c4, 0, 0, 0);
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[hb][ks]),
-                                                                     __builtin_bit_cast(bf16x8_t, ka[ks]), c4, 0, 0, 0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float rr = relu(c4[e]);
-                        sI = __builtin_fmaf(wl[hb][e], rr, sI);
-                        sW = __builtin_fmaf(fabsf(wl[hb][e]), rr, sW);
-                    }
-                }
-                sI = add_xor32(add_xor16(sI));
-                sW = add_xor32(add_xor16(sW));
-                if (lq == tb) {  // lane lq * 16 + l16 keeps token tb * 16 + l16
-                    mI = sI;
-                    mW = sW;
+                for (int e = 0; e < 4; ++e) {
+                    const float rr = relu(c4[e]);
+                    sI = __builtin_fmaf(wl[hb][e], rr, sI);
+                    sW = __builtin_fmaf(fabsf(wl[hb][e]), rr, sW);
                 }
             }
-            const float kn2 = kn2g ? kn2_pre : mK;
+            sI = add_xor32(add_xor16(sI));
+            sW = add_xor32(add_xor16(sW));
+            if (lq == tb) {  // lane lq * 16 + l16 keeps token tb * 16 + l16
+                mI = sI;
+                mW = sW;
+            }
+        };
+        // the (L, U) keys of the lane's token of chunk i, and its coarse bins
+        auto emit = [&](int64_t i, float scale, float mI, float mW, float mK) __attribute__((always_inline)) {
+            // |key|^2 of the lane's token, formed once per window when given
+            const float kn2 = kn2g ? kn2g[(off + i) * 64 + lane] : mK;
             const float kn = sqrtf(kn2 * (1.0f + gam(D + 8))) * (1.0f + 4 * kU2);
             const float ek = gam(D) * 2.0f * kn * wq;  // sum_h |w_h| eps_h
             float E = ek + 2.0f * gam(H + 24) * (mW + ek);
@@ -347,15 +373,42 @@ __global__ __launch_bounds__(64 * kWaves, (H * D > 64 * 128 ? 1 : 2)) void k_ref
             atomicAdd(&hl[kL >> 22], 1u);
             atomicAdd(&hl[kCoarse + (kU >> 22)], 1u);
         };
-        if constexpr (NBUF == 2) {
-            int j = 0;
-            for (; j + 1 < nj; j += 2) {
-                chunk(j, 0);
-                chunk(j + 1, 1);
+        // whole chunk j: each 16-token slot is refilled as soon as it is
+        // converted, with chunk j + 1's part, or after the last whole chunk
+        // with the wave's remainder part of that slot
+        for (int j = 0; j < nj; ++j) {
+            const int i = i0 + j * stride;
+            const float scale = cscale;
+            const bool more = j + 1 < nj;
+            const uint8_t* nbase = nullptr;
+            if (more) {
+                // the index window moves 64 chunks at a time; the chunk in
+                // flight already holds its page and scale
+                if (((j + 1) & 63) == 0) load_idx(j + 1, nj);
+                win_chunk(j + 1, nbase, cscale);
             }
-            if (j < nj) chunk(j, 0);
-        } else {
-            for (int j = 0; j < nj; ++j) chunk(j, 0);
+            float mI = 0.0f, mW = 0.0f, mK = 0.0f;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                uint4 ka[KS];
+                operands(tb, ka);
+                if (more) load_part(nbase, tb);
+                else load_rem(tb);
+                sums(tb, ka, mI, mW, mK);
+            }
+            emit(i, scale, mI, mW, mK);
+        }
+        // the remainder parts: lanes of group lq == tb keep token tb*16 + l16
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const int p = rem_part(tb);
+            if (p < 0) continue;  // uniform
+            const bool second = (p >> 2) != (pr0 >> 2);
+            uint4 ka[KS];
+            operands(tb, ka);
+            float mI = 0.0f, mW = 0.0f, mK = 0.0f;
+            sums(tb, ka, mI, mW, mK);
+            if (lq == tb) emit(rc0 + (second ? 1 : 0), second ? rs1 : rs0, mI, mW, mK);
         }
     }
     lds_barrier();

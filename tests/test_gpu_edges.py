@@ -84,12 +84,13 @@ def test_threshold_at_zero_logit(idx):
 
 
 # ------------------------------------------------ long walks of the refine pass
-@pytest.mark.parametrize("idx", ["fp8", "bf16"])
-def test_refine_one_block_per_request(idx):
-    """One refine block per request (forced), so each of its four waves walks
+@pytest.mark.parametrize("idx,blocks", [("fp8", 1), ("bf16", 1), ("fp8", 5), ("bf16", 7)])
+def test_refine_one_block_per_request(idx, blocks):
+    """Few refine blocks per request (forced), so each wave walks dozens to
     more than 128 of the request's chunks and its 64-chunk index window moves
-    while the next chunks' key rows are in flight (two ahead with fp8 keys,
-    one with bf16).  Every chunk selected, signed head weights: the top-k
+    while the next chunk's key rows are in flight; the chunks left over after
+    the whole-chunk rounds are split into 16-token parts, a run of which can
+    span two chunks.  Every chunk selected, signed head weights: the top-k
     bit for bit as the oracle's, and as the default launch shape's."""
     lsa = _lsa()
     dt = FP8 if idx == "fp8" else BF16
@@ -102,7 +103,7 @@ def test_refine_one_block_per_request(idx):
     _, sel_o, cnt_o = o.score_select(theta=float("-inf"))
     assert int(cnt_o[0]) // 4 >= 128
     for j in range(2):
-        lsa.lsa_tune_set(lsa.TUNE_REFINE_BLOCKS, 1)
+        lsa.lsa_tune_set(lsa.TUNE_REFINE_BLOCKS, blocks)
         try:
             topk1, tcnt1 = dev.refine_topk(sel, cnt, j, cfg.topk)
             torch.cuda.synchronize()
@@ -114,7 +115,8 @@ def test_refine_one_block_per_request(idx):
             a = int(inp["chunk_off"][r])
             want = o.refine_topk(r, sel_o[a:a + cnt_o[r]], inp["q_refine"][j, r], inp["w_refine"][j, r],
                                  cfg.topk)
-            print(f"[walk] {idx} step={j} request={r} candidates={int(cnt_o[r]) * 64}", flush=True)
+            print(f"[walk] {idx} blocks={blocks} step={j} request={r} candidates={int(cnt_o[r]) * 64}",
+                  flush=True)
             got1 = topk1.cpu().numpy()[r, :int(tcnt1[r])]
             got0 = topk0.cpu().numpy()[r, :int(tcnt0[r])]
             assert np.array_equal(got1, want), (j, r)
