@@ -314,14 +314,16 @@ def test_window_pipeline_matches_oracle(host_cold, variant):
     pipe.close()
 
 
-def test_window_pipeline_full_size_sampled():
-    """lsa_step64 on the 500K-token, batch-8 workload with the pinned-host cold
-    tier, 64 steps per window as the bench times it, over two windows with
-    2 % drift: sampled (request, step) units against the oracle (top-k bit
-    for bit, attention within tolerance) and every window's fetch count
-    against the pool simulation."""
+@pytest.mark.parametrize("workload", [4, 2])
+def test_window_pipeline_full_size_sampled(workload):
+    """lsa_step64 at full size, 64 steps per window as the bench times it,
+    over two windows with 2 % drift: the 500K-token batch of 8 (fp8 index
+    keys, pinned-host cold tier) and the ragged 32K-128K batch of 16 (bf16
+    index keys, HBM cold tier).  Sampled (request, step) units against the
+    oracle (top-k bit for bit, attention within tolerance) and every
+    window's fetch count against the pool simulation."""
     R = _runner()
-    cfg = synth.dataclasses.replace(synth.config(4), windows=3)
+    cfg = synth.dataclasses.replace(synth.config(workload), windows=3, drift=0.02)
     inp = synth.generate(cfg, steps=64, threads=16)
     dev = R.DeviceInputs(inp)
     pipe = R.Pipeline(dev)
