@@ -314,19 +314,23 @@ def test_window_pipeline_matches_oracle(host_cold, variant):
     pipe.close()
 
 
-@pytest.mark.parametrize("workload", [4, 2])
-def test_window_pipeline_full_size_sampled(workload):
+@pytest.mark.parametrize("workload,n_layers", [(4, 1), (2, 1), (4, 3)])
+def test_window_pipeline_full_size_sampled(workload, n_layers):
     """lsa_step64 at full size, 64 steps per window as the bench times it,
     over two windows with 2 % drift: the 500K-token batch of 8 (fp8 index
-    keys, pinned-host cold tier) and the ragged 32K-128K batch of 16 (bf16
-    index keys, HBM cold tier).  Sampled (request, step) units against the
-    oracle (top-k bit for bit, attention within tolerance) and every
-    window's fetch count against the pool simulation."""
+    keys, pinned-host cold tier), also with every trigger selecting the OR
+    union of three indexer layers (slots for a window's 2,200 or so chunks), and
+    the ragged 32K-128K batch of 16 (bf16 index keys, HBM cold tier).
+    Sampled (request, step) units against the oracle (top-k bit for bit,
+    attention within tolerance) and every window's fetch count against the
+    pool simulation."""
     R = _runner()
     cfg = synth.dataclasses.replace(synth.config(workload), windows=3, drift=0.02)
+    if n_layers > 1:
+        cfg = synth.dataclasses.replace(cfg, slots_per_req=3072)
     inp = synth.generate(cfg, steps=64, threads=16)
     dev = R.DeviceInputs(inp)
-    pipe = R.Pipeline(dev)
+    pipe = R.Pipeline(dev, n_layers=n_layers)
     B, S, windows = cfg.batch, 64, 2
     print(f"[setup] {cfg.name}: n_hist={list(inp['n_hist'])} slots/request={pipe.spr}", flush=True)
     st0, _ = pipe.prime()
@@ -345,7 +349,10 @@ def test_window_pipeline_full_size_sampled(workload):
     samples = [[(0, 0), (B // 2, 31), (B - 1, S - 1)], [(1, 63), (B - 2, 1)]]
     for m in range(windows):
         o = oracle.Oracle(inp, kic=inp["kic_windows"][m], kic_scale=inp["kic_scale_windows"][m])
-        _, sel_o, cnt_o = o.score_select()
+        if n_layers > 1:
+            _, sel_o, cnt_o = o.score_select_union(synth.indexer_layers(inp, n_layers, window=m))
+        else:
+            _, sel_o, cnt_o = o.score_select()
         for r in range(B):
             a = int(inp["chunk_off"][r])
             per_req_sets[r].append(set(sel_o[a:a + cnt_o[r]].tolist()))
