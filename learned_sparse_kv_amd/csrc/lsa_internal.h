@@ -144,13 +144,22 @@ void timing_end(const char* name, hipStream_t s);
 // Matrix-core refine with an exact re-score band (refine_band.hip).
 bool band_supported(lsa_dtype idx_dt, lsa_dtype q_dt, int H, int d);
 size_t band_ws_bytes(const GeomDev& g);
+// A growing context's new KV rows, one per request (rows: B * n16 16-byte
+// units), for the band's fine-histogram pass to write at the end of each
+// request's recent rows (row rec_off[r] + nrec[r] - 1); rows null: none.
+struct AppendRow {
+    const uint8_t* rows = nullptr;
+    uint8_t* recent = nullptr;
+    int32_t n16 = 0;  // 16-byte units per row, at most 256
+};
 hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_t* cnt,
                               const void* pages, int64_t page_bytes, int64_t ikey_off,
                               const int32_t* page_table, lsa_dtype idx_dt,
                               const float* ikey_scale, const int32_t* sel_slot,
                               const float* sel_scale, const float* kn2, const void* q,
                               const float* w, int H, int d, int k, int32_t* topk, int32_t* tcnt,
-                              void* ws, bool ws_clean, hipStream_t s);
+                              void* ws, bool ws_clean, hipStream_t s,
+                              const AppendRow& app = AppendRow());
 // |key|^2 of every token of the selected chunks (selection order, 64 per
 // chunk) for launch_refine_band's kn2 (nullptr: formed there per step).
 hipError_t launch_key_norm2(const GeomDev& g, const int32_t* cnt, const int32_t* sel_slot,

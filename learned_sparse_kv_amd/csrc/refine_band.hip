@@ -504,16 +504,25 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
     GeomDev g, const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
     const uint2* __restrict__ lu, int k, uint32_t* __restrict__ hist, int4* __restrict__ cinfo,
     int32_t* __restrict__ plist, int32_t* __restrict__ pcnt, int32_t* __restrict__ topk,
-    int32_t* __restrict__ tcnt) {
+    int32_t* __restrict__ tcnt, AppendRow app) {
     __shared__ __attribute__((aligned(16))) uint32_t hf[2 * kFine];
     __shared__ int wsum[kWaves], s_out[4], s_np[kPre][kWaves];
     const int r = blockIdx.y, X = gridDim.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // a growing context's new row for the request (block 0): requested now,
+    // stored at the end, so that its latency overlaps the block's work
+    const bool app_on = app.rows && blockIdx.x == 0 && tid < app.n16;
+    uint4 app_v = make_uint4(0u, 0u, 0u, 0u);
+    if (app_on) app_v = ((const uint4*)(app.rows + (int64_t)r * app.n16 * 16))[tid];
+    auto app_store = [&]() __attribute__((always_inline)) {
+        if (app_on) ((uint4*)(app.recent + (g.rec_off[r] + g.nrec[r] - 1) * (int64_t)app.n16 * 16))[tid] = app_v;
+    };
     const int nc = cnt[r], n = nc * 64;
     const int64_t off = g.chunk_off[r];
     if (n <= k) {  // every candidate is kept, already in token order
         for (int p = blockIdx.x * blockDim.x + tid; p < n; p += X * blockDim.x)
             topk[(int64_t)r * k + p] = sel[off + (p >> 6)] * 64 + (p & 63);
         if (blockIdx.x == 0 && tid == 0) tcnt[r] = n;
+        app_store();
         return;
     }
     int c0, c1;
@@ -579,6 +588,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_band_fine(
     uint32_t* gf = gh + 2 * kCoarse;
     for (int i = tid; i < 2 * kFine; i += blockDim.x)
         if (hf[i]) atomicAdd(&gf[i], hf[i]);
+    app_store();
 }
 
 // K3.  Grid (X, B).  Block x lists, in token order, the band candidates
@@ -1131,7 +1141,7 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
                               const float* ikey_scale, const int32_t* sel_slot,
                               const float* sel_scale, const float* kn2, const void* q,
                               const float* w, int H, int d, int k, int32_t* topk, int32_t* tcnt,
-                              void* ws, bool ws_clean, hipStream_t s) {
+                              void* ws, bool ws_clean, hipStream_t s, const AppendRow& app) {
     const size_t nc = (size_t)g.chunk_off[g.B] * 64 + 64;
     const int X1 = k1_blocks(g), X2 = k23_blocks(g);
     hipError_t e;
@@ -1177,7 +1187,7 @@ hipError_t launch_refine_band(const GeomDev& g, const int32_t* sel, const int32_
     if (e != hipSuccess) return e;
     timing_begin("k_band_fine", s);
     hipLaunchKernelGGL(k_band_fine, dim3(X2, g.B), dim3(64 * kWaves), 0, s, g, sel, cnt, lu, k,
-                       hist, cinfo, plist, pcnt, topk, tcnt);
+                       hist, cinfo, plist, pcnt, topk, tcnt, app);
     timing_end("k_band_fine", s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = hipErrorInvalidValue;

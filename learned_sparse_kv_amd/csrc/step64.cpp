@@ -371,14 +371,25 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
         int32_t* tc = out->topk_cnt ? out->topk_cnt + (size_t)j * g.B : x->tcnt_tmp;
         const uint8_t* qr = (const uint8_t*)in->q_refine + j * qr_step;
         const float* wr = in->w_refine + (size_t)j * g.B * d.H;
-        if (x->growing) {  // the step's token joins the recent region first
+        // the step's token joins the recent region first: its row is written
+        // by the band's fine-histogram pass (before attention reads the
+        // recent rows), else by a copy kernel of its own
+        AppendRow app;
+        const bool app_band = x->growing && groups > 0 && band && d.kv.row_bytes % 16 == 0 &&
+                              d.kv.row_bytes <= 16 * 256;
+        if (x->growing) {
             for (int r = 0; r < g.B; ++r) {
                 ++g.L[r];
                 ++g.nrec[r];
             }
-            if (launch_append_kv(g, (const uint8_t*)in->new_rows + (size_t)j * g.B * d.kv.row_bytes,
-                                 d.kv.row_bytes, (void*)d.recent, ms) != hipSuccess)
+            const uint8_t* rows = (const uint8_t*)in->new_rows + (size_t)j * g.B * d.kv.row_bytes;
+            if (app_band) {
+                app.rows = rows;
+                app.recent = (uint8_t*)d.recent;
+                app.n16 = (int32_t)(d.kv.row_bytes / 16);
+            } else if (launch_append_kv(g, rows, d.kv.row_bytes, (void*)d.recent, ms) != hipSuccess) {
                 return LSA_ERR_HIP;
+            }
         }
         if (groups > 0 && band) {
             const bool clean = x->band_clean;
@@ -386,7 +397,7 @@ lsa_status lsa_step64(lsa_ctx* x, const lsa_window_in* in, lsa_window_out* out,
             if (launch_refine_band(g, x->sel[cur], x->cnt[cur], lsa_pool_slots(d.pool),
                                    d.kv.page_bytes, d.kv.ikey_off, x->pt[cur], d.idx_dt,
                                    d.ikey_scale, x->sel_slot, x->sel_scale, x->kn2, qr, wr, d.H,
-                                   d.d, d.k, tk, tc, x->scores, clean, ms) != hipSuccess)
+                                   d.d, d.k, tk, tc, x->scores, clean, ms, app) != hipSuccess)
                 return LSA_ERR_HIP;
             x->band_clean = true;
         } else {
