@@ -111,7 +111,10 @@ constexpr int score_waves() {
 
 // Grid (X, B): the waves of block column x of request r take the request's
 // tiles x*nw + wave, stepping by X*nw, and load the next tile into registers
-// while the current one is scored from LDS.
+// while the current one is scored from LDS.  The launcher gives every wave
+// one tile of the longest request (all loads of the pass in flight at once:
+// faster than two tiles a wave, which kept the second one's loads behind the
+// first).
 template <int KDT, int D>
 __global__ __launch_bounds__((64 * score_waves<KDT, D>())) void k_score(
     GeomDev g, const uint8_t* __restrict__ kic, const float* __restrict__ kscale,
@@ -291,7 +294,7 @@ hipError_t launch_score(const GeomDev& g, const void* kic, lsa_dtype kdt, const 
     if (kdt == KDT && d == D) {                                                                 \
         constexpr int nw = score_waves<KDT, D>();                                               \
         timing_begin("k_score", s);                                                             \
-        hipLaunchKernelGGL((k_score<KDT, D>), dim3((mt + 2 * nw - 1) / (2 * nw), g.B),           \
+        hipLaunchKernelGGL((k_score<KDT, D>), dim3((mt + nw - 1) / nw, g.B),                     \
                            dim3(64 * nw), 0, s,                                                 \
                            g, k, kscale, qbar, bias, z, combine ? 1 : 0, theta, tmask, tcount); \
         timing_end("k_score", s);                                                               \
