@@ -532,8 +532,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the LSA decode "
-              "path here is a single-GPU build; see DESIGN.md for how it would shard.",
-              file=sys.stderr)
+              "path of this library runs every request of a batch on one GPU and has no "
+              "multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
