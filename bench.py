@@ -519,7 +519,8 @@ def main():
     ap.add_argument("--no-sustained", action="store_true",
                     help="skip the cold-cache scoring / attention GB/s points at 128K and 500K")
     ap.add_argument("--no-workloads", action="store_true",
-                    help="skip the decode steps/s of the 128K workloads and of the three-layer union")
+                    help="skip the decode steps/s of the 64K, 128K and 500K batch-4 workloads and of the "
+                         "three-layer union")
     ap.add_argument("--no-growing", action="store_true",
                     help="skip the growing-context decode (append per step, chunk commit per window)")
     ap.add_argument("--no-policies", action="store_true",
@@ -736,11 +737,15 @@ def main():
         # batch at 131,072 tokens each) and the pages' three-layer union at 500K
         t0 = time.perf_counter()
         result["decode_steps_128k"] = [window_rate(synth.config(2)), window_rate(synth.config_2u())]
+        # the other two window workloads: one request of 64K tokens (bf16 index
+        # keys) and 4 requests of 500K (fp8 index keys), both with the HBM cold tier
+        result["decode_steps_64k_500k_b4"] = [window_rate(synth.config(1)), window_rate(synth.config(3))]
         # the union of three layers selects about 1 - 0.9^3 = 27 % of the
         # chunks: a pool with room for two windows' selections
         result["union3_window"] = window_rate(synth.dataclasses.replace(cfg, slots_per_req=3072), n_layers=3)
         log(f"[bench] other workloads in {time.perf_counter() - t0:.1f}s: "
-            + json.dumps({"128k": result["decode_steps_128k"], "union3": result["union3_window"]}))
+            + json.dumps({"128k": result["decode_steps_128k"], "64k_500k_b4": result["decode_steps_64k_500k_b4"],
+                          "union3": result["union3_window"]}))
     if not args.no_policies:
         result["policy_comparison"] = policy_comparison(inp)
         log("[bench] policies: " + json.dumps(result["policy_comparison"]))
