@@ -683,6 +683,12 @@ def main():
         "attention_500k": hbm("k_attn_mla") or hbm("k_attn_f32"),
         "kernels": kern,
         "initial_fill_ms": round(prime_s * 1e3, 2),
+        # 256 decode steps from a cold pool: the first trigger and its fill
+        # (measured once) plus four windows at the timed rate
+        "end_to_end_256_steps": {
+            "ms_with_initial_fill": round(prime_s * 1e3 + 4 * wall * 1e3 / args.steps, 2),
+            "ms_without_initial_fill": round(4 * wall * 1e3 / args.steps, 2),
+            "steps_per_s_with_initial_fill": round(4 * S / (prime_s + 4 * wall / args.steps), 1)},
         "refill_mb_per_window": round(float(np.mean(refill_mb)), 2),
         "selected_chunks_per_request": round(float(win_cnt.mean()), 1),
         "resident_fraction": round(float(resident.mean()), 4),
